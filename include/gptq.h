@@ -1,0 +1,144 @@
+/*
+ * gptq.h -- C ABI of libgptq.so, a GPTQ layer quantizer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The pages describe GPTQ as the Hessian-guided 2-4 bit weight quantizer at
+ * the base of OneComp's pipeline (OneComp hub article, "core features", item 2,
+ * quantizer table; item 3, the LPCD example GPTQ(wbits=3, groupsize=128)),
+ * run layer by layer (same article, "limitations", point 3), with a Quantizer
+ * interface exposing quantize() and save() (same article, "code
+ * architecture").  The three entry points below are that layer pass:
+ * calibration statistics (gptq_accumulate_hessian), quantize()
+ * (gptq_quantize_layer) and the packed artefact behind save() (gptq_pack).
+ *
+ * Conventions for every call
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  Row-major.
+ *   - Work is queued on `stream` in order; calls return before the GPU is done
+ *     unless stated otherwise.  The library never allocates or frees memory.
+ *   - Return 0 (GPTQ_OK) on success, a positive gptq_status otherwise.
+ *     Argument errors are detected on the host and return before any launch.
+ *   - Calls that share a workspace or an output buffer on one device must not
+ *     overlap in time (same stream, or ordered by the caller).
+ */
+#ifndef GPTQ_H
+#define GPTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* gptq_stream_t; /* a hipStream_t; NULL = default stream */
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_EINVAL = 1,       /* bad shape, pointer, dtype or parameter */
+  GPTQ_ENOTPD = 2,       /* damped Hessian not positive definite (pivot <= 0 or not finite) */
+  GPTQ_EWORKSPACE = 3,   /* workspace smaller than the matching *_workspace_bytes() */
+  GPTQ_EUNSUPPORTED = 4, /* valid request this build does not implement */
+  GPTQ_EHIP = 5          /* a HIP runtime call or kernel launch failed */
+} gptq_status;
+
+typedef enum { GPTQ_BF16 = 0, GPTQ_F32 = 1 } gptq_dtype;
+
+/* gptq_params.flags */
+enum {
+  /* H already holds the factor U written by an earlier gptq_quantize_layer
+     call with the same cols (shared Hessian: q/k/v, gate/up).  Damping and the
+     factor are skipped; the dead-column mask is read back from H's strictly
+     lower triangle (see gptq_quantize_layer).  Needs cols >= 3. */
+  GPTQ_H_IS_FACTOR = 1
+};
+
+/* Quantizer knobs: wbits and groupsize as in GPTQ(wbits, groupsize) on the
+   OneComp hub article (LPCD example). */
+typedef struct {
+  int32_t bits;      /* 2, 3, 4 or 8; maxq = 2^bits - 1 */
+  int32_t groupsize; /* -1 (one group per row), 32, 64, or a multiple of 128 */
+  int32_t blocksize; /* lazy-batch width; 128 is the one supported value */
+  float damp;        /* lambda = damp * mean(diag H); typically 0.01; >= 0 and finite */
+  int32_t flags;     /* GPTQ_H_IS_FACTOR or 0 */
+} gptq_params;
+
+/* ---------------------------------------------------------------------------
+ * Hessian accumulation.  H[n, n] += 2 * X^T X over one chunk of calibration
+ * tokens X[tokens, n] (row stride ldx elements, dtype x_dtype).
+ *
+ * H is fp32, full symmetric (both triangles written, bit-identical).  The
+ * caller zero-fills H before the first chunk and calls once per chunk; each
+ * call reads H and adds to it.  Accumulation is in fp32 (bf16 products are
+ * exact in fp32); the summation order is fixed, so repeated calls give
+ * bit-identical H.  Alignment: X may have any alignment; 8-byte-aligned X
+ * with ldx % 4 == 0 takes the vector path.
+ * workspace: at least gptq_hessian_workspace_bytes(n, tokens, x_dtype) bytes
+ * of device memory (may be 0 bytes, then NULL is accepted), 256-byte aligned.
+ * tokens == 0 or n == 0: no work, GPTQ_OK.
+ * ------------------------------------------------------------------------- */
+size_t gptq_hessian_workspace_bytes(int64_t n, int64_t tokens, gptq_dtype x_dtype);
+
+int gptq_accumulate_hessian(float* H, int64_t n, const void* X, gptq_dtype x_dtype,
+                            int64_t tokens, int64_t ldx, void* workspace,
+                            size_t workspace_bytes, gptq_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Quantize one linear layer W[rows, cols] (dtype w_dtype, row stride cols)
+ * against its Hessian H[cols, cols] (fp32, full symmetric as written by
+ * gptq_accumulate_hessian).
+ *
+ * Steps (all on the device, in order): dead columns (H_ii == 0: H_ii := 1,
+ * W[:, i] := 0); damping H_d = H + lambda I, lambda = damp * mean(diag H);
+ * the upper factor U with positive diagonal and U^T U = inv(H_d); then the
+ * column loop in lazy batches of 128 columns: per-row asymmetric min/max grid
+ * at each group start from the current, error-updated weights;
+ * q = clamp(rint(w/s) + z, 0, maxq); w^ = s (q - z); e = (w - w^) / U_jj fed
+ * back into the later columns of the block; after each block the trailing
+ * update W[:, c1:] -= E U[c0:c1, c1:].
+ *
+ * H is overwritten IN PLACE (unless GPTQ_H_IS_FACTOR): its upper triangle
+ * (with the diagonal) holds U in fp32; H[i][i-1] = 1.0f if column i is dead
+ * else 0.0f (i >= 1) and H[cols-1][0] carries the same flag for column 0
+ * (cols >= 3); the rest of the lower triangle is unspecified.
+ *
+ * Outputs (device, caller-owned):
+ *   codes    uint8 [rows, cols]     integer codes in [0, maxq]
+ *   scales   float [rows, G]        G = ceil(cols / groupsize) (1 if groupsize == -1)
+ *   zeros    uint8 [rows, G]        integer zero points in [0, maxq]
+ *   w_hat    float [rows, cols]     s (q - z); may be NULL
+ *   row_loss float [rows]           sum_j (w_j - w^_j)^2 / (2 U_jj^2); may be NULL
+ * workspace: gptq_quantize_workspace_bytes(rows, cols, p) bytes, 256-byte aligned.
+ * d_status: if non-NULL, a device int32 that receives the final status
+ *   (GPTQ_OK or GPTQ_ENOTPD) and the call is fully asynchronous; if NULL the
+ *   call synchronizes `stream` once at the end and returns that status.
+ * W, X and the outputs must not alias each other, H or the workspace.
+ * rows == 0 or cols == 0: no work, GPTQ_OK.
+ * ------------------------------------------------------------------------- */
+size_t gptq_quantize_workspace_bytes(int64_t rows, int64_t cols, const gptq_params* p);
+
+int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t rows, int64_t cols,
+                        float* H, const gptq_params* p, uint8_t* codes, float* scales,
+                        uint8_t* zeros, float* w_hat, float* row_loss, void* workspace,
+                        size_t workspace_bytes, int32_t* d_status, gptq_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Pack codes[rows, cols] (uint8, each < 2^bits) into packed[rows, cols*bits/32]
+ * uint32 words: per row one little-endian bitstream, code i in bits
+ * [i*bits, (i+1)*bits), word w holding stream bits [32w, 32w+32).  For bits = 3
+ * a run of 32 codes fills three words.  bits in {2, 3, 4, 8};
+ * (cols * bits) % 32 == 0.  Codes >= 2^bits are masked to their low bits.
+ * ------------------------------------------------------------------------- */
+int gptq_pack(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits, uint32_t* packed,
+              gptq_stream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* gptq_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int gptq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_H */
