@@ -1,0 +1,206 @@
+"""GPTQ layer quantizer for AMD Instinct MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libgptq.so`` (declared in
+``include/gptq.h``).  The functions carry the C names; they only marshal
+arguments -- device pointers and the current HIP stream of PyTorch-ROCm
+tensors -- and raise ``GptqError`` on a non-zero status.  Every step of the
+quantizer runs in the library's HIP kernels; there is no other code path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgptq.so")
+
+GPTQ_OK, GPTQ_EINVAL, GPTQ_ENOTPD, GPTQ_EWORKSPACE, GPTQ_EUNSUPPORTED, GPTQ_EHIP = range(6)
+GPTQ_BF16, GPTQ_F32 = 0, 1
+GPTQ_H_IS_FACTOR = 1
+
+
+class GptqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {gptq_status_string(status)} (status {status})")
+
+
+class gptq_params(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("groupsize", ctypes.c_int32), ("blocksize", ctypes.c_int32),
+                ("damp", ctypes.c_float), ("flags", ctypes.c_int32)]
+
+
+@dataclass
+class Params:
+    """GPTQ(wbits, groupsize) knobs; see gptq_params in include/gptq.h."""
+
+    bits: int = 4
+    groupsize: int = 128
+    blocksize: int = 128
+    damp: float = 0.01
+    flags: int = 0
+
+    def c(self) -> gptq_params:
+        return gptq_params(self.bits, self.groupsize, self.blocksize, self.damp, self.flags)
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libgptq.so.  Raises if it has not been built: there is no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with post_weight_quantization_03_amd.build")
+    # PyTorch-ROCm ships its own HIP runtime under the same soname.  Loading torch first
+    # makes the library bind to that already-loaded runtime, so tensors, streams and the
+    # library's launches share one runtime instead of two in one process.
+    import torch  # noqa: F401
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    L.gptq_hessian_workspace_bytes.argtypes = [i64, i64, ctypes.c_int]
+    L.gptq_hessian_workspace_bytes.restype = sz
+    L.gptq_accumulate_hessian.argtypes = [vp, i64, vp, ctypes.c_int, i64, i64, vp, sz, vp]
+    L.gptq_accumulate_hessian.restype = ctypes.c_int
+    L.gptq_quantize_workspace_bytes.argtypes = [i64, i64, ctypes.POINTER(gptq_params)]
+    L.gptq_quantize_workspace_bytes.restype = sz
+    L.gptq_quantize_layer.argtypes = [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(gptq_params), vp, vp, vp,
+                                      vp, vp, vp, sz, vp, vp]
+    L.gptq_quantize_layer.restype = ctypes.c_int
+    L.gptq_pack.argtypes = [vp, i64, i64, i32, vp, vp]
+    L.gptq_pack.restype = ctypes.c_int
+    L.gptq_status_string.argtypes = [ctypes.c_int]
+    L.gptq_status_string.restype = ctypes.c_char_p
+    L.gptq_version.argtypes = []
+    L.gptq_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+# --------------------------------------------------------------------------- marshalling helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return GPTQ_BF16
+    if t.dtype == torch.float32:
+        return GPTQ_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def _workspace(nbytes, like):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=like.device)
+
+
+# --------------------------------------------------------------------------- entry points
+
+def gptq_status_string(status: int) -> str:
+    return lib().gptq_status_string(int(status)).decode()
+
+
+def gptq_version() -> int:
+    return int(lib().gptq_version())
+
+
+def gptq_hessian_workspace_bytes(n: int, tokens: int, x_dtype: int) -> int:
+    return int(lib().gptq_hessian_workspace_bytes(n, tokens, x_dtype))
+
+
+def gptq_accumulate_hessian(H, X, workspace=None, stream=None):
+    """H [n, n] fp32 += 2 X^T X for X [tokens, n] (bf16 or fp32, unit column stride)."""
+    _check_dev(H)
+    if not X.is_cuda or X.stride(1) != 1:
+        raise ValueError("X must be a device tensor with unit column stride")
+    n = H.shape[0]
+    if H.dtype != _torch().float32 or H.shape != (n, n) or X.shape[1] != n:
+        raise ValueError("shape or dtype mismatch")
+    dt = _dtype_code(X)
+    need = gptq_hessian_workspace_bytes(n, X.shape[0], dt)
+    if workspace is None:
+        workspace = _workspace(need, H)
+    st = lib().gptq_accumulate_hessian(_ptr(H), n, _ptr(X), dt, X.shape[0], X.stride(0), _ptr(workspace),
+                                       workspace.numel(), _stream(stream))
+    if st:
+        raise GptqError(st, "gptq_accumulate_hessian")
+    return H
+
+
+def gptq_quantize_workspace_bytes(rows: int, cols: int, params: Params) -> int:
+    p = params.c()
+    return int(lib().gptq_quantize_workspace_bytes(rows, cols, ctypes.byref(p)))
+
+
+def gptq_quantize_layer(W, H, params: Params, codes, scales, zeros, w_hat=None, row_loss=None, workspace=None,
+                        d_status=None, stream=None):
+    """Quantize W [rows, cols] against H [cols, cols]; H is overwritten by the factor.
+
+    With ``d_status`` (a device int32 tensor) the call is asynchronous and the final
+    status lands there; without it the call synchronizes and raises on failure.
+    """
+    _check_dev(W, H, codes, scales, zeros, w_hat, row_loss, d_status)
+    rows, cols = W.shape
+    p = params.c()
+    need = int(lib().gptq_quantize_workspace_bytes(rows, cols, ctypes.byref(p)))
+    if workspace is None:
+        workspace = _workspace(need, W)
+    st = lib().gptq_quantize_layer(_ptr(W), _dtype_code(W), rows, cols, _ptr(H), ctypes.byref(p), _ptr(codes),
+                                   _ptr(scales), _ptr(zeros), _ptr(w_hat), _ptr(row_loss), _ptr(workspace),
+                                   workspace.numel(), _ptr(d_status), _stream(stream))
+    if st:
+        raise GptqError(st, "gptq_quantize_layer")
+    return codes
+
+
+def gptq_pack(codes, bits: int, packed, stream=None):
+    """codes [rows, cols] uint8 -> packed [rows, cols*bits/32] (int32 tensor holding uint32 words)."""
+    _check_dev(codes, packed)
+    rows, cols = codes.shape
+    st = lib().gptq_pack(_ptr(codes), rows, cols, bits, _ptr(packed), _stream(stream))
+    if st:
+        raise GptqError(st, "gptq_pack")
+    return packed
+
+
+def quantize(W, H, params: Params, stream=None, want_what=True):
+    """Allocates the outputs on W's device and runs gptq_quantize_layer synchronously."""
+    torch = _torch()
+    rows, cols = W.shape
+    g = cols if params.groupsize == -1 else params.groupsize
+    G = -(-cols // g)
+    dev = W.device
+    out = {
+        "codes": torch.empty((rows, cols), dtype=torch.uint8, device=dev),
+        "scales": torch.empty((rows, G), dtype=torch.float32, device=dev),
+        "zeros": torch.empty((rows, G), dtype=torch.uint8, device=dev),
+        "w_hat": torch.empty((rows, cols), dtype=torch.float32, device=dev) if want_what else None,
+        "row_loss": torch.empty((rows,), dtype=torch.float32, device=dev),
+    }
+    gptq_quantize_layer(W, H, params, out["codes"], out["scales"], out["zeros"], out["w_hat"], out["row_loss"],
+                        stream=stream)
+    return out

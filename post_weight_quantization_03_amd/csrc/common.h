@@ -1,0 +1,107 @@
+// Internal declarations shared by the kernel files of libgptq.so (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gptq.h"
+
+namespace gptq {
+
+// ---------------------------------------------------------------------------
+// MFMA operand and accumulator types.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// 32x32 MFMA accumulator layout (v_mfma_f32_32x32x*): lane l, register r holds
+// element (row, col) of the 32x32 block with col = l % 32 and
+// row = 8 * (r / 4) + 4 * (l / 32) + r % 4.
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+__device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
+
+// Device status codes are gptq_status values; kernels raise them with atomicMax.
+__device__ __forceinline__ void raise_status(int* st, int code) { atomicMax(st, code); }
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------------------
+// fp32 MFMA GEMM:  C(m, n) = alpha * sum_k A(m, k) B(k, n) + (beta ? C(m, n) : 0)
+//   A(m, k) = A[m * lda + k]
+//   B(k, n) = B[k * ldb + n]        (b_kmajor)   or   B[n * ldb + k]   (!b_kmajor)
+//   C(m, n) = C[m * ldc + n]
+// 128x128 tiles.  tri: grid.x enumerates only the lower tiles (tile_m >= tile_n)
+// of a square tile grid.  klo_n: B is lower triangular, so k < n0 is skipped.
+// khi_m: A is lower triangular, so k >= m0 + 128 is skipped.  Batches run over
+// blockIdx.z with element strides sA, sB, sC.
+struct GemmF32 {
+  const float* A;
+  const float* B;
+  float* C;
+  int64_t lda, ldb, ldc;
+  int64_t sA, sB, sC;
+  int M, N, K;
+  float alpha;
+  int beta;
+  int b_kmajor;
+  int tri;
+  int klo_n;
+  int khi_m;
+  int batch;
+};
+hipError_t gemm_f32(const GemmF32& g, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Hessian accumulation (k_hessian.hip).
+size_t hessian_workspace(int64_t n, int64_t tokens, gptq_dtype dt);
+int hessian_launch(float* H, int64_t n, const void* X, gptq_dtype dt, int64_t tokens, int64_t ldx,
+                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Damping and factor (k_factor.hip).
+struct FactorWs {
+  int* status;      // device int32
+  float* lam;       // device: lambda (float)
+  uint8_t* dead;    // device [n]
+  float* A;         // [n, n] reversed damped Hessian -> lower Cholesky factor (off-diagonal blocks)
+  float* Minv;      // [n, n] inverse of that factor (lower)
+  float* T;         // [tmax, tmax] scratch for the triangular inverse
+  int64_t tmax;
+};
+size_t factor_scratch_floats(int64_t n, int64_t* tmax);
+// H (fp32 [n, n]) -> damped, factored; U written back to H's upper triangle, dead flags to the
+// strictly lower slots.  Status (ENOTPD) is raised on the device.
+hipError_t factor_run(float* H, int64_t n, float damp, const FactorWs& ws, hipStream_t stream);
+// H holds a factor from an earlier call: read the dead flags back from it.
+hipError_t dead_from_factor(const float* H, int64_t n, uint8_t* dead, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Quantize loop (k_quant.hip).
+struct QuantArgs {
+  const void* W;
+  gptq_dtype w_dtype;
+  int64_t rows, cols;
+  const float* U;  // [cols, cols], upper triangle used
+  const uint8_t* dead;
+  int bits, groupsize;  // groupsize already resolved (-1 -> cols)
+  uint8_t* codes;
+  float* scales;
+  uint8_t* zeros;
+  float* w_hat;
+  float* row_loss;
+  float* Wf;  // [rows, cols] working copy
+  float* E;   // [rows, 128] scaled errors of the current block
+  int64_t G;
+};
+hipError_t quant_run(const QuantArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Packing (k_pack.hip).
+hipError_t pack_launch(const uint8_t* codes, int64_t rows, int64_t cols, int bits, uint32_t* packed,
+                       hipStream_t stream);
+
+// Small utility kernels (k_factor.hip).
+hipError_t fill_i32(int* p, int64_t n, int v, hipStream_t stream);
+hipError_t copy_status(const int* src, int32_t* dst, hipStream_t stream);
+
+}  // namespace gptq

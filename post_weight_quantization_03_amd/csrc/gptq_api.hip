@@ -1,0 +1,180 @@
+// C ABI of libgptq.so: argument checks on the host, workspace carving and the
+// launch sequence of each entry point.  Every declaration is documented in
+// include/gptq.h.
+#include "common.h"
+
+namespace {
+
+using namespace gptq;
+
+constexpr int VERSION = 100;  // 0.1.0
+constexpr int64_t MAX_DIM = (int64_t)1 << 30;
+
+struct QuantLayout {
+  size_t status, lam, dead, loss, Wf, E, A, Minv, T, total;
+  int64_t tmax;
+};
+
+bool params_ok(const gptq_params* p, int64_t cols, int* why) {
+  if (!p) return (*why = GPTQ_EINVAL), false;
+  if (!(p->bits == 2 || p->bits == 3 || p->bits == 4 || p->bits == 8)) return (*why = GPTQ_EINVAL), false;
+  if (!(p->damp >= 0.0f) || !(p->damp < INFINITY)) return (*why = GPTQ_EINVAL), false;
+  if (p->flags & ~GPTQ_H_IS_FACTOR) return (*why = GPTQ_EINVAL), false;
+  if (p->groupsize == 0 || p->groupsize < -1) return (*why = GPTQ_EINVAL), false;
+  if (p->blocksize != 128) return (*why = GPTQ_EUNSUPPORTED), false;
+  const int64_t g = p->groupsize;
+  if (!(g == -1 || g == 32 || g == 64 || g % 128 == 0)) return (*why = GPTQ_EUNSUPPORTED), false;
+  if ((p->flags & GPTQ_H_IS_FACTOR) && cols < 3) return (*why = GPTQ_EINVAL), false;
+  return true;
+}
+
+QuantLayout layout(int64_t rows, int64_t cols, const gptq_params* p) {
+  QuantLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  L.status = take(4 * sizeof(int));
+  L.lam = take(sizeof(float));
+  L.dead = take((size_t)cols);
+  L.loss = take((size_t)rows * sizeof(float));
+  L.Wf = take((size_t)rows * cols * sizeof(float));
+  L.E = take((size_t)rows * 128 * sizeof(float));
+  if (!(p->flags & GPTQ_H_IS_FACTOR)) {
+    int64_t tmax = 0;
+    factor_scratch_floats(cols, &tmax);
+    L.tmax = tmax;
+    L.A = take((size_t)cols * cols * sizeof(float));
+    L.Minv = take((size_t)cols * cols * sizeof(float));
+    L.T = take((size_t)(tmax > 0 ? tmax : 1) * sizeof(float));
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gptq_status_string(int status) {
+  switch (status) {
+    case GPTQ_OK: return "ok";
+    case GPTQ_EINVAL: return "invalid argument";
+    case GPTQ_ENOTPD: return "damped Hessian is not positive definite";
+    case GPTQ_EWORKSPACE: return "workspace too small";
+    case GPTQ_EUNSUPPORTED: return "unsupported parameter combination";
+    case GPTQ_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int gptq_version(void) { return VERSION; }
+
+size_t gptq_hessian_workspace_bytes(int64_t n, int64_t tokens, gptq_dtype x_dtype) {
+  if (n <= 0 || tokens <= 0 || n > MAX_DIM || tokens > MAX_DIM) return 0;
+  return hessian_workspace(n, tokens, x_dtype);
+}
+
+int gptq_accumulate_hessian(float* H, int64_t n, const void* X, gptq_dtype x_dtype, int64_t tokens, int64_t ldx,
+                            void* workspace, size_t workspace_bytes, gptq_stream_t stream) {
+  if (n < 0 || tokens < 0 || n > MAX_DIM || tokens > MAX_DIM) return GPTQ_EINVAL;
+  if (!(x_dtype == GPTQ_BF16 || x_dtype == GPTQ_F32)) return GPTQ_EINVAL;
+  if (n == 0 || tokens == 0) return GPTQ_OK;
+  if (!H || !X || ldx < n) return GPTQ_EINVAL;
+  if (n * n > ((int64_t)1 << 31) * 2) return GPTQ_EUNSUPPORTED;
+  const size_t need = hessian_workspace(n, tokens, x_dtype);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return GPTQ_EWORKSPACE;
+  return hessian_launch(H, n, X, x_dtype, tokens, ldx, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+size_t gptq_quantize_workspace_bytes(int64_t rows, int64_t cols, const gptq_params* p) {
+  int why = 0;
+  if (rows <= 0 || cols <= 0 || rows > MAX_DIM || cols > MAX_DIM || !params_ok(p, cols, &why)) return 0;
+  return layout(rows, cols, p).total;
+}
+
+int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t rows, int64_t cols, float* H,
+                        const gptq_params* p, uint8_t* codes, float* scales, uint8_t* zeros, float* w_hat,
+                        float* row_loss, void* workspace, size_t workspace_bytes, int32_t* d_status,
+                        gptq_stream_t stream_) {
+  hipStream_t stream = (hipStream_t)stream_;
+  if (rows < 0 || cols < 0 || rows > MAX_DIM || cols > MAX_DIM) return GPTQ_EINVAL;
+  if (!(w_dtype == GPTQ_BF16 || w_dtype == GPTQ_F32)) return GPTQ_EINVAL;
+  int why = GPTQ_EINVAL;
+  if (!params_ok(p, cols, &why)) return why;
+  if (rows == 0 || cols == 0) return GPTQ_OK;
+  if (!W || !H || !codes || !scales || !zeros || !workspace) return GPTQ_EINVAL;
+  if (cols > 65535 * 4 || rows * cols > ((int64_t)1 << 40)) return GPTQ_EUNSUPPORTED;
+  const QuantLayout L = layout(rows, cols, p);
+  if (workspace_bytes < L.total) return GPTQ_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return GPTQ_EINVAL;
+
+  char* ws = static_cast<char*>(workspace);
+  int* status = reinterpret_cast<int*>(ws + L.status);
+  uint8_t* dead = reinterpret_cast<uint8_t*>(ws + L.dead);
+  const int64_t g = p->groupsize == -1 ? cols : p->groupsize;
+  const int64_t G = (cols + g - 1) / g;
+
+  // the row loss is always accumulated; without a caller buffer it lands in the workspace
+  float* loss = row_loss ? row_loss : reinterpret_cast<float*>(ws + L.loss);
+
+  hipError_t e = fill_i32(status, 1, GPTQ_OK, stream);
+  if (e != hipSuccess) return GPTQ_EHIP;
+  if (p->flags & GPTQ_H_IS_FACTOR) {
+    e = dead_from_factor(H, cols, dead, stream);
+  } else {
+    FactorWs f{};
+    f.status = status;
+    f.lam = reinterpret_cast<float*>(ws + L.lam);
+    f.dead = dead;
+    f.A = reinterpret_cast<float*>(ws + L.A);
+    f.Minv = reinterpret_cast<float*>(ws + L.Minv);
+    f.T = reinterpret_cast<float*>(ws + L.T);
+    f.tmax = L.tmax;
+    e = factor_run(H, cols, p->damp, f, stream);
+  }
+  if (e != hipSuccess) return GPTQ_EHIP;
+
+  QuantArgs q{};
+  q.W = W;
+  q.w_dtype = w_dtype;
+  q.rows = rows;
+  q.cols = cols;
+  q.U = H;
+  q.dead = dead;
+  q.bits = p->bits;
+  q.groupsize = (int)g;
+  q.codes = codes;
+  q.scales = scales;
+  q.zeros = zeros;
+  q.w_hat = w_hat;
+  q.row_loss = loss;
+  q.Wf = reinterpret_cast<float*>(ws + L.Wf);
+  q.E = reinterpret_cast<float*>(ws + L.E);
+  q.G = G;
+  e = quant_run(q, stream);
+  if (e != hipSuccess) return GPTQ_EHIP;
+
+  if (d_status) {
+    e = copy_status(status, d_status, stream);
+    return e == hipSuccess ? GPTQ_OK : GPTQ_EHIP;
+  }
+  int host = 0;
+  if (hipMemcpyAsync(&host, status, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess) return GPTQ_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return GPTQ_EHIP;
+  return host;
+}
+
+int gptq_pack(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits, uint32_t* packed,
+              gptq_stream_t stream) {
+  if (rows < 0 || cols < 0 || rows > MAX_DIM || cols > MAX_DIM) return GPTQ_EINVAL;
+  if (!(bits == 2 || bits == 3 || bits == 4 || bits == 8)) return GPTQ_EINVAL;
+  if ((cols * bits) % 32 != 0) return GPTQ_EINVAL;
+  if (rows == 0 || cols == 0) return GPTQ_OK;
+  if (!codes || !packed) return GPTQ_EINVAL;
+  return pack_launch(codes, rows, cols, bits, packed, (hipStream_t)stream) == hipSuccess ? GPTQ_OK : GPTQ_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,320 @@
+// The GPTQ column loop in lazy batches of 128 columns.
+//
+// k_stage_w      W (bf16 or fp32) -> fp32 working copy Wf, dead columns zeroed.
+// k_quant_block  one 128-column block: per-row grid at group starts from the
+//                current weights, then 128 serial steps
+//                  q = clamp(rint(w_j / s) + z, 0, maxq), w^ = s (q - z),
+//                  e_j = (w_j - w^) / U_jj, w_k -= e_j U_jk (k in the block)
+//                writing codes, grid, w^, row loss and E (the block's e_j).
+// Then the trailing update W[:, c1:] -= E U[c0:c1, c1:] as an fp32 MFMA GEMM.
+//
+// Layout of k_quant_block: a 64-lane wave holds 4 rows, 16 lanes per row; lane
+// t of a row owns columns 8t .. 8t+7 of the block in registers.  At step j the
+// owner lane (j / 8) rounds its column, and e_j reaches the row's 16 lanes by
+// a DPP row broadcast (row_newbcast, one instruction, rows of 16 lanes are
+// exactly the wave's DPP rows).  The U block sits in LDS; each lane reads the
+// 8 entries of row j it needs as two 16-byte reads.  Group ranges are reduced
+// over the lanes that hold the group with xor shuffles.
+#include <utility>
+
+#include "common.h"
+
+namespace gptq {
+namespace {
+
+constexpr int B = 128;
+
+enum GroupMode { GM_BIG = 0, GM_32 = 1, GM_64 = 2 };
+
+__global__ void k_stage_w(const void* W, int is_bf16, int64_t rows, int64_t cols, const uint8_t* dead,
+                          float* Wf) {
+  const int64_t total = rows * cols;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t c = i % cols;
+    float v;
+    if (is_bf16) {
+      const uint16_t b = static_cast<const uint16_t*>(W)[i];
+      v = __uint_as_float((uint32_t)b << 16);
+    } else {
+      v = static_cast<const float*>(W)[i];
+    }
+    Wf[i] = dead[c] ? 0.0f : v;
+  }
+}
+
+struct BlockArgs {
+  float* Wf;
+  const float* U;
+  int64_t rows, cols;
+  int64_t c0;
+  int bw;  // columns in this block (<= 128)
+  float maxq;
+  int64_t g;  // resolved group size
+  int64_t G;
+  uint8_t* codes;
+  float* scales;
+  uint8_t* zeros;
+  float* w_hat;
+  float* row_loss;
+  float* E;
+};
+
+template <int O>
+__device__ __forceinline__ float row_bcast(float v) {
+  // DPP row_newbcast: every lane of a 16-lane row reads lane O of that row.
+  return __builtin_amdgcn_update_dpp(0.0f, v, 0x150 + O, 0xf, 0xf, false);
+}
+
+template <int WIDTH>
+__device__ __forceinline__ void reduce_minmax(float& mn, float& mx) {
+#pragma unroll
+  for (int m = 1; m < WIDTH; m <<= 1) {
+    mn = fminf(mn, __shfl_xor(mn, m, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+  }
+}
+
+// Asymmetric min/max grid with zero forced into the range; an all-zero group uses [-1, 1].
+__device__ __forceinline__ void grid_from_range(float mn, float mx, float maxq, float& s, float& z) {
+  float xmin = fminf(mn, 0.0f), xmax = fmaxf(mx, 0.0f);
+  if (xmin == 0.0f && xmax == 0.0f) {
+    xmin = -1.0f;
+    xmax = 1.0f;
+  }
+  s = (xmax - xmin) / maxq;
+  z = rintf(-xmin / s);
+}
+
+struct Lane {
+  float w[8], q[8], e[8], wh[8];
+  float s, z, loss;
+  int t;
+};
+
+template <int MODE, int J>
+__device__ __forceinline__ void step(Lane& L, const BlockArgs& a, const float (*Us)[B], const float* rUd,
+                                     int64_t row, bool row_ok) {
+  if (J >= a.bw) return;
+  constexpr int O = J >> 3, SL = J & 7;
+  if constexpr (MODE != GM_BIG) {
+    constexpr int GW = (MODE == GM_32) ? 32 : 64;
+    if constexpr (J % GW == 0) {
+      // every lane reduces its own aligned lane group; only the group starting at
+      // column J is used from here on, the others are recomputed at their start
+      constexpr int LANES = GW / 8;
+      float mn = L.w[0], mx = L.w[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) {
+        mn = fminf(mn, L.w[i]);
+        mx = fmaxf(mx, L.w[i]);
+      }
+      reduce_minmax<LANES>(mn, mx);
+      float s, z;
+      grid_from_range(mn, mx, a.maxq, s, z);
+      if ((L.t / LANES) == (O / LANES)) {
+        L.s = s;
+        L.z = z;
+      }
+      if (L.t == O && row_ok) {
+        const int64_t gi = (a.c0 + J) / a.g;
+        a.scales[row * a.G + gi] = s;
+        a.zeros[row * a.G + gi] = (uint8_t)z;
+      }
+    }
+  }
+  const float x = L.w[SL];
+  const float r = x / L.s;
+  const float qv = fminf(fmaxf(rintf(r) + L.z, 0.0f), a.maxq);
+  const float whv = L.s * (qv - L.z);
+  const float d = x - whv;
+  const float ev = d * rUd[J];
+  if (L.t == O) {
+    L.q[SL] = qv;
+    L.wh[SL] = whv;
+    L.e[SL] = ev;
+    L.loss += 0.5f * ev * ev;
+  }
+  const float eb = row_bcast<O>(ev);
+  const float4 u0 = *reinterpret_cast<const float4*>(&Us[J][8 * L.t]);
+  const float4 u1 = *reinterpret_cast<const float4*>(&Us[J][8 * L.t + 4]);
+  L.w[0] = fmaf(-eb, u0.x, L.w[0]);
+  L.w[1] = fmaf(-eb, u0.y, L.w[1]);
+  L.w[2] = fmaf(-eb, u0.z, L.w[2]);
+  L.w[3] = fmaf(-eb, u0.w, L.w[3]);
+  L.w[4] = fmaf(-eb, u1.x, L.w[4]);
+  L.w[5] = fmaf(-eb, u1.y, L.w[5]);
+  L.w[6] = fmaf(-eb, u1.z, L.w[6]);
+  L.w[7] = fmaf(-eb, u1.w, L.w[7]);
+}
+
+template <int MODE, int... Js>
+__device__ __forceinline__ void run_steps(Lane& L, const BlockArgs& a, const float (*Us)[B], const float* rUd,
+                                          int64_t row, bool row_ok, std::integer_sequence<int, Js...>) {
+  (step<MODE, Js>(L, a, Us, rUd, row, row_ok), ...);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void k_quant_block(BlockArgs a) {
+  __shared__ __attribute__((aligned(16))) float Us[B][B];
+  __shared__ float rUd[B];
+  const int tid = threadIdx.x;
+  const int64_t c0 = a.c0, cols = a.cols;
+  // U block: Us[j][k] = U[c0+j][c0+k] for k >= j inside the block, else 0
+  for (int idx = tid; idx < B * B; idx += 256) {
+    const int j = idx >> 7, k = idx & (B - 1);
+    float v = 0.0f;
+    if (j < a.bw && k < a.bw && k >= j) v = a.U[(c0 + j) * cols + c0 + k];
+    Us[j][k] = v;
+  }
+  if (tid < B) rUd[tid] = tid < a.bw ? 1.0f / a.U[(c0 + tid) * cols + c0 + tid] : 0.0f;
+  __syncthreads();
+
+  Lane L;
+  const int lane = tid & 63;
+  L.t = lane & 15;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 6) * 4 + (lane >> 4);
+  const bool row_ok = row < a.rows;
+  const int64_t base = row * cols + c0 + 8 * L.t;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    L.w[i] = (row_ok && 8 * L.t + i < a.bw) ? a.Wf[base + i] : 0.0f;
+    L.q[i] = 0.0f;
+    L.e[i] = 0.0f;
+    L.wh[i] = 0.0f;
+  }
+  L.loss = 0.0f;
+  L.s = 1.0f;
+  L.z = 0.0f;
+
+  if constexpr (MODE == GM_BIG) {
+    const int64_t gi = c0 / a.g;
+    if (c0 % a.g == 0) {
+      // group starts here: range over its columns in the current weights
+      float mn = L.w[0], mx = L.w[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) {
+        mn = fminf(mn, L.w[i]);
+        mx = fmaxf(mx, L.w[i]);
+      }
+      const int64_t gend = (c0 + a.g) < cols ? (c0 + a.g) : cols;
+      if (row_ok) {
+        for (int64_t cb = c0 + B; cb < gend; cb += B) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int64_t c = cb + 8 * L.t + i;
+            if (c < gend) {
+              const float v = a.Wf[row * cols + c];
+              mn = fminf(mn, v);
+              mx = fmaxf(mx, v);
+            }
+          }
+        }
+      }
+      reduce_minmax<16>(mn, mx);
+      grid_from_range(mn, mx, a.maxq, L.s, L.z);
+      if (L.t == 0 && row_ok) {
+        a.scales[row * a.G + gi] = L.s;
+        a.zeros[row * a.G + gi] = (uint8_t)L.z;
+      }
+    } else if (row_ok) {
+      L.s = a.scales[row * a.G + gi];
+      L.z = (float)a.zeros[row * a.G + gi];
+    }
+  }
+
+  run_steps<MODE>(L, a, Us, rUd, row, row_ok, std::make_integer_sequence<int, B>{});
+
+  // loss over the row's 16 lanes
+  float ls = L.loss;
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) ls += __shfl_xor(ls, m, 64);
+  if (!row_ok) return;
+  if (L.t == 0) a.row_loss[row] = (c0 == 0 ? 0.0f : a.row_loss[row]) + ls;
+  const bool full = (8 * L.t + 8 <= a.bw);
+  uint8_t* cp = a.codes + base;
+  if (full && ((cols & 7) == 0)) {
+    uint2 pk;
+    pk.x = (uint32_t)L.q[0] | ((uint32_t)L.q[1] << 8) | ((uint32_t)L.q[2] << 16) | ((uint32_t)L.q[3] << 24);
+    pk.y = (uint32_t)L.q[4] | ((uint32_t)L.q[5] << 8) | ((uint32_t)L.q[6] << 16) | ((uint32_t)L.q[7] << 24);
+    *reinterpret_cast<uint2*>(cp) = pk;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (8 * L.t + i < a.bw) cp[i] = (uint8_t)L.q[i];
+  }
+  if (a.w_hat) {
+    float* hp = a.w_hat + base;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (8 * L.t + i < a.bw) hp[i] = L.wh[i];
+  }
+  float* ep = a.E + row * B + 8 * L.t;
+  *reinterpret_cast<float4*>(ep) = make_float4(L.e[0], L.e[1], L.e[2], L.e[3]);
+  *reinterpret_cast<float4*>(ep + 4) = make_float4(L.e[4], L.e[5], L.e[6], L.e[7]);
+}
+
+}  // namespace
+
+hipError_t quant_run(const QuantArgs& q, hipStream_t stream) {
+  const int64_t rows = q.rows, cols = q.cols;
+  {
+    const int64_t total = rows * cols;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(k_stage_w, dim3((unsigned)blocks), dim3(256), 0, stream, q.W, q.w_dtype == GPTQ_BF16 ? 1 : 0,
+                       rows, cols, q.dead, q.Wf);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  BlockArgs a{};
+  a.Wf = q.Wf;
+  a.U = q.U;
+  a.rows = rows;
+  a.cols = cols;
+  a.maxq = (float)((1 << q.bits) - 1);
+  a.g = q.groupsize;
+  a.G = q.G;
+  a.codes = q.codes;
+  a.scales = q.scales;
+  a.zeros = q.zeros;
+  a.w_hat = q.w_hat;
+  a.row_loss = q.row_loss;
+  a.E = q.E;
+  const int mode = (q.groupsize == 32) ? GM_32 : (q.groupsize == 64) ? GM_64 : GM_BIG;
+  const dim3 grid((unsigned)((rows + 15) / 16));
+  for (int64_t c0 = 0; c0 < cols; c0 += B) {
+    a.c0 = c0;
+    a.bw = (int)((cols - c0) < B ? (cols - c0) : B);
+    if (mode == GM_32)
+      hipLaunchKernelGGL(k_quant_block<GM_32>, grid, dim3(256), 0, stream, a);
+    else if (mode == GM_64)
+      hipLaunchKernelGGL(k_quant_block<GM_64>, grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(k_quant_block<GM_BIG>, grid, dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t c1 = c0 + B;
+    if (c1 < cols) {
+      GemmF32 g{};
+      g.A = q.E;
+      g.lda = B;
+      g.B = q.U + c0 * cols + c1;
+      g.ldb = cols;
+      g.b_kmajor = 1;
+      g.C = q.Wf + c1;
+      g.ldc = cols;
+      g.M = (int)rows;
+      g.N = (int)(cols - c1);
+      g.K = B;
+      g.alpha = -1.0f;
+      g.beta = 1;
+      g.batch = 1;
+      e = gemm_f32(g, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace gptq
