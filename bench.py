@@ -1,0 +1,211 @@
+"""Benchmark: GPTQ layer quantization throughput on one MI355X.
+
+One step is one full pass of the layer quantizer over one linear layer with its
+calibration activations already resident in HBM: H = 0; H += 2 X^T X
+(gptq_accumulate_hessian); damping, factor and the 128-column quantize loop
+with trailing updates (gptq_quantize_layer); packing (gptq_pack).
+
+Default workload: one Llama-2-7B q_proj-shaped layer, W 4096x4096 bf16
+~N(0, 0.02^2), X 262144 tokens x 4096 bf16 Student-t(4) with 41 outlier
+channels x20, 4-bit asymmetric, groupsize 128, block 128, damp 0.01.
+
+Prints one JSON line.  Stage times come from HIP events on the stream the
+library launches on (PyTorch's current stream).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GPTQ layers/sec + TFLOP/s (4096×4096 & 11008×4096, 4-bit g128) vs MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="q_proj_4096")
+    ap.add_argument("--tokens", type=int, default=None, help="override the calibration token count")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens in the oracle's Hessian sample")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="rows in the oracle's quantize sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
+    return ap.parse_args()
+
+
+def algorithmic(rows, cols, tokens, bits):
+    """Algorithmic work of one step (SURVEY conventions: symmetric Hessian N n(n+1), factor 2n^3/3,
+    quantize rows*cols^2 of which trailing rows*cols*(cols-128))."""
+    hess = tokens * cols * (cols + 1)
+    factor = 2.0 * cols ** 3 / 3.0
+    quant = float(rows) * cols * cols
+    trailing = float(rows) * cols * max(cols - 128, 0)
+    x_bytes = 2.0 * tokens * cols
+    return {"hessian_flop": float(hess), "factor_flop": factor, "quantize_flop": quant,
+            "trailing_flop": trailing, "x_bytes": x_bytes,
+            "total_flop": float(hess) + factor + quant}
+
+
+def cpu_baseline(W, X_bits, rows, cols, tokens, bits, args):
+    """The oracle on the host cores, on a bounded sample, scaled to one full layer."""
+    from oracle import gptq_quantize, hessian_ref
+    from post_weight_quantization_03_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"),
+                      default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    nt = min(args.cpu_tokens, tokens)
+    Xs = synth.bf16_to_f32(X_bits[:nt])
+    t0 = time.perf_counter()
+    H = hessian_ref([Xs], cols)
+    t_h = time.perf_counter() - t0
+    H = H * (tokens / nt)  # a same-law stand-in for the full-token Hessian
+    nr = min(args.cpu_rows, rows)
+    Ws = synth.bf16_to_f32(W[:nr]).astype(np.float64)
+    t0 = time.perf_counter()
+    out = gptq_quantize(Ws, H, bits, 128, 0.01, blocksize=128)
+    t_fq = time.perf_counter() - t0
+    # split factor from loop: time the factor alone
+    from oracle import damp_ref, factor_ref
+    t0 = time.perf_counter()
+    Hd, _, _, _ = damp_ref(H, Ws[:1], 0.01)
+    factor_ref(Hd)
+    t_f = time.perf_counter() - t0
+    t_q = max(t_fq - t_f, 0.0)
+    est = t_h * (tokens / nt) + t_f + t_q * (rows / nr)
+    del out
+    return {"value": 1.0 / est, "unit": "layers/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle: Hessian over {nt} of {tokens} tokens (x{tokens / nt:g}), "
+                       f"full {cols}x{cols} factor, lazy-batch GPTQ loop over {nr} of {rows} rows "
+                       f"(x{rows / nr:g}); measured {t_h:.2f}s + {t_f:.2f}s + {t_q:.2f}s"),
+            "seconds_full_layer_est": est}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the Hessian would shard by tokens with one reduction, rows and layers are independent; "
+              "see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import post_weight_quantization_03_amd as g
+    from post_weight_quantization_03_amd import synth
+
+    wl = synth.workload(args.workload, tokens=args.tokens)
+    lin = wl.linears[0]
+    acts = wl.hessians[lin.hessian]
+    rows, cols, tokens, bits = lin.rows, lin.cols, acts.tokens, lin.bits
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    X_bits = acts.full()
+    W_bits = lin.weight()
+    gen_s = time.perf_counter() - t0
+    Xd = torch.from_numpy(X_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    Wd = torch.from_numpy(W_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    params = g.Params(bits=bits, groupsize=wl.groupsize, blocksize=wl.blocksize, damp=wl.damp)
+    G = -(-cols // wl.groupsize)
+    H = torch.zeros((cols, cols), dtype=torch.float32, device=dev)
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, G), dtype=torch.float32, device=dev)
+    zeros = torch.empty((rows, G), dtype=torch.uint8, device=dev)
+    loss = torch.empty((rows,), dtype=torch.float32, device=dev)
+    packed = torch.empty((rows, cols * bits // 32), dtype=torch.int32, device=dev)
+    dstat = torch.zeros((1,), dtype=torch.int32, device=dev)
+    ws_h = torch.empty(max(g.gptq_hessian_workspace_bytes(cols, tokens, g.GPTQ_BF16), 1), dtype=torch.uint8,
+                       device=dev)
+    ws_q = torch.empty(g.gptq_quantize_workspace_bytes(rows, cols, params), dtype=torch.uint8, device=dev)
+
+    if args.calib_copy:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    ev = {k: [] for k in ("h0", "h1", "q1", "p1")}
+
+    def step(record):
+        H.zero_()
+        if record:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record()
+        g.gptq_accumulate_hessian(H, Xd, workspace=ws_h)
+        if record:
+            e[1].record()
+        g.gptq_quantize_layer(Wd, H, params, codes, scales, zeros, None, loss, workspace=ws_q, d_status=dstat)
+        if record:
+            e[2].record()
+        g.gptq_pack(codes, bits, packed)
+        if record:
+            e[3].record()
+            for k, x in zip(("h0", "h1", "q1", "p1"), e):
+                ev[k].append(x)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if int(dstat.item()) != 0:
+        raise SystemExit(f"quantizer status {int(dstat.item())}: {g.gptq_status_string(int(dstat.item()))}")
+
+    t_h = float(np.mean([a.elapsed_time(b) for a, b in zip(ev["h0"], ev["h1"])])) / 1e3
+    t_q = float(np.mean([a.elapsed_time(b) for a, b in zip(ev["h1"], ev["q1"])])) / 1e3
+    t_p = float(np.mean([a.elapsed_time(b) for a, b in zip(ev["q1"], ev["p1"])])) / 1e3
+    step_s = wall / args.steps
+    alg = algorithmic(rows, cols, tokens, bits)
+    hess_tflops = alg["hessian_flop"] / t_h / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": 1.0 / step_s,
+        "unit": "layers/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.description, "rows": rows, "cols": cols, "tokens": tokens, "bits": bits,
+                   "groupsize": wl.groupsize, "blocksize": wl.blocksize, "damp": wl.damp},
+        "tflops": alg["total_flop"] / step_s / 1e12,
+        "stages_ms": {"hessian": t_h * 1e3, "factor_and_quantize": t_q * 1e3, "pack": t_p * 1e3},
+        "stage_tflops": {"hessian_bf16_mfma": hess_tflops,
+                         "factor_and_quantize_f32": (alg["factor_flop"] + alg["quantize_flop"]) / t_q / 1e12},
+        "quantize_only_layers_per_s": 1.0 / (t_q + t_p),
+        "roofline": {"bound": "mfma", "kernel": "k_syrk_bf16 (Hessian)", "achieved": hess_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": hess_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": None},
+        "input_generation_s": gen_s,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(W_bits, X_bits, rows, cols, tokens, bits, args)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -67,15 +67,22 @@ __global__ void k_reverse_damped(const float* H, int64_t n, const uint8_t* dead,
 // Factor the diagonal block A[k0:k0+kb, k0:k0+kb] (lower) and write its inverse
 // (lower, zeros above the diagonal) into Minv at the same place.
 //
-// 256 threads; thread (tr, tc) = (tid / 16, tid % 16) owns the 8x8 elements
-// (tr + 16a, tc + 16b) in registers.  Right-looking elimination with the
-// column kept unscaled: at step c, S[r][q] -= S[r][c] S[q][c] / S[c][c] for
-// c < q <= r; the owners of column c publish it to LDS first (double-buffered,
-// one barrier per step).  L[r][c] = S[r][c] / sqrt(S[c][c]).
-// The inverse X = L^-1 is formed the same way by forward elimination of the
-// identity, row c published at step c.
+// 256 threads, tr = tid / 16, tc = tid % 16, each holding 8x8 elements in
+// registers, one barrier per column, no data-dependent branches.
+//
+// Cholesky: thread owns rows tr + 16a and columns 8tc + b, so column c sits in
+// register slot c % 8 of the threads with tc == c / 8 (a compile-time slot in
+// a loop unrolled by 8).  The column is kept unscaled: at step c its owners
+// publish it to LDS, then every thread applies
+//   S[r][q] -= S[r][c] S[q][c] / S[c][c]   for c < q (and r > c)
+// with masked operands; L[r][c] = S[r][c] / sqrt(S[c][c]) at the end.
+// Inverse X = L^-1 by forward elimination of the identity: thread owns rows
+// 8tr + a and columns tc + 16b, so row c is slot c % 8 of the threads with
+// tr == c / 8; at step c the owners scale row c by 1/L[c][c] and publish it,
+// then B[r][q] -= L[r][c] X[c][q] for r > c.
 __global__ __launch_bounds__(256) void k_chol_diag(float* A, float* Minv, int64_t n, int64_t k0, int* status) {
   __shared__ float col[2][NB];
+  __shared__ float dg[NB];
   __shared__ float Ls[NB][NB + 1];
   const int kb = (int)((n - k0) < NB ? (n - k0) : NB);
   const int tid = threadIdx.x;
@@ -85,54 +92,54 @@ __global__ __launch_bounds__(256) void k_chol_diag(float* A, float* Minv, int64_
   for (int a = 0; a < 8; ++a)
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const int r = tr + 16 * a, q = tc + 16 * b;
-      S[a][b] = (r < kb && q <= r) ? A[(k0 + r) * n + k0 + q] : 0.0f;
+      const int r = tr + 16 * a, q = 8 * tc + b;
+      S[a][b] = (r < kb && q <= r) ? A[(k0 + r) * n + k0 + q] : ((r == q) ? 1.0f : 0.0f);
     }
   bool bad = false;
-  for (int c = 0; c < kb; ++c) {
-    const int buf = c & 1;
-    // publish column c (rows >= c), final after step c-1
-    if (tc == (c & 15)) {
-      const int bsel = c >> 4;
+  for (int cb = 0; cb < NB / 8; ++cb) {
+    if (8 * cb >= kb) break;
 #pragma unroll
-      for (int a = 0; a < 8; ++a)
+    for (int ci = 0; ci < 8; ++ci) {
+      const int c = 8 * cb + ci;
+      const int buf = ci & 1;
+      if (tc == cb) {
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          const int r = tr + 16 * a;
-          if (b == bsel && r >= c && r < kb) col[buf][r] = S[a][b];
-        }
-    }
-    __syncthreads();
-    float piv = col[buf][c];
-    if (!(piv > 0.0f) || !(piv < INFINITY)) {
-      bad = true;
-      piv = 1.0f;
-    }
-    const float rp = 1.0f / piv;
+        for (int a = 0; a < 8; ++a) col[buf][tr + 16 * a] = S[a][ci];
+      }
+      __syncthreads();
+      float piv = col[buf][c];
+      const bool ok = (piv > 0.0f) && (piv < INFINITY) && (c < kb);
+      bad |= (c < kb) && !ok;
+      piv = ok ? piv : 1.0f;
+      const float rp = 1.0f / piv;
+      float cq[8];
+      const float4 c0 = *reinterpret_cast<const float4*>(&col[buf][8 * tc]);
+      const float4 c1 = *reinterpret_cast<const float4*>(&col[buf][8 * tc + 4]);
+      cq[0] = c0.x; cq[1] = c0.y; cq[2] = c0.z; cq[3] = c0.w;
+      cq[4] = c1.x; cq[5] = c1.y; cq[6] = c1.z; cq[7] = c1.w;
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      const int r = tr + 16 * a;
-      if (r <= c || r >= kb) continue;
-      const float lr = col[buf][r] * rp;
+      for (int b = 0; b < 8; ++b) cq[b] = (8 * tc + b > c) ? cq[b] * rp : 0.0f;
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const int q = tc + 16 * b;
-        if (q > c && q <= r) S[a][b] -= lr * col[buf][q];
+      for (int a = 0; a < 8; ++a) {
+        if (16 * a + 15 <= c) continue;  // uniform: every row of slot a is done
+        const int r = tr + 16 * a;
+        const float lr = (r > c) ? col[buf][r] : 0.0f;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) S[a][b] = fmaf(-lr, cq[b], S[a][b]);
       }
     }
   }
   if (bad && tid == 0) raise_status(status, GPTQ_ENOTPD);
   __syncthreads();  // the last step may still be reading col[]
-  // L into LDS: diagonal sqrt(S_cc), below S_rc / sqrt(S_cc).
+  // diagonal of L
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const int r = tr + 16 * a, q = tc + 16 * b;
-      if (r < kb && q <= r && r == q) {
-        float d = S[a][b];
-        if (!(d > 0.0f) || !(d < INFINITY)) d = 1.0f;
-        col[0][r] = sqrtf(d);
+      const int r = tr + 16 * a, q = 8 * tc + b;
+      if (r == q && r < kb) {
+        const float d = S[a][b];
+        dg[r] = sqrtf((d > 0.0f && d < INFINITY) ? d : 1.0f);
       }
     }
   __syncthreads();
@@ -140,42 +147,45 @@ __global__ __launch_bounds__(256) void k_chol_diag(float* A, float* Minv, int64_
   for (int a = 0; a < 8; ++a)
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const int r = tr + 16 * a, q = tc + 16 * b;
-      if (r < NB && q < NB) Ls[r][q] = (r < kb && q <= r) ? (r == q ? col[0][r] : S[a][b] / col[0][q]) : 0.0f;
+      const int r = tr + 16 * a, q = 8 * tc + b;
+      // beyond kb the block is padded with the identity, so the unrolled steps
+      // past the last column divide by 1 and eliminate nothing
+      float v = (r == q) ? 1.0f : 0.0f;
+      if (r < kb && q < kb) v = (q < r) ? S[a][b] / dg[q] : ((q == r) ? dg[r] : 0.0f);
+      Ls[r][q] = v;
     }
   __syncthreads();
-  // X = L^-1: B starts as I; at step c, row c of X is B[c][:] / L[c][c] (q <= c);
-  // then B[r][q] -= L[r][c] X[c][q] for r > c, q <= c.
+  // inverse: rows 8tr + a, columns tc + 16b; B starts as the identity
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) S[a][b] = ((tr + 16 * a) == (tc + 16 * b)) ? 1.0f : 0.0f;
-  for (int c = 0; c < kb; ++c) {
-    const int buf = c & 1;
-    const float rl = 1.0f / Ls[c][c];
-    if (tr == (c & 15)) {
-      const int asel = c >> 4;
+    for (int b = 0; b < 8; ++b) S[a][b] = ((8 * tr + a) == (tc + 16 * b)) ? 1.0f : 0.0f;
+  for (int cb = 0; cb < NB / 8; ++cb) {
+    if (8 * cb >= kb) break;
 #pragma unroll
-      for (int a = 0; a < 8; ++a)
+    for (int ci = 0; ci < 8; ++ci) {
+      const int c = 8 * cb + ci;
+      const int buf = ci & 1;
+      if (tr == cb) {
+        const float rl = 1.0f / Ls[c][c];
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
-          const int q = tc + 16 * b;
-          if (a == asel && q <= c) {
-            S[a][b] *= rl;
-            col[buf][q] = S[a][b];
-          }
+          S[ci][b] *= rl;
+          col[buf][tc + 16 * b] = S[ci][b];
         }
-    }
-    __syncthreads();
+      }
+      __syncthreads();
+      if (32 * (tid >> 6) + 31 > c) {  // uniform per wave: its rows are 32w .. 32w+31
+        float rq[8];
 #pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      const int r = tr + 16 * a;
-      if (r <= c || r >= kb) continue;
-      const float lrc = Ls[r][c];
+        for (int b = 0; b < 8; ++b) rq[b] = col[buf][tc + 16 * b];
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const int q = tc + 16 * b;
-        if (q <= c) S[a][b] -= lrc * col[buf][q];
+        for (int a = 0; a < 8; ++a) {
+          const int r = 8 * tr + a;
+          const float lm = (r > c && r < kb) ? Ls[r][c] : 0.0f;
+#pragma unroll
+          for (int b = 0; b < 8; ++b) S[a][b] = fmaf(-lm, rq[b], S[a][b]);
+        }
       }
     }
   }
@@ -183,7 +193,7 @@ __global__ __launch_bounds__(256) void k_chol_diag(float* A, float* Minv, int64_
   for (int a = 0; a < 8; ++a)
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const int r = tr + 16 * a, q = tc + 16 * b;
+      const int r = 8 * tr + a, q = tc + 16 * b;
       if (r < kb && q < kb) Minv[(k0 + r) * n + k0 + q] = (q <= r) ? S[a][b] : 0.0f;
     }
 }

@@ -5,34 +5,36 @@
 // Only upper tiles (I <= J) are computed; each writes its block and the
 // mirrored block, so both triangles of H hold bit-identical values.
 //
-// bf16 path (v_mfma_f32_32x32x16_bf16): a lane supplies 8 consecutive k
-// (tokens) of one row/column, so token-major X is transposed on its way into
-// LDS.  Each thread loads a 4-token x 4-column block as four 8-byte reads,
-// transposes it in registers and stores four 8-byte column pieces; LDS holds
-// Xs[column][token] with an 80-byte row pitch, which keeps both the stores
-// and the 16-byte MFMA operand reads free of bank conflicts.
-// fp32 path (v_mfma_f32_32x32x2_f32): a lane supplies one k, so X stays
-// token-major in LDS and operand reads are 32 consecutive floats.
+// bf16 path (v_mfma_f32_32x32x16_bf16), 256x256 tiles: four waves in a 2x2
+// grid, each owning a 128x128 quarter as 4x4 MFMA blocks whose accumulators
+// live in AGPRs.  A lane supplies 8 consecutive k (tokens) of one row/column,
+// so token-major X is transposed on its way into LDS: each thread reads
+// 4 tokens x 8 columns as four 16-byte loads (a cache line per 8 lanes),
+// transposes in registers and stores eight 8-byte column pieces.  LDS holds
+// Xs[column][token] for 64 tokens at a 144-byte pitch, double-buffered: the
+// next stage's global loads are in flight during the current stage's 64
+// MFMAs per wave.  On diagonal tiles one operand is loaded and the wave whose
+// quarter lies below the diagonal skips its MFMAs.
 //
-// Work items are (tile, token split).  With one split an item adds 2*acc to H
-// directly.  With S splits each item stores its partial tile; the last of the
-// S items of a tile to finish (per-tile arrival counter) sums the S partials
-// in split order and writes H, so the result does not depend on scheduling.
+// fp32 path (v_mfma_f32_32x32x2_f32), 128x128 tiles for fp32 activations: a
+// lane supplies one k, so X stays token-major in LDS.
+//
+// Work items are (tile, token split) with item = tile * S + split.  Blocks are
+// dispatched to the 8 XCDs round robin, so with S a multiple of 8 every XCD
+// works on its own token range and streams only that part of X through its
+// L2.  With one split an item adds 2*acc to H directly; with S splits each
+// item stores its partial tile and the last of the S items of a tile to finish
+// (per-tile arrival counter) sums the partials in split order and writes H,
+// so the result does not depend on scheduling.
 #include "common.h"
 
 namespace gptq {
 namespace {
 
-constexpr int TILE = 128;
-constexpr int KT_BF16 = 32;   // tokens per LDS stage, bf16 path
-constexpr int KT_F32 = 16;    // tokens per LDS stage, fp32 path
-constexpr int ROWB = 40;      // LDS pitch of a column row in bf16 elements (80 bytes)
-constexpr int PARTIAL = TILE * TILE;  // floats per partial tile
-
 struct SyrkArgs {
   const void* X;
   float* H;
-  float* part;     // [T * S][PARTIAL] (S > 1)
+  float* part;     // [T * S][tile * tile] (S > 1)
   int* counters;   // [T] (S > 1)
   int64_t ldx;
   int n, tokens;
@@ -40,6 +42,8 @@ struct SyrkArgs {
   int T;           // upper tiles
   int S;           // token splits
   int tps;         // tokens per split
+  int h_vec;       // H rows are 16-byte aligned (n % 4 == 0, aligned base)
+  int h_vec_x;     // X rows are 16-byte aligned (ldx % 8 == 0, aligned base): direct loads allowed
 };
 
 __device__ __forceinline__ void decode_upper(int t, int nbt, int& I, int& J) {
@@ -53,42 +57,64 @@ __device__ __forceinline__ void decode_upper(int t, int nbt, int& I, int& J) {
   J = i + (t - base);
 }
 
-// Epilogue shared by both paths: add 2*v to H at (gr, gc) and mirror, upper tiles only.
-__device__ __forceinline__ void write_tile(const SyrkArgs& a, int I, int J, f32x16 (&acc)[2][2], int lane,
+// acc[i][j] is the 32x32 block (i, j) of this wave's (32 WB) x (32 WB) quarter.
+template <int TILE, int WB>
+__device__ __forceinline__ void write_tile(const SyrkArgs& a, int I, int J, f32x16 (&acc)[WB][WB], int lane,
                                            int wm, int wn) {
   const int n = a.n;
+  const bool vec_mirror = a.h_vec != 0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < WB; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int gr = I * TILE + wm * 64 + 32 * i + acc_row(r, lane);
-        const int gc = J * TILE + wn * 64 + 32 * j + acc_col(lane);
-        if (gr < n && gc < n && gr <= gc) {
-          float* p = a.H + (int64_t)gr * n + gc;
-          const float v = *p + 2.0f * acc[i][j][r];
-          *p = v;
-          if (gr != gc) a.H[(int64_t)gc * n + gr] = v;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int gr0 = I * TILE + wm * 32 * WB + 32 * i + acc_row(4 * r4, lane);
+        const int gc = J * TILE + wn * 32 * WB + 32 * j + acc_col(lane);
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int gr = gr0 + e;
+          v[e] = 0.f;
+          if (gr < n && gc < n && gr <= gc) {
+            float* p = a.H + (int64_t)gr * n + gc;
+            v[e] = *p + 2.0f * acc[i][j][4 * r4 + e];
+            *p = v[e];
+          }
+        }
+        // mirror: rows gr0..gr0+3 of column gc become four consecutive floats of row gc
+        if (gc < n) {
+          float* m = a.H + (int64_t)gc * n + gr0;
+          if (vec_mirror && gr0 + 3 < gc && gr0 + 3 < n) {
+            *reinterpret_cast<float4*>(m) = make_float4(v[0], v[1], v[2], v[3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (gr0 + e < gc && gr0 + e < n) m[e] = v[e];
+          }
         }
       }
 }
 
 // Split-K bookkeeping: store this item's partial; the last arrival reduces.
 // Returns true when this workgroup must write H with acc = sum of partials.
-__device__ __forceinline__ bool splitk_reduce(const SyrkArgs& a, int tile, int s, f32x16 (&acc)[2][2],
-                                              int lane, int wave) {
+// Partial layout: float4 k4 of thread tid at [(k4 * 256 + tid) * 4].
+template <int TILE, int WB>
+__device__ __forceinline__ bool splitk_reduce(const SyrkArgs& a, int tile, int s, f32x16 (&acc)[WB][WB]) {
+  constexpr int PARTIAL = TILE * TILE;
+  constexpr int NV = WB * WB * 4;  // float4s per thread
   __shared__ int last;
-  float* mine = a.part + ((int64_t)tile * a.S + s) * PARTIAL;
+  const int tid = threadIdx.x;
+  float4* mine = reinterpret_cast<float4*>(a.part + ((int64_t)tile * a.S + s) * PARTIAL);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mine[(((wave * 4 + i * 2 + j) * 16 + r) << 6) + lane] = acc[i][j][r];
+  for (int k = 0; k < NV; ++k) {
+    const int i = k / (4 * WB), j = (k / 4) % WB, r4 = k % 4;
+    mine[k * 256 + tid] = make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2],
+                                      acc[i][j][4 * r4 + 3]);
+  }
   __threadfence();
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     const int prev = atomicAdd(a.counters + tile, 1);
     last = (prev == a.S - 1);
   }
@@ -96,81 +122,132 @@ __device__ __forceinline__ bool splitk_reduce(const SyrkArgs& a, int tile, int s
   if (!last) return false;
   __threadfence();
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < WB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   for (int q = 0; q < a.S; ++q) {
-    const float* pq = a.part + ((int64_t)tile * a.S + q) * PARTIAL;
+    const float4* pq = reinterpret_cast<const float4*>(a.part + ((int64_t)tile * a.S + q) * PARTIAL) + tid;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          acc[i][j][r] += pq[(((wave * 4 + i * 2 + j) * 16 + r) << 6) + lane];
+    for (int k = 0; k < NV; ++k) {
+      const int i = k / (4 * WB), j = (k / 4) % WB, r4 = k % 4;
+      const float4 v = pq[k * 256];
+      acc[i][j][4 * r4] += v.x;
+      acc[i][j][4 * r4 + 1] += v.y;
+      acc[i][j][4 * r4 + 2] += v.z;
+      acc[i][j][4 * r4 + 3] += v.w;
+    }
   }
-  if (threadIdx.x == 0) a.counters[tile] = 0;  // ready for the next call
+  if (tid == 0) a.counters[tile] = 0;  // ready for the next call
   return true;
 }
 
 // ------------------------------------------------------------------ bf16 path
 
-struct Blk4x4 {
-  uint2 v[4];  // v[i] = 4 bf16 of token i (columns c..c+3)
-};
+constexpr int TB = 256;             // tile
+constexpr int KB = 64;              // tokens per LDS stage
+constexpr int ROWB = TB * 2;        // bytes per token row of one operand stage (no padding)
+constexpr int STAGEB = KB * ROWB;   // 32 KB per operand stage
 
-template <bool VEC>
-__device__ __forceinline__ void load_bf16(const SyrkArgs& a, const uint16_t* X, int col0, int t, int t1,
-                                          int q, int cg, Blk4x4& b) {
-  const int c = col0 + 4 * cg;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Byte offset of element (row = token, col) in a stage buffer.  The 16-byte
+// chunk index is XORed with 4 * (row & 3), so the transposing operand reads
+// (4 consecutive rows x 4 chunks per 32 lanes) hit 16 distinct bank groups.
+__device__ __forceinline__ int sw_off(int row, int col) {
+  const int phys = (col >> 3) ^ ((row & 3) << 2);
+  return row * ROWB + (phys << 4) + ((col & 7) << 1);
+}
+
+// Fast path: the whole stage lies inside X.  Each wave copies 16 token rows
+// with 8 direct global->LDS loads of 16 bytes per lane (2 rows per load; lane
+// p lands at chunk position p & 31 and fetches the chunk that the swizzle
+// places there).
+__device__ __forceinline__ void stage_direct(const SyrkArgs& a, const uint16_t* X, int col0, int t,
+                                             char* buf, int wave, int lane) {
+  const int pos = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tok = t + 4 * q + i;
-    const uint16_t* p = X + (int64_t)tok * a.ldx + c;
-    if (VEC && tok < t1 && c + 3 < a.n) {
-      b.v[i] = *reinterpret_cast<const uint2*>(p);
-    } else {
-      uint16_t e[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) e[k] = (tok < t1 && c + k < a.n) ? p[k] : (uint16_t)0;
-      b.v[i].x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
-      b.v[i].y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int r0 = 16 * wave + 2 * i;
+    const int row = r0 + (lane >> 5);
+    const int gchunk = pos ^ ((row & 3) << 2);
+    const uint16_t* src = X + (int64_t)(t + row) * a.ldx + col0 + 8 * gchunk;
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + r0 * ROWB), 16, 0, 0);
   }
 }
 
-// Transposes the 4x4 block and stores four 8-byte column pieces: Xs[col][4q .. 4q+3].
-__device__ __forceinline__ void store_bf16(uint16_t (*Xs)[ROWB], int q, int cg, const Blk4x4& b) {
-  // column k of the block, tokens 0..3: low/high halves of v[i].x (k = 0, 1) or v[i].y (k = 2, 3)
-  const uint32_t x0 = b.v[0].x, x1 = b.v[1].x, x2 = b.v[2].x, x3 = b.v[3].x;
-  const uint32_t y0 = b.v[0].y, y1 = b.v[1].y, y2 = b.v[2].y, y3 = b.v[3].y;
-  uint2 c0, c1, c2, c3;
-  c0.x = (x0 & 0xffffu) | (x1 << 16);          // tok0.col0 | tok1.col0
-  c0.y = (x2 & 0xffffu) | (x3 << 16);          // tok2.col0 | tok3.col0
-  c1.x = (x0 >> 16) | (x1 & 0xffff0000u);      // tok0.col1 | tok1.col1
-  c1.y = (x2 >> 16) | (x3 & 0xffff0000u);
-  c2.x = (y0 & 0xffffu) | (y1 << 16);
-  c2.y = (y2 & 0xffffu) | (y3 << 16);
-  c3.x = (y0 >> 16) | (y1 & 0xffff0000u);
-  c3.y = (y2 >> 16) | (y3 & 0xffff0000u);
-  const int col = 4 * cg;
-  *reinterpret_cast<uint2*>(&Xs[col + 0][4 * q]) = c0;
-  *reinterpret_cast<uint2*>(&Xs[col + 1][4 * q]) = c1;
-  *reinterpret_cast<uint2*>(&Xs[col + 2][4 * q]) = c2;
-  *reinterpret_cast<uint2*>(&Xs[col + 3][4 * q]) = c3;
+// Guarded path for ragged stages or tiles: zero-filled register loads and
+// 16-byte LDS stores into the same swizzled layout.
+__device__ __forceinline__ void stage_guarded(const SyrkArgs& a, const uint16_t* X, int col0, int t, int t1,
+                                              char* buf) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = threadIdx.x + 256 * i;
+    const int row = idx >> 5, c = idx & 31;
+    const int tok = t + row, col = col0 + 8 * c;
+    const uint16_t* p = X + (int64_t)tok * a.ldx + col;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = (tok < t1 && col + 2 * k < a.n) ? p[2 * k] : 0u;
+      const uint32_t hi = (tok < t1 && col + 2 * k + 1 < a.n) ? p[2 * k + 1] : 0u;
+      w[k] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint4*>(buf + sw_off(row, 8 * c)) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
 }
 
-__device__ __forceinline__ bf16x8 frag_bf16(const uint16_t (*Xs)[ROWB], int row, int chunk) {
-  const uint4 v = *reinterpret_cast<const uint4*>(&Xs[row][8 * chunk]);
+// MFMA operand of the 32-column block at m0 for tokens 16kk .. 16kk+15.  In a
+// 16-lane group, source lane s points at 4 columns (m0 + 16(g&1) + 4(s&3)) of
+// token row 16kk + 8(g>>1) + s/4; the transposing read hands lane l of the
+// group 4 consecutive tokens of column m0 + 16(g&1) + l.  Two reads give the
+// 8 tokens a lane supplies to v_mfma_f32_32x32x16_bf16.
+__device__ __forceinline__ bf16x8 frag_tr(const char* buf, int m0, int kk, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int col = m0 + 16 * (g & 1) + 4 * (s & 3);
+  const int row = 16 * kk + 8 * (g >> 1) + (s >> 2);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + sw_off(row, col)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + sw_off(row + 4, col)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <bool VEC>
-__global__ __launch_bounds__(256) void k_syrk_bf16(SyrkArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][TILE][ROWB];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][TILE][ROWB];
+struct StageFrags {
+  bf16x8 a[KB / 16][4], b[KB / 16][4];
+};
+
+__device__ __forceinline__ void read_frags(const char* Ab, const char* Bb, int wm, int wn, int lane,
+                                           StageFrags& f) {
+#pragma unroll
+  for (int kk = 0; kk < KB / 16; ++kk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[kk][i] = frag_tr(Ab, wm * 128 + 32 * i, kk, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.b[kk][j] = frag_tr(Bb, wn * 128 + 32 * j, kk, lane);
+  }
+}
+
+__device__ __forceinline__ void mfma_frags(const StageFrags& f, f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int kk = 0; kk < KB / 16; ++kk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j], acc[i][j], 0, 0, 0);
+}
+
+// FULL: every tile is inside X and every stage holds 64 tokens (n % 256 == 0,
+// tokens % 64 == 0, 16-byte aligned rows), so only direct loads are compiled.
+template <bool FULL>
+__global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
+  // two stage buffers, each [operand A | operand B]
+  __shared__ __attribute__((aligned(16))) char L0[2 * STAGEB];
+  __shared__ __attribute__((aligned(16))) char L1[2 * STAGEB];
 
   const int item = blockIdx.x;
   const int tile = item / a.S, s = item % a.S;
@@ -182,62 +259,73 @@ __global__ __launch_bounds__(256) void k_syrk_bf16(SyrkArgs a) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int q = lane & 7, cg = (lane >> 3) + 8 * wave;
+  const bool idle = diag && wm > wn;  // quarter strictly below the diagonal
   const uint16_t* X = static_cast<const uint16_t*>(a.X);
+  const int colA = I * TB, colB = J * TB;
+  const bool fullA = a.h_vec_x && colA + TB <= a.n;
+  const bool fullB = a.h_vec_x && colB + TB <= a.n;
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  if (t0 < t1) {
-    Blk4x4 ba, bb;
-    load_bf16<VEC>(a, X, I * TILE, t0, t1, q, cg, ba);
-    if (!diag) load_bf16<VEC>(a, X, J * TILE, t0, t1, q, cg, bb);
-    store_bf16(As[0], q, cg, ba);
-    if (!diag) store_bf16(Bs[0], q, cg, bb);
+  auto issue = [&](int t, char* buf) {
+    if constexpr (FULL) {
+      stage_direct(a, X, colA, t, buf, wave, lane);
+      if (!diag) stage_direct(a, X, colB, t, buf + STAGEB, wave, lane);
+      return;
+    }
+    const bool full_t = t + KB <= t1;
+    if (full_t && fullA)
+      stage_direct(a, X, colA, t, buf, wave, lane);
+    else
+      stage_guarded(a, X, colA, t, t1, buf);
+    if (!diag) {
+      if (full_t && fullB)
+        stage_direct(a, X, colB, t, buf + STAGEB, wave, lane);
+      else
+        stage_guarded(a, X, colB, t, t1, buf + STAGEB);
+    }
+  };
+
+  // One stage: read all operand fragments of the current buffer into
+  // registers, then queue the next stage's loads into the other buffer, then
+  // run the MFMAs.  The wait for those loads therefore falls before the next
+  // stage's fragment reads, after this stage's MFMAs.
+  auto stage = [&](const char* cur, int tnext, char* nxt) {
+    StageFrags f;
+    if (!idle) read_frags(cur, diag ? cur : cur + STAGEB, wm, wn, lane, f);
+    if (tnext < t1) issue(tnext, nxt);
+    if (!idle) mfma_frags(f, acc);
     __syncthreads();
-    int buf = 0;
-    for (int t = t0; t < t1; t += KT_BF16) {
-      const bool more = t + KT_BF16 < t1;
-      if (more) {
-        load_bf16<VEC>(a, X, I * TILE, t + KT_BF16, t1, q, cg, ba);
-        if (!diag) load_bf16<VEC>(a, X, J * TILE, t + KT_BF16, t1, q, cg, bb);
-      }
-      const uint16_t(*Bsrc)[ROWB] = diag ? As[buf] : Bs[buf];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int chunk = 2 * kk + (lane >> 5);
-        const bf16x8 a0 = frag_bf16(As[buf], wm * 64 + (lane & 31), chunk);
-        const bf16x8 a1 = frag_bf16(As[buf], wm * 64 + 32 + (lane & 31), chunk);
-        const bf16x8 b0 = frag_bf16(Bsrc, wn * 64 + (lane & 31), chunk);
-        const bf16x8 b1 = frag_bf16(Bsrc, wn * 64 + 32 + (lane & 31), chunk);
-        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0][0], 0, 0, 0);
-        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[0][1], 0, 0, 0);
-        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[1][0], 0, 0, 0);
-        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1][1], 0, 0, 0);
-      }
-      if (more) {
-        store_bf16(As[buf ^ 1], q, cg, ba);
-        if (!diag) store_bf16(Bs[buf ^ 1], q, cg, bb);
-        __syncthreads();
-        buf ^= 1;
-      }
+  };
+
+  if (t0 < t1) {
+    issue(t0, L0);
+    __syncthreads();
+    // two stages per trip so each buffer is a distinct LDS object
+    for (int t = t0; t < t1; t += 2 * KB) {
+      stage(L0, t + KB, L1);
+      if (t + KB >= t1) break;
+      stage(L1, t + 2 * KB, L0);
     }
   }
 
   if (a.S > 1) {
-    if (!splitk_reduce(a, tile, s, acc, lane, wave)) return;
+    if (!splitk_reduce<TB, 4>(a, tile, s, acc)) return;
   }
-  write_tile(a, I, J, acc, lane, wm, wn);
+  if (!idle) write_tile<TB, 4>(a, I, J, acc, lane, wm, wn);
 }
 
 // ------------------------------------------------------------------ fp32 path
 
-constexpr int F32_PITCH = TILE + 4;
+constexpr int TF = 128;          // tile
+constexpr int KT_F32 = 16;       // tokens per LDS stage
+constexpr int F32_PITCH = TF + 4;
 
 template <bool VEC>
 __device__ __forceinline__ void load_f32(const SyrkArgs& a, const float* X, int col0, int t, int t1,
@@ -292,8 +380,8 @@ __global__ __launch_bounds__(256) void k_syrk_f32(SyrkArgs a) {
 
   if (t0 < t1) {
     float4 va[2], vb[2];
-    load_f32<VEC>(a, X, I * TILE, t0, t1, va);
-    if (!diag) load_f32<VEC>(a, X, J * TILE, t0, t1, vb);
+    load_f32<VEC>(a, X, I * TF, t0, t1, va);
+    if (!diag) load_f32<VEC>(a, X, J * TF, t0, t1, vb);
     store_f32(As[0], va);
     if (!diag) store_f32(Bs[0], vb);
     __syncthreads();
@@ -301,8 +389,8 @@ __global__ __launch_bounds__(256) void k_syrk_f32(SyrkArgs a) {
     for (int t = t0; t < t1; t += KT_F32) {
       const bool more = t + KT_F32 < t1;
       if (more) {
-        load_f32<VEC>(a, X, I * TILE, t + KT_F32, t1, va);
-        if (!diag) load_f32<VEC>(a, X, J * TILE, t + KT_F32, t1, vb);
+        load_f32<VEC>(a, X, I * TF, t + KT_F32, t1, va);
+        if (!diag) load_f32<VEC>(a, X, J * TF, t + KT_F32, t1, vb);
       }
       float(*Bsrc)[F32_PITCH] = diag ? As[buf] : Bs[buf];
 #pragma unroll
@@ -327,9 +415,9 @@ __global__ __launch_bounds__(256) void k_syrk_f32(SyrkArgs a) {
   }
 
   if (a.S > 1) {
-    if (!splitk_reduce(a, tile, s, acc, lane, wave)) return;
+    if (!splitk_reduce<TF, 2>(a, tile, s, acc)) return;
   }
-  write_tile(a, I, J, acc, lane, wm, wn);
+  write_tile<TF, 2>(a, I, J, acc, lane, wm, wn);
 }
 
 __global__ void k_zero_i32(int* p, int n) {
@@ -337,61 +425,74 @@ __global__ void k_zero_i32(int* p, int n) {
   if (i < n) p[i] = 0;
 }
 
-// Work decomposition: enough (tile, split) items to keep every CU busy, with
-// at least 512 tokens per split.
-void plan(int64_t n, int64_t tokens, gptq_dtype dt, int& nbt, int& T, int& S, int& tps) {
-  nbt = (int)((n + TILE - 1) / TILE);
-  T = nbt * (nbt + 1) / 2;
-  const int kt = dt == GPTQ_BF16 ? KT_BF16 : KT_F32;
-  const int64_t target = 1024;
-  int64_t s = (target + T - 1) / T;
-  const int64_t max_s = (tokens + 511) / 512;
-  if (s > max_s) s = max_s;
-  if (s < 1) s = 1;
+struct Plan {
+  int tile, nbt, T, S, tps;
+};
+
+// Work decomposition.  bf16: with fewer than three upper tiles per CU the
+// tokens are split 8 ways (one split per XCD), else not at all.  fp32 (small
+// problems): enough items for the chip with at least 512 tokens per split.
+Plan plan(int64_t n, int64_t tokens, gptq_dtype dt) {
+  Plan p{};
+  p.tile = dt == GPTQ_BF16 ? TB : TF;
+  p.nbt = (int)((n + p.tile - 1) / p.tile);
+  p.T = p.nbt * (p.nbt + 1) / 2;
+  const int kt = dt == GPTQ_BF16 ? KB : KT_F32;
+  int64_t s;
+  if (dt == GPTQ_BF16) {
+    s = (p.T >= 768 || tokens < 8 * 2 * KB) ? 1 : 8;
+  } else {
+    const int64_t target = 1024;
+    s = (target + p.T - 1) / p.T;
+    const int64_t max_s = (tokens + 511) / 512;
+    if (s > max_s) s = max_s;
+    if (s < 1) s = 1;
+  }
   int64_t per = (tokens + s - 1) / s;
   per = (per + kt - 1) / kt * kt;
   s = (tokens + per - 1) / per;
   if (s < 1) s = 1;
-  S = (int)s;
-  tps = (int)per;
+  p.S = (int)s;
+  p.tps = (int)per;
+  return p;
 }
 
 }  // namespace
 
 size_t hessian_workspace(int64_t n, int64_t tokens, gptq_dtype dt) {
   if (n <= 0 || tokens <= 0) return 0;
-  int nbt, T, S, tps;
-  plan(n, tokens, dt, nbt, T, S, tps);
-  if (S == 1) return 0;
-  return align_up((size_t)T * S * PARTIAL * sizeof(float), 256) + align_up((size_t)T * sizeof(int), 256);
+  const Plan p = plan(n, tokens, dt);
+  if (p.S == 1) return 0;
+  return align_up((size_t)p.T * p.S * p.tile * p.tile * sizeof(float), 256) +
+         align_up((size_t)p.T * sizeof(int), 256);
 }
 
 int hessian_launch(float* H, int64_t n, const void* X, gptq_dtype dt, int64_t tokens, int64_t ldx, void* ws,
                    size_t ws_bytes, hipStream_t stream) {
-  int nbt, T, S, tps;
-  plan(n, tokens, dt, nbt, T, S, tps);
+  const Plan p = plan(n, tokens, dt);
   SyrkArgs a{};
   a.X = X;
   a.H = H;
   a.ldx = ldx;
   a.n = (int)n;
   a.tokens = (int)tokens;
-  a.nbt = nbt;
-  a.T = T;
-  a.S = S;
-  a.tps = tps;
-  if (S > 1) {
+  a.nbt = p.nbt;
+  a.T = p.T;
+  a.S = p.S;
+  a.tps = p.tps;
+  a.h_vec = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(H) & 15) == 0);
+  if (p.S > 1) {
     if (ws_bytes < hessian_workspace(n, tokens, dt) || ws == nullptr) return GPTQ_EWORKSPACE;
     a.part = static_cast<float*>(ws);
     a.counters = reinterpret_cast<int*>(static_cast<char*>(ws) +
-                                        align_up((size_t)T * S * PARTIAL * sizeof(float), 256));
-    hipLaunchKernelGGL(k_zero_i32, dim3((T + 255) / 256), dim3(256), 0, stream, a.counters, T);
+                                        align_up((size_t)p.T * p.S * p.tile * p.tile * sizeof(float), 256));
+    hipLaunchKernelGGL(k_zero_i32, dim3((p.T + 255) / 256), dim3(256), 0, stream, a.counters, p.T);
     if (hipGetLastError() != hipSuccess) return GPTQ_EHIP;
   }
-  const dim3 grid((unsigned)(T * S));
+  const dim3 grid((unsigned)(p.T * p.S));
   if (dt == GPTQ_BF16) {
-    const bool vec = (ldx % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & 7) == 0);
-    if (vec)
+    a.h_vec_x = (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+    if (a.h_vec_x && n % TB == 0 && tokens % KB == 0)
       hipLaunchKernelGGL(k_syrk_bf16<true>, grid, dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL(k_syrk_bf16<false>, grid, dim3(256), 0, stream, a);
