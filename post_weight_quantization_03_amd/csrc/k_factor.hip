@@ -64,137 +64,142 @@ __global__ void k_reverse_damped(const float* H, int64_t n, const uint8_t* dead,
   }
 }
 
-// Factor the diagonal block A[k0:k0+kb, k0:k0+kb] (lower) and write its inverse
-// (lower, zeros above the diagonal) into Minv at the same place.
+// Factor the diagonal block A[k0:k0+kb, k0:k0+kb] (lower) and write the
+// inverse of its Cholesky factor (lower, zeros above the diagonal) into Minv
+// at the same place.
 //
-// 256 threads, tr = tid / 16, tc = tid % 16, each holding 8x8 elements in
-// registers, one barrier per column, no data-dependent branches.
+// 256 threads, tr = tid / 16, tc = tid % 16; each thread holds the elements
+// (tr + 16a, tc + 16b), a, b = 0..7, of two 128x128 register arrays: S, the
+// block under elimination, and B, the inverse being formed.  Column c of the
+// block lives in register slot c / 16 of the lanes with tc == c % 16; the
+// slot is a template parameter, so finished rows and columns are skipped at
+// compile time.
 //
-// Cholesky: thread owns rows tr + 16a and columns 8tc + b, so column c sits in
-// register slot c % 8 of the threads with tc == c / 8 (a compile-time slot in
-// a loop unrolled by 8).  The column is kept unscaled: at step c its owners
-// publish it to LDS, then every thread applies
-//   S[r][q] -= S[r][c] S[q][c] / S[c][c]   for c < q (and r > c)
-// with masked operands; L[r][c] = S[r][c] / sqrt(S[c][c]) at the end.
-// Inverse X = L^-1 by forward elimination of the identity: thread owns rows
-// 8tr + a and columns tc + 16b, so row c is slot c % 8 of the threads with
-// tr == c / 8; at step c the owners scale row c by 1/L[c][c] and publish it,
-// then B[r][q] -= L[r][c] X[c][q] for r > c.
-__global__ __launch_bounds__(256) void k_chol_diag(float* A, float* Minv, int64_t n, int64_t k0, int* status) {
-  __shared__ float col[2][NB];
-  __shared__ float dg[NB];
-  __shared__ float Ls[NB][NB + 1];
-  const int kb = (int)((n - k0) < NB ? (n - k0) : NB);
-  const int tid = threadIdx.x;
-  const int tr = tid >> 4, tc = tid & 15;
+// Step c (one barrier) does two things:
+//  * Cholesky, right-looking with the column left unscaled: the owners of
+//    column c publish it, then S[r][q] -= S[r][c] S[q][c] / S[c][c] for
+//    r, q > c.  L[r][c] = S[r][c] / sqrt(S[c][c]).
+//  * inverse by forward elimination of the identity, one row behind: the
+//    owners of row c-1 scale it by 1 / L[c-1][c-1] and publish it, then
+//    B[r][q] -= L[r][c-1] X[c-1][q] for r > c-1, q <= c-1.
+// L itself is never stored.  Columns are triple-buffered in LDS (step c reads
+// columns c and c-1 while step c+1 publishes column c+1), rows double-buffered.
+// Beyond kb the block is padded with the identity.  Pivot reciprocals use the
+// hardware reciprocal and reciprocal square root (1 ulp).
+namespace chol {
+
+struct Ctx {
   float S[8][8];
+  float B[8][8];
+  int tr, tc, kb;
+  bool bad;
+};
+
+__device__ __forceinline__ float sane(float piv) { return (piv > 0.0f && piv < INFINITY) ? piv : 1.0f; }
+
+// K: slot of column c = 16K + L.  KP: slot of c - 1.
+template <int K, int KP>
+__device__ __forceinline__ void step(Ctx& x, float (*col)[NB], float (*row)[NB], int c) {
+  const int L = c & 15, P = c - 1, LP = P & 15;
+  float* colC = col[c % 3];
+  const float* colP = col[(c + 2) % 3];
+  float* rowP = row[P & 1];
+  // publish column c (Cholesky) and row c - 1 of the inverse
+  if (K < 8 && x.tc == L) {
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+    for (int a = (K < 8 ? K : 7); a < 8; ++a) colC[x.tr + 16 * a] = x.S[a][K < 8 ? K : 7];
+  }
+  if (KP >= 0 && c >= 1 && x.tr == LP) {
+    const float rl = __builtin_amdgcn_rsqf(sane(colP[P]));
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int r = tr + 16 * a, q = 8 * tc + b;
-      S[a][b] = (r < kb && q <= r) ? A[(k0 + r) * n + k0 + q] : ((r == q) ? 1.0f : 0.0f);
-    }
-  bool bad = false;
-  for (int cb = 0; cb < NB / 8; ++cb) {
-    if (8 * cb >= kb) break;
-#pragma unroll
-    for (int ci = 0; ci < 8; ++ci) {
-      const int c = 8 * cb + ci;
-      const int buf = ci & 1;
-      if (tc == cb) {
-#pragma unroll
-        for (int a = 0; a < 8; ++a) col[buf][tr + 16 * a] = S[a][ci];
-      }
-      __syncthreads();
-      float piv = col[buf][c];
-      const bool ok = (piv > 0.0f) && (piv < INFINITY) && (c < kb);
-      bad |= (c < kb) && !ok;
-      piv = ok ? piv : 1.0f;
-      const float rp = 1.0f / piv;
-      float cq[8];
-      const float4 c0 = *reinterpret_cast<const float4*>(&col[buf][8 * tc]);
-      const float4 c1 = *reinterpret_cast<const float4*>(&col[buf][8 * tc + 4]);
-      cq[0] = c0.x; cq[1] = c0.y; cq[2] = c0.z; cq[3] = c0.w;
-      cq[4] = c1.x; cq[5] = c1.y; cq[6] = c1.z; cq[7] = c1.w;
-#pragma unroll
-      for (int b = 0; b < 8; ++b) cq[b] = (8 * tc + b > c) ? cq[b] * rp : 0.0f;
-#pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        if (16 * a + 15 <= c) continue;  // uniform: every row of slot a is done
-        const int r = tr + 16 * a;
-        const float lr = (r > c) ? col[buf][r] : 0.0f;
-#pragma unroll
-        for (int b = 0; b < 8; ++b) S[a][b] = fmaf(-lr, cq[b], S[a][b]);
-      }
+    for (int b = 0; b <= (KP >= 0 ? KP : 0); ++b) {
+      x.B[KP >= 0 ? KP : 0][b] *= rl;
+      rowP[x.tc + 16 * b] = x.B[KP >= 0 ? KP : 0][b];
     }
   }
-  if (bad && tid == 0) raise_status(status, GPTQ_ENOTPD);
-  __syncthreads();  // the last step may still be reading col[]
-  // diagonal of L
-#pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int r = tr + 16 * a, q = 8 * tc + b;
-      if (r == q && r < kb) {
-        const float d = S[a][b];
-        dg[r] = sqrtf((d > 0.0f && d < INFINITY) ? d : 1.0f);
-      }
-    }
   __syncthreads();
+  if (K < 8) {
+    constexpr int KK = K < 8 ? K : 7;
+    const float piv0 = colC[c];
+    x.bad |= (c < x.kb) && !(piv0 > 0.0f && piv0 < INFINITY);
+    const float rp = __builtin_amdgcn_rcpf(sane(piv0));
+    float cq[8];
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int r = tr + 16 * a, q = 8 * tc + b;
-      // beyond kb the block is padded with the identity, so the unrolled steps
-      // past the last column divide by 1 and eliminate nothing
-      float v = (r == q) ? 1.0f : 0.0f;
-      if (r < kb && q < kb) v = (q < r) ? S[a][b] / dg[q] : ((q == r) ? dg[r] : 0.0f);
-      Ls[r][q] = v;
+    for (int b = KK; b < 8; ++b) {
+      const float v = colC[x.tc + 16 * b] * rp;
+      cq[b] = (b == KK && x.tc <= L) ? 0.0f : v;
     }
-  __syncthreads();
-  // inverse: rows 8tr + a, columns tc + 16b; B starts as the identity
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+    for (int a = KK; a < 8; ++a) {
+      float lr = colC[x.tr + 16 * a];
+      if (a == KK && x.tr <= L) lr = 0.0f;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) S[a][b] = ((8 * tr + a) == (tc + 16 * b)) ? 1.0f : 0.0f;
-  for (int cb = 0; cb < NB / 8; ++cb) {
-    if (8 * cb >= kb) break;
-#pragma unroll
-    for (int ci = 0; ci < 8; ++ci) {
-      const int c = 8 * cb + ci;
-      const int buf = ci & 1;
-      if (tr == cb) {
-        const float rl = 1.0f / Ls[c][c];
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          S[ci][b] *= rl;
-          col[buf][tc + 16 * b] = S[ci][b];
-        }
-      }
-      __syncthreads();
-      if (32 * (tid >> 6) + 31 > c) {  // uniform per wave: its rows are 32w .. 32w+31
-        float rq[8];
-#pragma unroll
-        for (int b = 0; b < 8; ++b) rq[b] = col[buf][tc + 16 * b];
-#pragma unroll
-        for (int a = 0; a < 8; ++a) {
-          const int r = 8 * tr + a;
-          const float lm = (r > c && r < kb) ? Ls[r][c] : 0.0f;
-#pragma unroll
-          for (int b = 0; b < 8; ++b) S[a][b] = fmaf(-lm, rq[b], S[a][b]);
-        }
-      }
+      for (int b = KK; b < 8; ++b) x.S[a][b] = fmaf(-lr, cq[b], x.S[a][b]);
     }
   }
+  if (KP >= 0 && c >= 1) {
+    constexpr int KQ = KP >= 0 ? KP : 0;
+    const float rl = __builtin_amdgcn_rsqf(sane(colP[P]));
+    float rq[8];
+#pragma unroll
+    for (int b = 0; b <= KQ; ++b) rq[b] = rowP[x.tc + 16 * b];
+#pragma unroll
+    for (int a = KQ; a < 8; ++a) {
+      float lm = colP[x.tr + 16 * a] * rl;
+      if (a == KQ && x.tr <= LP) lm = 0.0f;
+#pragma unroll
+      for (int b = 0; b <= KQ; ++b) x.B[a][b] = fmaf(-lm, rq[b], x.B[a][b]);
+    }
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void slot(Ctx& x, float (*col)[NB], float (*row)[NB]) {
+  const int c0 = 16 * K;
+  if (c0 > x.kb) return;
+  step<K, K - 1>(x, col, row, c0);  // row c0 - 1 belongs to the previous slot
+  if (K < 8) {
+    for (int l = 1; l < 16; ++l) {
+      if (c0 + l > x.kb) return;
+      step<K, K>(x, col, row, c0 + l);
+    }
+  }
+}
+
+}  // namespace chol
+
+__global__ __launch_bounds__(256) void k_chol_diag(float* A, float* Minv, int64_t n, int64_t k0, int* status) {
+  __shared__ float col[3][NB];
+  __shared__ float row[2][NB];
+  chol::Ctx x;
+  x.kb = (int)((n - k0) < NB ? (n - k0) : NB);
+  x.tr = threadIdx.x >> 4;
+  x.tc = threadIdx.x & 15;
+  x.bad = false;
 #pragma unroll
   for (int a = 0; a < 8; ++a)
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const int r = 8 * tr + a, q = tc + 16 * b;
-      if (r < kb && q < kb) Minv[(k0 + r) * n + k0 + q] = (q <= r) ? S[a][b] : 0.0f;
+      const int r = x.tr + 16 * a, q = x.tc + 16 * b;
+      x.S[a][b] = (r < x.kb && q <= r) ? A[(k0 + r) * n + k0 + q] : ((r == q) ? 1.0f : 0.0f);
+      x.B[a][b] = (r == q) ? 1.0f : 0.0f;
+    }
+  chol::slot<0>(x, col, row);
+  chol::slot<1>(x, col, row);
+  chol::slot<2>(x, col, row);
+  chol::slot<3>(x, col, row);
+  chol::slot<4>(x, col, row);
+  chol::slot<5>(x, col, row);
+  chol::slot<6>(x, col, row);
+  chol::slot<7>(x, col, row);
+  chol::slot<8>(x, col, row);  // the inverse's last row
+  if (x.bad) raise_status(status, GPTQ_ENOTPD);
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int r = x.tr + 16 * a, q = x.tc + 16 * b;
+      if (r < x.kb && q < x.kb) Minv[(k0 + r) * n + k0 + q] = (q <= r) ? x.B[a][b] : 0.0f;
     }
 }
 

@@ -7,14 +7,22 @@
 //
 // bf16 path (v_mfma_f32_32x32x16_bf16), 256x256 tiles: four waves in a 2x2
 // grid, each owning a 128x128 quarter as 4x4 MFMA blocks whose accumulators
-// live in AGPRs.  A lane supplies 8 consecutive k (tokens) of one row/column,
-// so token-major X is transposed on its way into LDS: each thread reads
-// 4 tokens x 8 columns as four 16-byte loads (a cache line per 8 lanes),
-// transposes in registers and stores eight 8-byte column pieces.  LDS holds
-// Xs[column][token] for 64 tokens at a 144-byte pitch, double-buffered: the
-// next stage's global loads are in flight during the current stage's 64
-// MFMAs per wave.  On diagonal tiles one operand is loaded and the wave whose
-// quarter lies below the diagonal skips its MFMAs.
+// live in AGPRs.  A stage is 32 tokens of both column slabs.  Global memory is
+// copied into LDS by direct loads (global_load_lds, 16 bytes a lane, no
+// registers), token-major: a 256-column slab of one token is a 512-byte LDS
+// row.  An MFMA operand needs 8 consecutive tokens of one column per lane;
+// ds_read_b64_tr_b16 returns exactly that from token-major rows, so the
+// transpose happens on the read.  The 16-byte chunks of each row are XOR
+// swizzled by the row's low bits so the transposing reads of a 16-lane group
+// hit distinct banks.
+//
+// Four LDS buffers per operand rotate: loads run four stages ahead of the
+// MFMAs, and each buffer is read at least one full stage after the barrier
+// that retired its loads (reading it in the very stage whose barrier waited on
+// the loads was seen to return stale data).  The barrier waits with a counted
+// vmcnt so later stages' loads stay in flight.  On diagonal tiles one operand
+// is loaded and the wave whose quarter lies below the diagonal skips its
+// MFMAs.
 //
 // fp32 path (v_mfma_f32_32x32x2_f32), 128x128 tiles for fp32 activations: a
 // lane supplies one k, so X stays token-major in LDS.
@@ -146,9 +154,9 @@ __device__ __forceinline__ bool splitk_reduce(const SyrkArgs& a, int tile, int s
 // ------------------------------------------------------------------ bf16 path
 
 constexpr int TB = 256;             // tile
-constexpr int KB = 64;              // tokens per LDS stage
+constexpr int KB = 32;              // tokens per LDS stage
 constexpr int ROWB = TB * 2;        // bytes per token row of one operand stage (no padding)
-constexpr int STAGEB = KB * ROWB;   // 32 KB per operand stage
+constexpr int STAGEB = KB * ROWB;   // 16 KB per operand stage
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -162,21 +170,38 @@ __device__ __forceinline__ int sw_off(int row, int col) {
   return row * ROWB + (phys << 4) + ((col & 7) << 1);
 }
 
-// Fast path: the whole stage lies inside X.  Each wave copies 16 token rows
-// with 8 direct global->LDS loads of 16 bytes per lane (2 rows per load; lane
+// Fast path: the whole stage lies inside X.  Each wave copies 8 token rows
+// with 4 direct global->LDS loads of 16 bytes per lane (2 rows per load; lane
 // p lands at chunk position p & 31 and fetches the chunk that the swizzle
-// places there).
-__device__ __forceinline__ void stage_direct(const SyrkArgs& a, const uint16_t* X, int col0, int t,
-                                             char* buf, int wave, int lane) {
+// places there).  The source pointers advance by one stage per call: src[0]
+// serves loads 0 and 2 (swizzle of rows = 0/1 mod 4), src[1] loads 1 and 3.
+struct DirectSrc {
+  const uint16_t* src[2];
+  int64_t row2;  // elements in 4 token rows
+};
+
+__device__ __forceinline__ DirectSrc direct_src(const SyrkArgs& a, const uint16_t* X, int col0, int t, int wave,
+                                                int lane) {
+  DirectSrc d;
   const int pos = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r0 = 16 * wave + 2 * i;
-    const int row = r0 + (lane >> 5);
+  for (int h = 0; h < 2; ++h) {
+    const int row = (KB / 4) * wave + 2 * h + (lane >> 5);
     const int gchunk = pos ^ ((row & 3) << 2);
-    const uint16_t* src = X + (int64_t)(t + row) * a.ldx + col0 + 8 * gchunk;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(buf + r0 * ROWB), 16, 0, 0);
+    d.src[h] = X + (int64_t)(t + row) * a.ldx + col0 + 8 * gchunk;
   }
+  d.row2 = 4 * a.ldx;
+  return d;
+}
+
+__device__ __forceinline__ void stage_direct(DirectSrc& d, char* buf, int wave, int64_t stage_step) {
+#pragma unroll
+  for (int i = 0; i < KB / 8; ++i) {
+    const int r0 = (KB / 4) * wave + 2 * i;
+    __builtin_amdgcn_global_load_lds(d.src[i & 1] + (i >> 1) * d.row2, (lds_void*)(buf + r0 * ROWB), 16, 0, 0);
+  }
+  d.src[0] += stage_step;
+  d.src[1] += stage_step;
 }
 
 // Guarded path for ragged stages or tiles: zero-filled register loads and
@@ -184,7 +209,7 @@ __device__ __forceinline__ void stage_direct(const SyrkArgs& a, const uint16_t* 
 __device__ __forceinline__ void stage_guarded(const SyrkArgs& a, const uint16_t* X, int col0, int t, int t1,
                                               char* buf) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < KB / 8; ++i) {
     const int idx = threadIdx.x + 256 * i;
     const int row = idx >> 5, c = idx & 31;
     const int tok = t + row, col = col0 + 8 * c;
@@ -203,14 +228,18 @@ __device__ __forceinline__ void stage_guarded(const SyrkArgs& a, const uint16_t*
 // MFMA operand of the 32-column block at m0 for tokens 16kk .. 16kk+15.  In a
 // 16-lane group, source lane s points at 4 columns (m0 + 16(g&1) + 4(s&3)) of
 // token row 16kk + 8(g>>1) + s/4; the transposing read hands lane l of the
-// group 4 consecutive tokens of column m0 + 16(g&1) + l.  Two reads give the
-// 8 tokens a lane supplies to v_mfma_f32_32x32x16_bf16.
-__device__ __forceinline__ bf16x8 frag_tr(const char* buf, int m0, int kk, int lane) {
+// group 4 consecutive tokens of column m0 + 16(g&1) + l.  Two reads (rows +0
+// and +4) give the 8 tokens a lane supplies to v_mfma_f32_32x32x16_bf16.
+// Rows +4 and +16kk keep row & 3, hence the swizzle: both are fixed byte
+// offsets from the kk = 0 address, which is computed once per block.
+__device__ __forceinline__ int frag_off(int m0, int lane) {
   const int g = lane >> 4, s = lane & 15;
-  const int col = m0 + 16 * (g & 1) + 4 * (s & 3);
-  const int row = 16 * kk + 8 * (g >> 1) + (s >> 2);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + sw_off(row, col)));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(buf + sw_off(row + 4, col)));
+  return sw_off(8 * (g >> 1) + (s >> 2), m0 + 16 * (g & 1) + 4 * (s & 3));
+}
+
+__device__ __forceinline__ bf16x8 frag_at(const char* p) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ROWB));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
@@ -220,14 +249,14 @@ struct StageFrags {
   bf16x8 a[KB / 16][4], b[KB / 16][4];
 };
 
-__device__ __forceinline__ void read_frags(const char* Ab, const char* Bb, int wm, int wn, int lane,
-                                           StageFrags& f) {
+__device__ __forceinline__ void read_frags(const char* Ab, const char* Bb, const int (&offA)[4],
+                                           const int (&offB)[4], StageFrags& f) {
 #pragma unroll
   for (int kk = 0; kk < KB / 16; ++kk) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[kk][i] = frag_tr(Ab, wm * 128 + 32 * i, kk, lane);
+    for (int i = 0; i < 4; ++i) f.a[kk][i] = frag_at(Ab + offA[i] + kk * 16 * ROWB);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f.b[kk][j] = frag_tr(Bb, wn * 128 + 32 * j, kk, lane);
+    for (int j = 0; j < 4; ++j) f.b[kk][j] = frag_at(Bb + offB[j] + kk * 16 * ROWB);
   }
 }
 
@@ -241,13 +270,29 @@ __device__ __forceinline__ void mfma_frags(const StageFrags& f, f32x16 (&acc)[4]
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j], acc[i][j], 0, 0, 0);
 }
 
-// FULL: every tile is inside X and every stage holds 64 tokens (n % 256 == 0,
-// tokens % 64 == 0, 16-byte aligned rows), so only direct loads are compiled.
+// FULL: every tile is inside X and every stage holds 32 tokens (n % 256 == 0,
+// tokens % 32 == 0, 16-byte aligned rows), so only direct loads are compiled.
+//
+// Pipeline (stage s lives in buffer s % 4; fragments alternate between two
+// register sets):
+//   wait + barrier   -- FULL: a counted vmcnt retires this wave's loads of stage
+//                       s+2 and leaves those of stage s+3 in flight; otherwise
+//                       a plain __syncthreads()
+//   read stage s+1 fragments into the other register set (in flight during
+//                       this stage's MFMAs)
+//   queue stage s+4 loads into the buffer stage s used
+//   32 MFMAs on stage s
+// Loads are queued four stages ahead and retired two stages later (two
+// stages of latency slack), and a buffer is read one full stage after the
+// barrier that retired its loads (reading a buffer straight after that
+// barrier returned stale data on this hardware).  The buffers are distinct
+// LDS objects, so fragment reads never wait for loads into another buffer.
 template <bool FULL>
 __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
-  // two stage buffers, each [operand A | operand B]
-  __shared__ __attribute__((aligned(16))) char L0[2 * STAGEB];
-  __shared__ __attribute__((aligned(16))) char L1[2 * STAGEB];
+  __shared__ __attribute__((aligned(16))) char B0[2 * STAGEB];
+  __shared__ __attribute__((aligned(16))) char B1[2 * STAGEB];
+  __shared__ __attribute__((aligned(16))) char B2[2 * STAGEB];
+  __shared__ __attribute__((aligned(16))) char B3[2 * STAGEB];
 
   const int item = blockIdx.x;
   const int tile = item / a.S, s = item % a.S;
@@ -256,6 +301,7 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
   const bool diag = (I == J);
   const int t0 = s * a.tps;
   const int t1 = min(a.tokens, t0 + a.tps);
+  const int nst = t1 > t0 ? (t1 - t0 + KB - 1) / KB : 0;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -273,45 +319,83 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto issue = [&](int t, char* buf) {
+  int offA[4], offB[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    offA[i] = frag_off(wm * 128 + 32 * i, lane);
+    offB[i] = frag_off(wn * 128 + 32 * i, lane);
+  }
+  const int64_t stage_step = (int64_t)KB * a.ldx;
+  DirectSrc dA = direct_src(a, X, colA, t0, wave, lane);
+  DirectSrc dB = direct_src(a, X, colB, t0, wave, lane);
+
+  // stages are issued in order, so the direct sources simply advance
+  auto issue = [&](int st, char* buf) {
+    const int t = t0 + st * KB;
     if constexpr (FULL) {
-      stage_direct(a, X, colA, t, buf, wave, lane);
-      if (!diag) stage_direct(a, X, colB, t, buf + STAGEB, wave, lane);
+      stage_direct(dA, buf, wave, stage_step);
+      if (!diag) stage_direct(dB, buf + STAGEB, wave, stage_step);
       return;
     }
     const bool full_t = t + KB <= t1;
     if (full_t && fullA)
-      stage_direct(a, X, colA, t, buf, wave, lane);
+      stage_direct(dA, buf, wave, stage_step);
     else
       stage_guarded(a, X, colA, t, t1, buf);
     if (!diag) {
       if (full_t && fullB)
-        stage_direct(a, X, colB, t, buf + STAGEB, wave, lane);
+        stage_direct(dB, buf + STAGEB, wave, stage_step);
       else
         stage_guarded(a, X, colB, t, t1, buf + STAGEB);
     }
   };
-
-  // One stage: read all operand fragments of the current buffer into
-  // registers, then queue the next stage's loads into the other buffer, then
-  // run the MFMAs.  The wait for those loads therefore falls before the next
-  // stage's fragment reads, after this stage's MFMAs.
-  auto stage = [&](const char* cur, int tnext, char* nxt) {
-    StageFrags f;
-    if (!idle) read_frags(cur, diag ? cur : cur + STAGEB, wm, wn, lane, f);
-    if (tnext < t1) issue(tnext, nxt);
-    if (!idle) mfma_frags(f, acc);
-    __syncthreads();
+  auto rd = [&](const char* buf, StageFrags& f) {
+    if (!idle) read_frags(buf, diag ? buf : buf + STAGEB, offA, offB, f);
+  };
+  // Barrier at the start of stage st.  FULL: each wave queued 4 (diagonal
+  // tile) or 8 direct loads per stage; leaving the newest stage's loads
+  // (st+3) outstanding retires stage st+2's.  The asm carries a memory clobber
+  // so no LDS access moves across it.
+  auto barrier = [&](int st) {
+    if constexpr (FULL) {
+      if (st + 3 >= nst)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else if (diag)
+        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
+      __syncthreads();
+    }
+  };
+  // stage st: fragments fc (stage st) are in registers; read stage st+1 from
+  // `nxt` into fn; queue stage st+4 into `dma` (stage st's buffer).
+  auto stage = [&](int st, const char* nxt, char* dma, StageFrags& fc, StageFrags& fn) {
+    barrier(st);
+    if (st + 1 < nst) rd(nxt, fn);
+    if (st + 4 < nst) issue(st + 4, dma);
+    if (!idle) mfma_frags(fc, acc);
   };
 
-  if (t0 < t1) {
-    issue(t0, L0);
+  if (nst > 0) {
+    StageFrags f0, f1;
+    // stages 0 and 1 retire first; retiring stage 2 (counted, if stage 3 was
+    // queued) gives them a full load latency before stage 0 is read
+    issue(0, B0);
+    if (nst > 1) issue(1, B1);
     __syncthreads();
-    // two stages per trip so each buffer is a distinct LDS object
-    for (int t = t0; t < t1; t += 2 * KB) {
-      stage(L0, t + KB, L1);
-      if (t + KB >= t1) break;
-      stage(L1, t + 2 * KB, L0);
+    if (nst > 2) issue(2, B2);
+    if (nst > 3) issue(3, B3);
+    barrier(-1);
+    rd(B0, f0);
+    for (int st = 0; st < nst; st += 4) {
+      stage(st + 0, B1, B0, f0, f1);
+      if (st + 1 >= nst) break;
+      stage(st + 1, B2, B1, f1, f0);
+      if (st + 2 >= nst) break;
+      stage(st + 2, B3, B2, f0, f1);
+      if (st + 3 >= nst) break;
+      stage(st + 3, B0, B3, f1, f0);
     }
   }
 
@@ -440,7 +524,7 @@ Plan plan(int64_t n, int64_t tokens, gptq_dtype dt) {
   const int kt = dt == GPTQ_BF16 ? KB : KT_F32;
   int64_t s;
   if (dt == GPTQ_BF16) {
-    s = (p.T >= 768 || tokens < 8 * 2 * KB) ? 1 : 8;
+    s = (p.T >= 768 || tokens < 8 * 4 * KB) ? 1 : 8;
   } else {
     const int64_t target = 1024;
     s = (target + p.T - 1) / p.T;
