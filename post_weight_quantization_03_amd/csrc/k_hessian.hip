@@ -34,6 +34,8 @@
 // item stores its partial tile and the last of the S items of a tile to finish
 // (per-tile arrival counter) sums the partials in split order and writes H,
 // so the result does not depend on scheduling.
+#include <type_traits>
+
 #include "common.h"
 
 namespace gptq {
@@ -173,24 +175,25 @@ __device__ __forceinline__ int sw_off(int row, int col) {
 // Fast path: the whole stage lies inside X.  Each wave copies 8 token rows
 // with 4 direct global->LDS loads of 16 bytes per lane (2 rows per load; lane
 // p lands at chunk position p & 31 and fetches the chunk that the swizzle
-// places there).  The source pointers advance by one stage per call: src[0]
-// serves loads 0 and 2 (swizzle of rows = 0/1 mod 4), src[1] loads 1 and 3.
+// places there).  The address is a wave-uniform base (first token of the
+// stage, first column of the slab; kept in SGPRs and advanced one stage per
+// call) plus a per-lane 32-bit byte offset that is the same for every stage.
 struct DirectSrc {
-  const uint16_t* src[2];
-  int64_t row2;  // elements in 4 token rows
+  const char* base;
+  uint32_t off[4];
 };
 
 __device__ __forceinline__ DirectSrc direct_src(const SyrkArgs& a, const uint16_t* X, int col0, int t, int wave,
                                                 int lane) {
   DirectSrc d;
+  d.base = reinterpret_cast<const char*>(X + (int64_t)t * a.ldx + col0);
   const int pos = lane & 31;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = (KB / 4) * wave + 2 * h + (lane >> 5);
+  for (int i = 0; i < KB / 8; ++i) {
+    const int row = (KB / 4) * wave + 2 * i + (lane >> 5);
     const int gchunk = pos ^ ((row & 3) << 2);
-    d.src[h] = X + (int64_t)(t + row) * a.ldx + col0 + 8 * gchunk;
+    d.off[i] = (uint32_t)(((int64_t)row * a.ldx + 8 * gchunk) * 2);
   }
-  d.row2 = 4 * a.ldx;
   return d;
 }
 
@@ -198,10 +201,14 @@ __device__ __forceinline__ void stage_direct(DirectSrc& d, char* buf, int wave, 
 #pragma unroll
   for (int i = 0; i < KB / 8; ++i) {
     const int r0 = (KB / 4) * wave + 2 * i;
-    __builtin_amdgcn_global_load_lds(d.src[i & 1] + (i >> 1) * d.row2, (lds_void*)(buf + r0 * ROWB), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(d.base + d.off[i], (lds_void*)(buf + r0 * ROWB), 16, 0, 0);
   }
-  d.src[0] += stage_step;
-  d.src[1] += stage_step;
+  // The empty asm hides the stage-to-stage relation of the base from loop
+  // strength reduction, which would otherwise keep one 64-bit VGPR address
+  // per load and unrolled stage (and spill them).
+  uint64_t b = reinterpret_cast<uint64_t>(d.base) + (uint64_t)(stage_step * 2);
+  asm volatile("" : "+s"(b));
+  d.base = reinterpret_cast<const char*>(b);
 }
 
 // Guarded path for ragged stages or tiles: zero-filled register loads and
@@ -303,7 +310,9 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
   const int t1 = min(a.tokens, t0 + a.tps);
   const int nst = t1 > t0 ? (t1 - t0 + KB - 1) / KB : 0;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave index through readfirstlane: provably uniform, so per-wave branches
+  // and the values they define stay scalar
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const bool idle = diag && wm > wn;  // quarter strictly below the diagonal
   const uint16_t* X = static_cast<const uint16_t*>(a.X);
@@ -376,6 +385,44 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
     if (st + 4 < nst) issue(st + 4, dma);
     if (!idle) mfma_frags(fc, acc);
   };
+  // Steady state of the FULL kernel: every stage reads its successor and
+  // queues stage +4, so the body has no branch and the scheduler may
+  // interleave the 32 transposing reads and the direct loads with the 32
+  // MFMAs (left in separate blocks, the reads stall the wave on the LDS
+  // queue before its MFMAs start).  TWO: off-diagonal tile (both operands);
+  // COMP: this wave reads fragments and runs MFMAs.
+  auto steady = [&](auto two_c, auto comp_c, StageFrags& f0, StageFrags& f1) {
+    constexpr bool TWO = decltype(two_c)::value, COMP = decltype(comp_c)::value;
+    auto body = [&](const char* nxt, char* dma, StageFrags& fc, StageFrags& fn) {
+      if constexpr (TWO)
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if constexpr (COMP) read_frags(nxt, TWO ? nxt + STAGEB : nxt, offA, offB, fn);
+      stage_direct(dA, dma, wave, stage_step);
+      if constexpr (TWO) stage_direct(dB, dma + STAGEB, wave, stage_step);
+      if constexpr (COMP) {
+        mfma_frags(fc, acc);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (TWO || (i & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // direct load
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          }
+        }
+      }
+    };
+    int st = 0;
+    for (; st + 8 <= nst; st += 4) {
+      body(B1, B0, f0, f1);
+      body(B2, B1, f1, f0);
+      body(B3, B2, f0, f1);
+      body(B0, B3, f1, f0);
+    }
+    return st;
+  };
 
   if (nst > 0) {
     StageFrags f0, f1;
@@ -388,7 +435,20 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
     if (nst > 3) issue(3, B3);
     barrier(-1);
     rd(B0, f0);
-    for (int st = 0; st < nst; st += 4) {
+    int st0 = 0;
+    if constexpr (FULL) {
+      using yes = std::true_type;
+      using no = std::false_type;
+      if (!diag)
+        st0 = steady(yes{}, yes{}, f0, f1);
+      else if (!idle)
+        st0 = steady(no{}, yes{}, f0, f1);
+      else
+        st0 = steady(no{}, no{}, f0, f1);
+    }
+    // the last stages (and every stage of a guarded tile), fragments of
+    // stage st0 in f0
+    for (int st = st0; st < nst; st += 4) {
       stage(st + 0, B1, B0, f0, f1);
       if (st + 1 >= nst) break;
       stage(st + 1, B2, B1, f1, f0);
