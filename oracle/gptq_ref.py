@@ -277,7 +277,7 @@ def _tie_distance(r):
 
 
 def replay_compare(W, U, bits: int, groupsize: int, codes, scales, zeros, tau: float,
-                   decision=np.float32, rows_sel=None):
+                   decision=np.float32, rows_sel=None, blocksize: int | None = None):
     """Run the per-column loop, adopting the other side's codes as it goes.
 
     At every (row, column) the oracle's own code is computed from its own
@@ -292,6 +292,11 @@ def replay_compare(W, U, bits: int, groupsize: int, codes, scales, zeros, tau: f
     ``codes``, ``scales``, ``zeros`` hold the other side's outputs for the
     rows in ``rows_sel`` (all rows when None); W and U are the staged weights
     of those rows and the full factor.
+
+    ``blocksize`` selects the lazy-batch form of the same loop, as in
+    gptq_from_factor: feedback inside the block per column, the rest of the
+    row once per block.  Both forms give the same result in exact arithmetic;
+    the per-column form (None) is the definition.
     """
     W = np.array(W, dtype=np.float64, copy=True)
     if rows_sel is not None:
@@ -308,8 +313,14 @@ def replay_compare(W, U, bits: int, groupsize: int, codes, scales, zeros, tau: f
           "zero_mismatch": 0, "zero_hard": 0, "max_scale_rel": 0.0, "min_tie_gap": np.inf,
           "groups": 0}
     what = np.zeros((rows, cols), dtype=np.float64)
+    err = np.zeros((rows, cols), dtype=np.float64)
     s = z = None
-    for j in range(cols):
+    B = cols if blocksize is None else int(blocksize)
+    if blocksize is not None and not (g % B == 0 or B % g == 0 or g >= cols):
+        raise ValueError("lazy-batch form needs block-aligned groups")
+
+    def step(j, b1):
+        nonlocal s, z
         if j % g == 0:
             s, z = grid_params(W[:, j:j + g], maxq, dt)
             gi = j // g
@@ -340,8 +351,20 @@ def replay_compare(W, U, bits: int, groupsize: int, codes, scales, zeros, tau: f
         wh = (s * (qa - z)).astype(dt).astype(np.float64)
         d = W[:, j] - wh
         e = d / U[j, j]
-        W[:, j + 1:] -= np.outer(e, U[j, j + 1:])
+        W[:, j + 1:b1] -= np.outer(e, U[j, j + 1:b1])
         what[:, j] = wh
+        err[:, j] = e
+
+    if blocksize is None:
+        for j in range(cols):
+            step(j, cols)
+    else:
+        for b0 in range(0, cols, B):
+            b1 = min(b0 + B, cols)
+            for j in range(b0, b1):
+                step(j, b1)
+            if b1 < cols:
+                W[:, b1:] -= err[:, b0:b1] @ U[b0:b1, b1:]
     st["identical_frac"] = 1.0 - st["mismatch"] / max(st["total"], 1)
     st["what"] = what
     return st

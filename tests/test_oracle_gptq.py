@@ -316,3 +316,22 @@ def test_replay_compare_self_and_planted_flips():
     assert st["mismatch"] == 1 and st["hard_flips"] == 1 and st["tie_flips"] == 0
     st = replay_compare(o["W_staged"], o["U"], 4, 32, codes, o["scales"], o["zeros"], 0.5)
     assert st["mismatch"] == 1 and st["tie_flips"] == 1
+
+
+@pytest.mark.parametrize("g,B", [(32, 32), (32, 64), (64, 32), (-1, 16)])
+def test_replay_compare_lazy_batch_equals_per_column(g, B):
+    """The lazy-batch replay reaches the per-column replay's result (exact in exact
+    arithmetic; here equal flip counts and w-hat within 1e-12), also with flips planted."""
+    W, H = _random_layer(12)
+    o = gptq_quantize(W, H, 3, g, 0.01, decision=np.float32)
+    codes = o["codes"].copy()
+    rng = np.random.default_rng(5)
+    for r, c in zip(rng.integers(0, codes.shape[0], 6), rng.integers(0, codes.shape[1], 6)):
+        codes[r, c] = codes[r, c] + (1 if codes[r, c] < 7 else -1)
+    a = replay_compare(o["W_staged"], o["U"], 3, g, codes, o["scales"], o["zeros"], 1e-3)
+    b = replay_compare(o["W_staged"], o["U"], 3, g, codes, o["scales"], o["zeros"], 1e-3, blocksize=B)
+    assert a["mismatch"] == b["mismatch"] >= 6
+    for k in ("tie_flips", "hard_flips", "zero_mismatch", "zero_hard", "groups"):
+        assert a[k] == b[k], k
+    assert abs(a["max_scale_rel"] - b["max_scale_rel"]) <= 1e-12
+    np.testing.assert_allclose(b["what"], a["what"], rtol=0, atol=1e-12)
