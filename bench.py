@@ -16,6 +16,7 @@ library launches on (PyTorch's current stream).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +31,23 @@ METRIC = "GPTQ layers/sec + TFLOP/s (4096×4096 & 11008×4096, 4-bit g128) vs MF
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+
+# HBM bytes per Hessian launch on this workload, from two rocprofv3 counter passes
+# (FETCH_SIZE, WRITE_SIZE) scaled by the reading of a plain 1 GiB copy; the summary with
+# the commands is profiles/hbm_counters_q_proj_4096x4096_262144tok.md.  Valid only for the
+# kernel source they were taken on: a different k_hessian.hip reports traffic as null.
+SYRK_TRAFFIC = {"k_hessian_sha256": "ea329aff9f4ca68a07312eccd457ba9305defe043215c911fe0f6cbb7665411c",
+                "workload": "q_proj_4096", "tokens": 262144,
+                "fetch_bytes": 14238888109.0, "write_bytes": 355773056.0}
+
+
+def syrk_traffic(workload, tokens):
+    path = os.path.join(ROOT, "post_weight_quantization_03_amd", "csrc", "k_hessian.hip")
+    sha = hashlib.sha256(open(path, "rb").read()).hexdigest()
+    t = SYRK_TRAFFIC
+    if sha != t["k_hessian_sha256"] or workload != t["workload"] or tokens != t["tokens"]:
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
 
 
 def parse():
@@ -199,7 +217,8 @@ def main():
         "quantize_only_layers_per_s": 1.0 / (t_q + t_p),
         "roofline": {"bound": "mfma", "kernel": "k_syrk_bf16 (Hessian)", "achieved": hess_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": hess_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": None},
+                     "traffic": syrk_traffic(args.workload, tokens),
+                     "algorithmic_bytes": alg["x_bytes"] + 4.0 * cols * cols},
         "input_generation_s": gen_s,
     }
     if not args.no_cpu_baseline:
