@@ -13,8 +13,10 @@
 // owner lane (j / 8) rounds its column, and e_j reaches the row's 16 lanes by
 // a DPP row broadcast (row_newbcast, one instruction, rows of 16 lanes are
 // exactly the wave's DPP rows).  The U block sits in LDS; each lane reads the
-// 8 entries of row j it needs as two 16-byte reads.  Group ranges are reduced
-// over the lanes that hold the group with xor shuffles.
+// 8 entries of row j+1 it needs as two 16-byte reads during step j.  Group
+// ranges are reduced over the lanes that hold the group with xor shuffles.
+// The serial chain of a step is the quotient (div_rn, 5 instructions), the
+// rounding and clamp, e_j, the broadcast and one fma.
 #include <utility>
 
 #include "common.h"
@@ -75,8 +77,9 @@ __device__ __forceinline__ void reduce_minmax(float& mn, float& mx) {
   }
 }
 
-// Asymmetric min/max grid with zero forced into the range; an all-zero group uses [-1, 1].
-__device__ __forceinline__ void grid_from_range(float mn, float mx, float maxq, float& s, float& z) {
+// Asymmetric min/max grid with zero forced into the range; an all-zero group
+// uses [-1, 1].  rs is 1/s rounded to nearest, for div_rn.
+__device__ __forceinline__ void grid_from_range(float mn, float mx, float maxq, float& s, float& z, float& rs) {
   float xmin = fminf(mn, 0.0f), xmax = fmaxf(mx, 0.0f);
   if (xmin == 0.0f && xmax == 0.0f) {
     xmin = -1.0f;
@@ -84,18 +87,45 @@ __device__ __forceinline__ void grid_from_range(float mn, float mx, float maxq, 
   }
   s = (xmax - xmin) / maxq;
   z = rintf(-xmin / s);
+  rs = 1.0f / s;
+}
+
+// x / s rounded to nearest, given rs = 1/s rounded to nearest (s a positive
+// normal number, x / s far from overflow and underflow).  Markstein's
+// correction (P. Markstein, IBM J. Res. Dev. 34(1), 1990; also the
+// Handbook of Floating-Point Arithmetic, division by iteration): when q is a
+// faithful quotient, the residual x - q s is exact in one fma and
+// q + residual * rs rounded to nearest is the correctly rounded quotient.
+// x * rs is within 1.5 ulp, so a first correction makes it faithful and a
+// second rounds it correctly; this keeps the loop's decision w / s identical
+// to an IEEE division at 5 dependent instructions instead of the full
+// division sequence.
+__device__ __forceinline__ float div_rn(float x, float s, float rs) {
+  float q = x * rs;
+  float r = fmaf(-q, s, x);
+  q = fmaf(r, rs, q);
+  r = fmaf(-q, s, x);
+  return fmaf(r, rs, q);
 }
 
 struct Lane {
-  float w[8], q[8], e[8], wh[8];
-  float s, z, loss;
+  float w[8];    // the lane's 8 columns of the row
+  float ru[8];   // 1 / U_jj of those columns (0 past the block's width)
+  float4 un[2];  // U row of the next step at the lane's columns, read one step ahead
+  float s, z, rs;
   int t;
 };
 
+// Step J of the block.  Columns past the block's width (a ragged last block)
+// hold w = 0, U = 0 and 1/U_jj = 0, so their steps change nothing and every
+// block runs all 128 steps without a branch between them.  Only the serial
+// chain is done here: the owner lane of column J rounds it and forms e_J, the
+// row's 16 lanes receive e_J and update their columns.  U is upper
+// triangular, so no later step changes column J again: the final registers
+// still hold every column's value at its decision, and codes, w^, e and the
+// loss are formed after the loop from them with the same operations.
 template <int MODE, int J>
-__device__ __forceinline__ void step(Lane& L, const BlockArgs& a, const float (*Us)[B], const float* rUd,
-                                     int64_t row, bool row_ok) {
-  if (J >= a.bw) return;
+__device__ __forceinline__ void step(Lane& L, const BlockArgs& a, const float (*Us)[B], int64_t row, bool row_ok) {
   constexpr int O = J >> 3, SL = J & 7;
   if constexpr (MODE != GM_BIG) {
     constexpr int GW = (MODE == GM_32) ? 32 : 64;
@@ -110,48 +140,42 @@ __device__ __forceinline__ void step(Lane& L, const BlockArgs& a, const float (*
         mx = fmaxf(mx, L.w[i]);
       }
       reduce_minmax<LANES>(mn, mx);
-      float s, z;
-      grid_from_range(mn, mx, a.maxq, s, z);
+      float s, z, rs;
+      grid_from_range(mn, mx, a.maxq, s, z, rs);
       if ((L.t / LANES) == (O / LANES)) {
         L.s = s;
         L.z = z;
+        L.rs = rs;
       }
-      if (L.t == O && row_ok) {
+      if (L.t == O && row_ok && J < a.bw) {
         const int64_t gi = (a.c0 + J) / a.g;
         a.scales[row * a.G + gi] = s;
         a.zeros[row * a.G + gi] = (uint8_t)z;
       }
     }
   }
-  const float x = L.w[SL];
-  const float r = x / L.s;
-  const float qv = fminf(fmaxf(rintf(r) + L.z, 0.0f), a.maxq);
-  const float whv = L.s * (qv - L.z);
-  const float d = x - whv;
-  const float ev = d * rUd[J];
-  if (L.t == O) {
-    L.q[SL] = qv;
-    L.wh[SL] = whv;
-    L.e[SL] = ev;
-    L.loss += 0.5f * ev * ev;
+  const float4 u0 = L.un[0], u1 = L.un[1];
+  if constexpr (J + 1 < B) {
+    L.un[0] = *reinterpret_cast<const float4*>(&Us[J + 1][8 * L.t]);
+    L.un[1] = *reinterpret_cast<const float4*>(&Us[J + 1][8 * L.t + 4]);
   }
+  const float x = L.w[SL];
+  const float qv = fminf(fmaxf(rintf(div_rn(x, L.s, L.rs)) + L.z, 0.0f), a.maxq);
+  const float ev = fmaf(-L.s, qv - L.z, x) * L.ru[SL];  // meaningful in the owner lane
   const float eb = row_bcast<O>(ev);
-  const float4 u0 = *reinterpret_cast<const float4*>(&Us[J][8 * L.t]);
-  const float4 u1 = *reinterpret_cast<const float4*>(&Us[J][8 * L.t + 4]);
-  L.w[0] = fmaf(-eb, u0.x, L.w[0]);
-  L.w[1] = fmaf(-eb, u0.y, L.w[1]);
-  L.w[2] = fmaf(-eb, u0.z, L.w[2]);
-  L.w[3] = fmaf(-eb, u0.w, L.w[3]);
-  L.w[4] = fmaf(-eb, u1.x, L.w[4]);
-  L.w[5] = fmaf(-eb, u1.y, L.w[5]);
-  L.w[6] = fmaf(-eb, u1.z, L.w[6]);
-  L.w[7] = fmaf(-eb, u1.w, L.w[7]);
+  // the column the next step rounds first, then the rest
+  constexpr int NX = (J + 1) & 7;
+  const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+  L.w[NX] = fmaf(-eb, uu[NX], L.w[NX]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i != NX) L.w[i] = fmaf(-eb, uu[i], L.w[i]);
 }
 
 template <int MODE, int... Js>
-__device__ __forceinline__ void run_steps(Lane& L, const BlockArgs& a, const float (*Us)[B], const float* rUd,
-                                          int64_t row, bool row_ok, std::integer_sequence<int, Js...>) {
-  (step<MODE, Js>(L, a, Us, rUd, row, row_ok), ...);
+__device__ __forceinline__ void run_steps(Lane& L, const BlockArgs& a, const float (*Us)[B], int64_t row,
+                                          bool row_ok, std::integer_sequence<int, Js...>) {
+  (step<MODE, Js>(L, a, Us, row, row_ok), ...);
 }
 
 template <int MODE>
@@ -160,12 +184,35 @@ __global__ __launch_bounds__(256) void k_quant_block(BlockArgs a) {
   __shared__ float rUd[B];
   const int tid = threadIdx.x;
   const int64_t c0 = a.c0, cols = a.cols;
-  // U block: Us[j][k] = U[c0+j][c0+k] for k >= j inside the block, else 0
-  for (int idx = tid; idx < B * B; idx += 256) {
-    const int j = idx >> 7, k = idx & (B - 1);
-    float v = 0.0f;
-    if (j < a.bw && k < a.bw && k >= j) v = a.U[(c0 + j) * cols + c0 + k];
-    Us[j][k] = v;
+  // U block without its diagonal: Us[j][k] = U[c0+j][c0+k] for k > j inside
+  // the block, else 0 (the feedback of step j reaches only k > j, so a column
+  // keeps its decision-time value; 1/U_jj comes separately).  Whole blocks
+  // with 16-byte rows load as 16 float4 per thread, all in flight at once.
+  const bool vec = a.bw == B && (cols & 3) == 0 && (reinterpret_cast<uintptr_t>(a.U) & 15) == 0;
+  if (vec) {
+    float4 v[B * B / 4 / 256];
+#pragma unroll
+    for (int i = 0; i < B * B / 4 / 256; ++i) {
+      const int idx = tid + 256 * i, j = idx >> 5, k = 4 * (idx & 31);
+      v[i] = *reinterpret_cast<const float4*>(a.U + (c0 + j) * cols + c0 + k);
+    }
+#pragma unroll
+    for (int i = 0; i < B * B / 4 / 256; ++i) {
+      const int idx = tid + 256 * i, j = idx >> 5, k = 4 * (idx & 31);
+      float4 w = v[i];
+      w.x = k + 0 > j ? w.x : 0.0f;
+      w.y = k + 1 > j ? w.y : 0.0f;
+      w.z = k + 2 > j ? w.z : 0.0f;
+      w.w = k + 3 > j ? w.w : 0.0f;
+      *reinterpret_cast<float4*>(&Us[j][k]) = w;
+    }
+  } else {
+    for (int idx = tid; idx < B * B; idx += 256) {
+      const int j = idx >> 7, k = idx & (B - 1);
+      float v = 0.0f;
+      if (j < a.bw && k < a.bw && k > j) v = a.U[(c0 + j) * cols + c0 + k];
+      Us[j][k] = v;
+    }
   }
   if (tid < B) rUd[tid] = tid < a.bw ? 1.0f / a.U[(c0 + tid) * cols + c0 + tid] : 0.0f;
   __syncthreads();
@@ -176,16 +223,22 @@ __global__ __launch_bounds__(256) void k_quant_block(BlockArgs a) {
   const int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 6) * 4 + (lane >> 4);
   const bool row_ok = row < a.rows;
   const int64_t base = row * cols + c0 + 8 * L.t;
+  if (vec && row_ok) {
+    const float4 w0 = *reinterpret_cast<const float4*>(a.Wf + base);
+    const float4 w1 = *reinterpret_cast<const float4*>(a.Wf + base + 4);
+    L.w[0] = w0.x; L.w[1] = w0.y; L.w[2] = w0.z; L.w[3] = w0.w;
+    L.w[4] = w1.x; L.w[5] = w1.y; L.w[6] = w1.z; L.w[7] = w1.w;
+  } else {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    L.w[i] = (row_ok && 8 * L.t + i < a.bw) ? a.Wf[base + i] : 0.0f;
-    L.q[i] = 0.0f;
-    L.e[i] = 0.0f;
-    L.wh[i] = 0.0f;
+    for (int i = 0; i < 8; ++i) L.w[i] = (row_ok && 8 * L.t + i < a.bw) ? a.Wf[base + i] : 0.0f;
   }
-  L.loss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) L.ru[i] = rUd[8 * L.t + i];
+  L.un[0] = *reinterpret_cast<const float4*>(&Us[0][8 * L.t]);
+  L.un[1] = *reinterpret_cast<const float4*>(&Us[0][8 * L.t + 4]);
   L.s = 1.0f;
   L.z = 0.0f;
+  L.rs = 1.0f;
 
   if constexpr (MODE == GM_BIG) {
     const int64_t gi = c0 / a.g;
@@ -212,7 +265,7 @@ __global__ __launch_bounds__(256) void k_quant_block(BlockArgs a) {
         }
       }
       reduce_minmax<16>(mn, mx);
-      grid_from_range(mn, mx, a.maxq, L.s, L.z);
+      grid_from_range(mn, mx, a.maxq, L.s, L.z, L.rs);
       if (L.t == 0 && row_ok) {
         a.scales[row * a.G + gi] = L.s;
         a.zeros[row * a.G + gi] = (uint8_t)L.z;
@@ -220,13 +273,24 @@ __global__ __launch_bounds__(256) void k_quant_block(BlockArgs a) {
     } else if (row_ok) {
       L.s = a.scales[row * a.G + gi];
       L.z = (float)a.zeros[row * a.G + gi];
+      L.rs = 1.0f / L.s;
     }
   }
 
-  run_steps<MODE>(L, a, Us, rUd, row, row_ok, std::make_integer_sequence<int, B>{});
+  run_steps<MODE>(L, a, Us, row, row_ok, std::make_integer_sequence<int, B>{});
 
+  // every column's decision again, from its value at decision time (the step's
+  // operations exactly); e and the loss vanish past the block's width
+  float q[8], wh[8], e[8], ls = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float x = L.w[i];
+    q[i] = fminf(fmaxf(rintf(div_rn(x, L.s, L.rs)) + L.z, 0.0f), a.maxq);
+    wh[i] = L.s * (q[i] - L.z);
+    e[i] = fmaf(-L.s, q[i] - L.z, x) * L.ru[i];
+    ls += 0.5f * e[i] * e[i];
+  }
   // loss over the row's 16 lanes
-  float ls = L.loss;
 #pragma unroll
   for (int m = 1; m < 16; m <<= 1) ls += __shfl_xor(ls, m, 64);
   if (!row_ok) return;
@@ -235,23 +299,23 @@ __global__ __launch_bounds__(256) void k_quant_block(BlockArgs a) {
   uint8_t* cp = a.codes + base;
   if (full && ((cols & 7) == 0)) {
     uint2 pk;
-    pk.x = (uint32_t)L.q[0] | ((uint32_t)L.q[1] << 8) | ((uint32_t)L.q[2] << 16) | ((uint32_t)L.q[3] << 24);
-    pk.y = (uint32_t)L.q[4] | ((uint32_t)L.q[5] << 8) | ((uint32_t)L.q[6] << 16) | ((uint32_t)L.q[7] << 24);
+    pk.x = (uint32_t)q[0] | ((uint32_t)q[1] << 8) | ((uint32_t)q[2] << 16) | ((uint32_t)q[3] << 24);
+    pk.y = (uint32_t)q[4] | ((uint32_t)q[5] << 8) | ((uint32_t)q[6] << 16) | ((uint32_t)q[7] << 24);
     *reinterpret_cast<uint2*>(cp) = pk;
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (8 * L.t + i < a.bw) cp[i] = (uint8_t)L.q[i];
+      if (8 * L.t + i < a.bw) cp[i] = (uint8_t)q[i];
   }
   if (a.w_hat) {
     float* hp = a.w_hat + base;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (8 * L.t + i < a.bw) hp[i] = L.wh[i];
+      if (8 * L.t + i < a.bw) hp[i] = wh[i];
   }
   float* ep = a.E + row * B + 8 * L.t;
-  *reinterpret_cast<float4*>(ep) = make_float4(L.e[0], L.e[1], L.e[2], L.e[3]);
-  *reinterpret_cast<float4*>(ep + 4) = make_float4(L.e[4], L.e[5], L.e[6], L.e[7]);
+  *reinterpret_cast<float4*>(ep) = make_float4(e[0], e[1], e[2], e[3]);
+  *reinterpret_cast<float4*>(ep + 4) = make_float4(e[4], e[5], e[6], e[7]);
 }
 
 }  // namespace
