@@ -56,6 +56,24 @@ struct SyrkArgs {
   int h_vec_x;     // X rows are 16-byte aligned (ldx % 8 == 0, aligned base): direct loads allowed
 };
 
+// Off-diagonal tiles first (row-major), the cheaper diagonal tiles last: the
+// dispatcher hands items out in order, so the last partial round of work
+// items consists of short ones.
+__device__ __forceinline__ void decode_offdiag_first(int t, int nbt, int& I, int& J) {
+  const int noff = nbt * (nbt - 1) / 2;
+  if (t >= noff) {
+    I = J = t - noff;
+    return;
+  }
+  int i = 0, base = 0;
+  while (base + (nbt - 1 - i) <= t) {
+    base += nbt - 1 - i;
+    ++i;
+  }
+  I = i;
+  J = i + 1 + (t - base);
+}
+
 __device__ __forceinline__ void decode_upper(int t, int nbt, int& I, int& J) {
   // row-major enumeration of upper tiles: row I holds nbt - I tiles
   int i = 0, base = 0;
@@ -197,11 +215,24 @@ __device__ __forceinline__ DirectSrc direct_src(const SyrkArgs& a, const uint16_
   return d;
 }
 
+// ASM: the load is issued from inline asm, invisible to the compiler's wait
+// insertion.  Only the whole-tile kernel does so: there every wait on these
+// loads is an explicit counted s_waitcnt, and without alias information the
+// compiler would otherwise drain all of them (vmcnt(0)) at the loop's back
+// edge before the first LDS read.
+typedef __attribute__((address_space(3))) char lds_char;
+
+template <bool ASM>
 __device__ __forceinline__ void stage_direct(DirectSrc& d, char* buf, int wave, int64_t stage_step) {
 #pragma unroll
   for (int i = 0; i < KB / 8; ++i) {
     const int r0 = (KB / 4) * wave + 2 * i;
-    __builtin_amdgcn_global_load_lds(d.base + d.off[i], (lds_void*)(buf + r0 * ROWB), 16, 0, 0);
+    if constexpr (ASM) {
+      const uint32_t lds = (uint32_t)(uintptr_t)(lds_char*)(buf + r0 * ROWB);
+      asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(d.off[i]), "s"(d.base), "{m0}"(lds));
+    } else {
+      __builtin_amdgcn_global_load_lds(d.base + d.off[i], (lds_void*)(buf + r0 * ROWB), 16, 0, 0);
+    }
   }
   // The empty asm hides the stage-to-stage relation of the base from loop
   // strength reduction, which would otherwise keep one 64-bit VGPR address
@@ -304,7 +335,7 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
   const int item = blockIdx.x;
   const int tile = item / a.S, s = item % a.S;
   int I, J;
-  decode_upper(tile, a.nbt, I, J);
+  decode_offdiag_first(tile, a.nbt, I, J);
   const bool diag = (I == J);
   const int t0 = s * a.tps;
   const int t1 = min(a.tokens, t0 + a.tps);
@@ -342,18 +373,18 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
   auto issue = [&](int st, char* buf) {
     const int t = t0 + st * KB;
     if constexpr (FULL) {
-      stage_direct(dA, buf, wave, stage_step);
-      if (!diag) stage_direct(dB, buf + STAGEB, wave, stage_step);
+      stage_direct<true>(dA, buf, wave, stage_step);
+      if (!diag) stage_direct<true>(dB, buf + STAGEB, wave, stage_step);
       return;
     }
     const bool full_t = t + KB <= t1;
     if (full_t && fullA)
-      stage_direct(dA, buf, wave, stage_step);
+      stage_direct<false>(dA, buf, wave, stage_step);
     else
       stage_guarded(a, X, colA, t, t1, buf);
     if (!diag) {
       if (full_t && fullB)
-        stage_direct(dB, buf + STAGEB, wave, stage_step);
+        stage_direct<false>(dB, buf + STAGEB, wave, stage_step);
       else
         stage_guarded(a, X, colB, t, t1, buf + STAGEB);
     }
@@ -398,19 +429,15 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
         asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       else
         asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if constexpr (COMP) read_frags(nxt, TWO ? nxt + STAGEB : nxt, offA, offB, fn);
-      stage_direct(dA, dma, wave, stage_step);
-      if constexpr (TWO) stage_direct(dB, dma + STAGEB, wave, stage_step);
+      stage_direct<true>(dA, dma, wave, stage_step);
+      if constexpr (TWO) stage_direct<true>(dB, dma + STAGEB, wave, stage_step);
       if constexpr (COMP) {
+        read_frags(nxt, TWO ? nxt + STAGEB : nxt, offA, offB, fn);
         mfma_frags(fc, acc);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (TWO || (i & 1) == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // direct load
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          }
+        for (int i = 0; i < 32; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         }
       }
     };
