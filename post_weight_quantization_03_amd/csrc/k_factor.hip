@@ -10,15 +10,19 @@
 //  1. k_damp_stats     one workgroup: dead columns (H_ii == 0 -> 1), lambda =
 //                      damp * mean(diag) (fp64 sum in a fixed order).
 //  2. k_reverse_damped A = P H_d P, lower triangle, fp32.
-//  3. blocked right-looking Cholesky, nb = 128: k_chol_diag factors the
-//     diagonal block in registers and LDS and writes its inverse into Minv;
-//     the panel below becomes L_ik = A_ik Linv_kk^T (GEMM) and the trailing
-//     lower tiles take A_ij -= L_ik L_jk^T (GEMM).
+//  3. blocked right-looking Cholesky, nb = 128: k_potrf_diag factors the
+//     diagonal block; the panel below becomes L_ik = A_ik L_kk^-T by
+//     row-parallel forward substitution (k_trsm_rows) and the trailing lower
+//     tiles take A_ij -= L_ik L_jk^T (GEMM).  The inverses of the diagonal
+//     blocks are formed after the loop, all at once and off the loop's
+//     critical path (k_trsm_rows on identity rows).
 //  4. triangular inverse by doubling: with the 128-blocks of Minv inverted,
 //     each level joins pairs of inverted diagonal blocks,
 //     [P 0; C Q]^-1 = [P^-1 0; -Q^-1 C P^-1 Q^-1], as two batched GEMMs.
 //  5. k_write_factor   U[i][j] = Minv[n-1-i][n-1-j] for i <= j into H, plus the
 //     dead flags in H's strictly lower triangle.
+#include <utility>
+
 #include "common.h"
 
 namespace gptq {
@@ -64,143 +68,281 @@ __global__ void k_reverse_damped(const float* H, int64_t n, const uint8_t* dead,
   }
 }
 
-// Factor the diagonal block A[k0:k0+kb, k0:k0+kb] (lower) and write the
-// inverse of its Cholesky factor (lower, zeros above the diagonal) into Minv
-// at the same place.
+// ------------------------------------------------------------------ diagonal block
+
+// Cholesky of the diagonal block A[k0:k0+kb, k0:k0+kb] (lower triangle in,
+// kb <= 128, padded with the identity beyond kb).  The block is written back
+// as L in the lower triangle and L^T in the strict upper triangle, so the
+// triangular solves below read rows of L^T contiguously.
 //
-// 256 threads, tr = tid / 16, tc = tid % 16; each thread holds the elements
-// (tr + 16a, tc + 16b), a, b = 0..7, of two 128x128 register arrays: S, the
-// block under elimination, and B, the inverse being formed.  Column c of the
-// block lives in register slot c / 16 of the lanes with tc == c % 16; the
-// slot is a template parameter, so finished rows and columns are skipped at
-// compile time.
-//
-// Step c (one barrier) does two things:
-//  * Cholesky, right-looking with the column left unscaled: the owners of
-//    column c publish it, then S[r][q] -= S[r][c] S[q][c] / S[c][c] for
-//    r, q > c.  L[r][c] = S[r][c] / sqrt(S[c][c]).
-//  * inverse by forward elimination of the identity, one row behind: the
-//    owners of row c-1 scale it by 1 / L[c-1][c-1] and publish it, then
-//    B[r][q] -= L[r][c-1] X[c-1][q] for r > c-1, q <= c-1.
-// L itself is never stored.  Columns are triple-buffered in LDS (step c reads
-// columns c and c-1 while step c+1 publishes column c+1), rows double-buffered.
-// Beyond kb the block is padded with the identity.  Pivot reciprocals use the
-// hardware reciprocal and reciprocal square root (1 ulp).
-namespace chol {
+// 16-column panels, right-looking.  A panel is factored wave-synchronously in
+// registers: each wave carries the panel's 16 diagonal rows in lanes 0..15
+// (the same in every wave) and 48 rows below it in lanes 16..63, a row per
+// lane, the panel's 16 values of the row in 16 VGPRs.  Step c takes the pivot
+// from lane c with readlane, scales column c (one multiply per lane) and
+// subtracts l_i l_j from the panel's later columns j, l_j read from lane j
+// with readlane: no barrier, no LDS inside a panel.  Rows of a lane above the
+// diagonal collect garbage in their upper entries, which no other lane ever
+// reads.  The trailing lower 16x16 tiles then take A_ij -= L_i L_j^T on
+// v_mfma_f32_16x16x4f32 from LDS.  Two barriers per panel.
+constexpr int PB = 16;      // panel width
+constexpr int LP = NB + 1;  // LDS pitch: a column read by 16 lanes hits 16 banks
 
-struct Ctx {
-  float S[8][8];
-  float B[8][8];
-  int tr, tc, kb;
-  bool bad;
-};
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
 
-__device__ __forceinline__ float sane(float piv) { return (piv > 0.0f && piv < INFINITY) ? piv : 1.0f; }
-
-// K: slot of column c = 16K + L.  KP: slot of c - 1.
-template <int K, int KP>
-__device__ __forceinline__ void step(Ctx& x, float (*col)[NB], float (*row)[NB], int c) {
-  const int L = c & 15, P = c - 1, LP = P & 15;
-  float* colC = col[c % 3];
-  const float* colP = col[(c + 2) % 3];
-  float* rowP = row[P & 1];
-  // publish column c (Cholesky) and row c - 1 of the inverse
-  if (K < 8 && x.tc == L) {
+template <int P>
+__device__ __forceinline__ void potrf_panel(float (*As)[LP], int kb, int wave, int lane, bool& bad) {
+  const int row = lane < PB ? PB * P + lane : PB * P + PB + 48 * wave + (lane - PB);
+  const bool act = wave < 3 && row < NB;
+  float a[PB];
 #pragma unroll
-    for (int a = (K < 8 ? K : 7); a < 8; ++a) colC[x.tr + 16 * a] = x.S[a][K < 8 ? K : 7];
+  for (int c = 0; c < PB; ++c) a[c] = act ? As[row][PB * P + c] : 0.0f;
+#pragma unroll
+  for (int c = 0; c < PB; ++c) {
+    const float d = readlane_f(a[c], c);
+    const bool ok = d > 0.0f && d < INFINITY;
+    bad |= (PB * P + c < kb) && !ok;
+    const float rl = __builtin_amdgcn_rsqf(ok ? d : 1.0f);
+    const float l = a[c] * rl;
+    a[c] = l;
+#pragma unroll
+    for (int j = c + 1; j < PB; ++j) a[j] = fmaf(-l, readlane_f(l, j), a[j]);
   }
-  if (KP >= 0 && c >= 1 && x.tr == LP) {
-    const float rl = __builtin_amdgcn_rsqf(sane(colP[P]));
+  // the diagonal rows once (wave 0), their lower part only
+  if (act && (wave == 0 || lane >= PB)) {
 #pragma unroll
-    for (int b = 0; b <= (KP >= 0 ? KP : 0); ++b) {
-      x.B[KP >= 0 ? KP : 0][b] *= rl;
-      rowP[x.tc + 16 * b] = x.B[KP >= 0 ? KP : 0][b];
+    for (int c = 0; c < PB; ++c)
+      if (lane >= PB || c <= lane) As[row][PB * P + c] = a[c];
+  }
+}
+
+template <int P>
+__device__ __forceinline__ void potrf_update(float (*As)[LP], int wave, int lane) {
+  constexpr int T0 = P + 1, NT = NB / PB - T0, NTILES = NT * (NT + 1) / 2;
+  const int i16 = lane & 15, g = lane >> 4;
+  for (int t = wave; t < NTILES; t += 4) {
+    int ti = 0;
+    while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+    const int tj = t - ti * (ti + 1) / 2 + T0;
+    ti += T0;
+    // v_mfma_f32_16x16x4f32: lane supplies A[i16][g] and B[g][i16]; holds
+    // D[4g + r][i16]
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    f32x4 acc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = As[PB * ti + 4 * g + r][PB * tj + i16];
+#pragma unroll
+    for (int kk = 0; kk < PB / 4; ++kk) {
+      const int k = PB * P + 4 * kk + g;
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-As[PB * ti + i16][k], As[PB * tj + i16][k], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) As[PB * ti + 4 * g + r][PB * tj + i16] = acc[r];
+  }
+}
+
+template <int P>
+__device__ __forceinline__ void potrf_step(float (*As)[LP], int kb, int wave, int lane, bool& bad) {
+  potrf_panel<P>(As, kb, wave, lane, bad);
+  __syncthreads();
+  if constexpr (P + 1 < NB / PB) {
+    potrf_update<P>(As, wave, lane);
+    __syncthreads();
+    potrf_step<P + 1>(As, kb, wave, lane, bad);
+  }
+}
+
+// Whole blocks with 16-byte rows move as float4, all loads of a thread in
+// flight at once; a ragged last block goes element by element.
+__device__ __forceinline__ bool block_vec(const float* A, int64_t n, int kb) {
+  return kb == NB && (n & 3) == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
+}
+
+__global__ __launch_bounds__(256) void k_potrf_diag(float* A, int64_t n, int64_t k0, int* status) {
+  __shared__ float As[NB][LP];
+  const int kb = (int)((n - k0) < NB ? (n - k0) : NB);
+  const int tid = threadIdx.x;
+  if (block_vec(A, n, kb)) {
+    constexpr int PER = NB * NB / 4 / 256;
+    float4 v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + 256 * i, r = idx >> 5, q = 4 * (idx & 31);
+      v[i] = *reinterpret_cast<const float4*>(A + (k0 + r) * n + k0 + q);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + 256 * i, r = idx >> 5, q = 4 * (idx & 31);
+      // the block's upper triangle holds no data yet: zeros there
+      As[r][q + 0] = q + 0 <= r ? v[i].x : 0.0f;
+      As[r][q + 1] = q + 1 <= r ? v[i].y : 0.0f;
+      As[r][q + 2] = q + 2 <= r ? v[i].z : 0.0f;
+      As[r][q + 3] = q + 3 <= r ? v[i].w : 0.0f;
+    }
+  } else {
+    for (int idx = tid; idx < NB * NB; idx += 256) {
+      const int r = idx >> 7, q = idx & (NB - 1);
+      float v = (r == q) ? 1.0f : 0.0f;
+      if (r < kb && q <= r) v = A[(k0 + r) * n + k0 + q];
+      As[r][q] = v;
     }
   }
   __syncthreads();
-  if (K < 8) {
-    constexpr int KK = K < 8 ? K : 7;
-    const float piv0 = colC[c];
-    x.bad |= (c < x.kb) && !(piv0 > 0.0f && piv0 < INFINITY);
-    const float rp = __builtin_amdgcn_rcpf(sane(piv0));
-    float cq[8];
-#pragma unroll
-    for (int b = KK; b < 8; ++b) {
-      const float v = colC[x.tc + 16 * b] * rp;
-      cq[b] = (b == KK && x.tc <= L) ? 0.0f : v;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  bool bad = false;
+  potrf_step<0>(As, kb, wave, lane, bad);
+  if (bad && threadIdx.x == 0) raise_status(status, GPTQ_ENOTPD);
+  __syncthreads();
+  if (block_vec(A, n, kb)) {
+#pragma unroll 4
+    for (int i = 0; i < NB * NB / 4 / 256; ++i) {
+      const int idx = tid + 256 * i, r = idx >> 5, q = 4 * (idx & 31);
+      float4 v;
+      v.x = q + 0 <= r ? As[r][q + 0] : As[q + 0][r];
+      v.y = q + 1 <= r ? As[r][q + 1] : As[q + 1][r];
+      v.z = q + 2 <= r ? As[r][q + 2] : As[q + 2][r];
+      v.w = q + 3 <= r ? As[r][q + 3] : As[q + 3][r];
+      *reinterpret_cast<float4*>(A + (k0 + r) * n + k0 + q) = v;
     }
-#pragma unroll
-    for (int a = KK; a < 8; ++a) {
-      float lr = colC[x.tr + 16 * a];
-      if (a == KK && x.tr <= L) lr = 0.0f;
-#pragma unroll
-      for (int b = KK; b < 8; ++b) x.S[a][b] = fmaf(-lr, cq[b], x.S[a][b]);
-    }
-  }
-  if (KP >= 0 && c >= 1) {
-    constexpr int KQ = KP >= 0 ? KP : 0;
-    const float rl = __builtin_amdgcn_rsqf(sane(colP[P]));
-    float rq[8];
-#pragma unroll
-    for (int b = 0; b <= KQ; ++b) rq[b] = rowP[x.tc + 16 * b];
-#pragma unroll
-    for (int a = KQ; a < 8; ++a) {
-      float lm = colP[x.tr + 16 * a] * rl;
-      if (a == KQ && x.tr <= LP) lm = 0.0f;
-#pragma unroll
-      for (int b = 0; b <= KQ; ++b) x.B[a][b] = fmaf(-lm, rq[b], x.B[a][b]);
+  } else {
+    for (int idx = tid; idx < NB * NB; idx += 256) {
+      const int r = idx >> 7, q = idx & (NB - 1);
+      if (r < kb && q < kb) A[(k0 + r) * n + k0 + q] = q <= r ? As[r][q] : As[q][r];
     }
   }
 }
 
-template <int K>
-__device__ __forceinline__ void slot(Ctx& x, float (*col)[NB], float (*row)[NB]) {
-  const int c0 = 16 * K;
-  if (c0 > x.kb) return;
-  step<K, K - 1>(x, col, row, c0);  // row c0 - 1 belongs to the previous slot
-  if (K < 8) {
-    for (int l = 1; l < 16; ++l) {
-      if (c0 + l > x.kb) return;
-      step<K, K>(x, col, row, c0 + l);
-    }
-  }
+// ------------------------------------------------------------------ triangular solves
+
+// Rows y = b L^-T for the diagonal block's L (read as L^T from the block's
+// upper triangle, diagonal from the block), i.e. L y^T = b^T by forward
+// substitution, right-looking: y_j = b_j / L_jj, then b_m -= y_j L_mj for m > j.
+// The same layout as the column loop: a 64-lane wave holds 4 rows, 16 lanes a
+// row, 8 consecutive columns per lane; y_j reaches the row's lanes by a DPP
+// row broadcast; L^T sits in LDS without its diagonal, and the row of step
+// j+1 is read during step j.  Column j is final after step j, so y is formed
+// after the loop as b * (1 / L_jj).
+//
+// IDENT = false: the panel below the block, rows [r0, r0 + rows) of A at
+//   columns [k0, k0 + 128), solved in place (L_ik = A_ik L_kk^-T).
+// IDENT = true: b = e_r for r = 0 .. 127 of diagonal block blockIdx.y: y is
+//   row r of L^-T, i.e. column r of L^-1, stored into the same block of Minv
+//   (lower, zeros above the diagonal).
+template <int O>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_amdgcn_update_dpp(0.0f, v, 0x150 + O, 0xf, 0xf, false);
 }
 
-}  // namespace chol
+struct TrsmLane {
+  float b[8], ru[8];
+  float4 un[2];
+  int t;
+};
 
-__global__ __launch_bounds__(256) void k_chol_diag(float* A, float* Minv, int64_t n, int64_t k0, int* status) {
-  __shared__ float col[3][NB];
-  __shared__ float row[2][NB];
-  chol::Ctx x;
-  x.kb = (int)((n - k0) < NB ? (n - k0) : NB);
-  x.tr = threadIdx.x >> 4;
-  x.tc = threadIdx.x & 15;
-  x.bad = false;
+template <int J>
+__device__ __forceinline__ void trsm_step(TrsmLane& L, const float (*Lt)[NB]) {
+  constexpr int O = J >> 3, SL = J & 7, NX = (J + 1) & 7;
+  const float4 u0 = L.un[0], u1 = L.un[1];
+  if constexpr (J + 1 < NB) {
+    L.un[0] = *reinterpret_cast<const float4*>(&Lt[J + 1][8 * L.t]);
+    L.un[1] = *reinterpret_cast<const float4*>(&Lt[J + 1][8 * L.t + 4]);
+  }
+  const float yb = row_bcast<O>(L.b[SL] * L.ru[SL]);
+  const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+  L.b[NX] = fmaf(-yb, uu[NX], L.b[NX]);
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int i = 0; i < 8; ++i)
+    if (i != NX) L.b[i] = fmaf(-yb, uu[i], L.b[i]);
+}
+
+template <int... Js>
+__device__ __forceinline__ void trsm_steps(TrsmLane& L, const float (*Lt)[NB], std::integer_sequence<int, Js...>) {
+  (trsm_step<Js>(L, Lt), ...);
+}
+
+template <bool IDENT>
+__global__ __launch_bounds__(256) void k_trsm_rows(float* A, float* Minv, int64_t n, int64_t k0_, int64_t r0,
+                                                   int64_t rows) {
+  __shared__ __attribute__((aligned(16))) float Lt[NB][NB];
+  __shared__ float rL[NB];
+  const int64_t k0 = IDENT ? (int64_t)blockIdx.y * NB : k0_;
+  const int kb = (int)((n - k0) < NB ? (n - k0) : NB);
+  const int tid = threadIdx.x;
+  // Lt[j][m] = L[m][j] for m > j (the block's upper triangle), else 0
+  if (block_vec(A, n, kb)) {
+    constexpr int PER = NB * NB / 4 / 256;
+    float4 v[PER];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int r = x.tr + 16 * a, q = x.tc + 16 * b;
-      x.S[a][b] = (r < x.kb && q <= r) ? A[(k0 + r) * n + k0 + q] : ((r == q) ? 1.0f : 0.0f);
-      x.B[a][b] = (r == q) ? 1.0f : 0.0f;
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + 256 * i, j = idx >> 5, m = 4 * (idx & 31);
+      v[i] = *reinterpret_cast<const float4*>(A + (k0 + j) * n + k0 + m);
     }
-  chol::slot<0>(x, col, row);
-  chol::slot<1>(x, col, row);
-  chol::slot<2>(x, col, row);
-  chol::slot<3>(x, col, row);
-  chol::slot<4>(x, col, row);
-  chol::slot<5>(x, col, row);
-  chol::slot<6>(x, col, row);
-  chol::slot<7>(x, col, row);
-  chol::slot<8>(x, col, row);  // the inverse's last row
-  if (x.bad) raise_status(status, GPTQ_ENOTPD);
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const int r = x.tr + 16 * a, q = x.tc + 16 * b;
-      if (r < x.kb && q < x.kb) Minv[(k0 + r) * n + k0 + q] = (q <= r) ? x.B[a][b] : 0.0f;
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + 256 * i, j = idx >> 5, m = 4 * (idx & 31);
+      float4 w = v[i];
+      w.x = m + 0 > j ? w.x : 0.0f;
+      w.y = m + 1 > j ? w.y : 0.0f;
+      w.z = m + 2 > j ? w.z : 0.0f;
+      w.w = m + 3 > j ? w.w : 0.0f;
+      *reinterpret_cast<float4*>(&Lt[j][m]) = w;
     }
+  } else {
+    for (int idx = tid; idx < NB * NB / 4; idx += 256) {
+      const int j = idx >> 5, m = 4 * (idx & 31);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < kb) {
+        const float* src = A + (k0 + j) * n + k0 + m;
+        v.x = (m + 0 > j && m + 0 < kb) ? src[0] : 0.0f;
+        v.y = (m + 1 > j && m + 1 < kb) ? src[1] : 0.0f;
+        v.z = (m + 2 > j && m + 2 < kb) ? src[2] : 0.0f;
+        v.w = (m + 3 > j && m + 3 < kb) ? src[3] : 0.0f;
+      }
+      *reinterpret_cast<float4*>(&Lt[j][m]) = v;
+    }
+  }
+  if (tid < NB) rL[tid] = tid < kb ? 1.0f / A[(k0 + tid) * (n + 1)] : 0.0f;
+  __syncthreads();
+
+  TrsmLane L;
+  const int lane = tid & 63;
+  L.t = lane & 15;
+  const int64_t rr = (int64_t)blockIdx.x * 16 + (tid >> 6) * 4 + (lane >> 4);
+  const bool ok = IDENT ? rr < kb : rr < rows;
+  const int64_t grow = r0 + rr;
+  if (!IDENT && ok && block_vec(A, n, kb)) {
+    const float4 b0 = *reinterpret_cast<const float4*>(A + grow * n + k0 + 8 * L.t);
+    const float4 b1 = *reinterpret_cast<const float4*>(A + grow * n + k0 + 8 * L.t + 4);
+    L.b[0] = b0.x; L.b[1] = b0.y; L.b[2] = b0.z; L.b[3] = b0.w;
+    L.b[4] = b1.x; L.b[5] = b1.y; L.b[6] = b1.z; L.b[7] = b1.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = 8 * L.t + i;
+      if constexpr (IDENT)
+        L.b[i] = (ok && c == rr) ? 1.0f : 0.0f;
+      else
+        L.b[i] = ok ? A[grow * n + k0 + c] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) L.ru[i] = rL[8 * L.t + i];
+  L.un[0] = *reinterpret_cast<const float4*>(&Lt[0][8 * L.t]);
+  L.un[1] = *reinterpret_cast<const float4*>(&Lt[0][8 * L.t + 4]);
+  trsm_steps(L, Lt, std::make_integer_sequence<int, NB>{});
+  if (!ok) return;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = 8 * L.t + i;
+    const float y = L.b[i] * L.ru[i];
+    if constexpr (IDENT) {
+      if (c < kb) Minv[(k0 + c) * n + k0 + rr] = (c >= rr) ? y : 0.0f;
+    } else {
+      A[grow * n + k0 + c] = y;
+    }
+  }
 }
 
 // U[i][j] = Minv[n-1-i][n-1-j] for j >= i, written into H; dead flags into the
@@ -285,26 +427,14 @@ hipError_t factor_run(float* H, int64_t n, float damp, const FactorWs& ws, hipSt
   for (int64_t k = 0; k < nk; ++k) {
     const int64_t k0 = k * NB;
     const int64_t kb = (n - k0) < NB ? (n - k0) : NB;
-    hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(256), 0, stream, ws.A, ws.Minv, n, k0, ws.status);
+    hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, stream, ws.A, n, k0, ws.status);
     FCHECK(hipGetLastError());
     const int64_t rest = n - k0 - kb;
     if (rest <= 0) break;
-    // panel: A[k0+kb:, k0:k0+kb] <- A[..] * Linv_kk^T   (in place, one tile column)
-    GemmF32 p{};
-    p.A = ws.A + (k0 + kb) * n + k0;
-    p.lda = n;
-    p.B = ws.Minv + k0 * n + k0;
-    p.ldb = n;
-    p.b_kmajor = 0;  // B(k, c) = Linv[c][k]
-    p.C = ws.A + (k0 + kb) * n + k0;
-    p.ldc = n;
-    p.M = (int)rest;
-    p.N = (int)kb;
-    p.K = (int)kb;
-    p.alpha = 1.0f;
-    p.beta = 0;
-    p.batch = 1;
-    FCHECK(gemm_f32(p, stream));
+    // panel: A[k0+kb:, k0:k0+kb] <- A[..] L_kk^-T   (in place, a row per 16 lanes)
+    hipLaunchKernelGGL(k_trsm_rows<false>, dim3((unsigned)((rest + 15) / 16)), dim3(256), 0, stream, ws.A,
+                       ws.Minv, n, k0, k0 + kb, rest);
+    FCHECK(hipGetLastError());
     // trailing lower tiles: A22 -= L21 L21^T
     GemmF32 t{};
     t.A = ws.A + (k0 + kb) * n + k0;
@@ -323,6 +453,10 @@ hipError_t factor_run(float* H, int64_t n, float damp, const FactorWs& ws, hipSt
     t.batch = 1;
     FCHECK(gemm_f32(t, stream));
   }
+  // inverses of all diagonal blocks at once, into Minv's diagonal blocks
+  hipLaunchKernelGGL(k_trsm_rows<true>, dim3(NB / 16, (unsigned)nk), dim3(256), 0, stream, ws.A, ws.Minv, n,
+                     (int64_t)0, (int64_t)0, (int64_t)0);
+  FCHECK(hipGetLastError());
   // triangular inverse by doubling over the 128-blocks already inverted in Minv
   for (int64_t s = NB; s < n; s *= 2) {
     const int64_t pairs_full = n / (2 * s);
