@@ -222,6 +222,17 @@ __device__ __forceinline__ DirectSrc direct_src(const SyrkArgs& a, const uint16_
 // edge before the first LDS read.
 typedef __attribute__((address_space(3))) char lds_char;
 
+__device__ __forceinline__ void dma_piece(const DirectSrc& d, char* buf, int wave, int i) {
+  const int r0 = (KB / 4) * wave + 2 * i;
+  const uint32_t lds = (uint32_t)(uintptr_t)(lds_char*)(buf + r0 * ROWB);
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(d.off[i]), "s"(d.base), "{m0}"(lds));
+}
+__device__ __forceinline__ void dma_advance(DirectSrc& d, int64_t stage_step) {
+  uint64_t b = reinterpret_cast<uint64_t>(d.base) + (uint64_t)(stage_step * 2);
+  asm volatile("" : "+s"(b));
+  d.base = reinterpret_cast<const char*>(b);
+}
+
 template <bool ASM>
 __device__ __forceinline__ void stage_direct(DirectSrc& d, char* buf, int wave, int64_t stage_step) {
 #pragma unroll
@@ -429,16 +440,34 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
         asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       else
         asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      stage_direct<true>(dA, dma, wave, stage_step);
-      if constexpr (TWO) stage_direct<true>(dB, dma + STAGEB, wave, stage_step);
       if constexpr (COMP) {
-        read_frags(nxt, TWO ? nxt + STAGEB : nxt, offA, offB, fn);
+        // direct loads spread over the stage: one before every two fragments
+        const char* Ab = nxt;
+        const char* Bb = TWO ? nxt + STAGEB : nxt;
+#pragma unroll
+        for (int kk = 0; kk < KB / 16; ++kk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int g = 4 * kk + i;  // 0..7
+            if constexpr (TWO) {
+              if (g < 4) dma_piece(dA, dma, wave, g); else dma_piece(dB, dma + STAGEB, wave, g - 4);
+            } else {
+              if ((g & 1) == 0) dma_piece(dA, dma, wave, g >> 1);
+            }
+            fn.a[kk][i] = frag_at(Ab + offA[i] + kk * 16 * ROWB);
+            fn.b[kk][i] = frag_at(Bb + offB[i] + kk * 16 * ROWB);
+          }
+        dma_advance(dA, stage_step);
+        if constexpr (TWO) dma_advance(dB, stage_step);
         mfma_frags(fc, acc);
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         }
+      } else {
+        stage_direct<true>(dA, dma, wave, stage_step);
+        if constexpr (TWO) stage_direct<true>(dB, dma + STAGEB, wave, stage_step);
       }
     };
     int st = 0;
