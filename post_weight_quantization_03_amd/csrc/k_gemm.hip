@@ -37,7 +37,7 @@ namespace {
 
 constexpr int KS = 16;  // k per stage
 
-typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) char lds_char;
 
 template <int TM>
 struct Geo {
@@ -97,10 +97,15 @@ __device__ __forceinline__ DmaOp<TM> dma_kmajor(const float* Bm, int64_t ld, int
 
 template <int TM>
 __device__ __forceinline__ void dma_issue(DmaOp<TM>& d, char* dst, int wave) {
+  // issued from asm: only the whole-tile pipeline uses these loads and every
+  // wait on them there is an explicit counted s_waitcnt, so the compiler's
+  // wait insertion (which would drain them all at the loop's back edge) must
+  // not see them
 #pragma unroll
-  for (int i = 0; i < Geo<TM>::LPW; ++i)
-    __builtin_amdgcn_global_load_lds(d.base + d.off[i], (lds_void*)(dst + (wave * Geo<TM>::LPW + i) * 1024), 16,
-                                     0, 0);
+  for (int i = 0; i < Geo<TM>::LPW; ++i) {
+    const uint32_t lds = (uint32_t)(uintptr_t)(lds_char*)(dst + (wave * Geo<TM>::LPW + i) * 1024);
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(d.off[i]), "s"(d.base), "{m0}"(lds));
+  }
   uint64_t b = reinterpret_cast<uint64_t>(d.base) + (uint64_t)d.step;
   asm volatile("" : "+s"(b));
   d.base = reinterpret_cast<const char*>(b);
