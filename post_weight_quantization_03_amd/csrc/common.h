@@ -90,7 +90,7 @@ struct QuantArgs {
   float* w_hat;
   float* row_loss;
   float* Wf;  // [rows, cols] working copy
-  float* E;   // [rows, 128] scaled errors of the current block
+  float* E;   // [2][rows, 128] scaled errors of the current and the previous block
   int64_t G;
 };
 hipError_t quant_run(const QuantArgs& a, hipStream_t stream);

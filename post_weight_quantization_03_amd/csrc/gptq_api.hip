@@ -41,7 +41,7 @@ QuantLayout layout(int64_t rows, int64_t cols, const gptq_params* p) {
   L.dead = take((size_t)cols);
   L.loss = take((size_t)rows * sizeof(float));
   L.Wf = take((size_t)rows * cols * sizeof(float));
-  L.E = take((size_t)rows * 128 * sizeof(float));
+  L.E = take((size_t)rows * 128 * sizeof(float) * 2);  // this block's errors and the previous block's
   if (!(p->flags & GPTQ_H_IS_FACTOR)) {
     int64_t tmax = 0;
     factor_scratch_floats(cols, &tmax);

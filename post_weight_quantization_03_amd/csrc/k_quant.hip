@@ -19,7 +19,7 @@
 // rounding and clamp, e_j, the broadcast and one fma.
 #include <utility>
 
-#include "common.h"
+#include "gemm_tile.h"
 
 namespace gptq {
 namespace {
@@ -59,7 +59,8 @@ struct BlockArgs {
   uint8_t* zeros;
   float* w_hat;
   float* row_loss;
-  float* E;
+  float* E;            // this block's scaled errors [rows, 128]
+  const float* Eprev;  // the previous block's, when its update of this block is applied here (else null)
 };
 
 template <int O>
@@ -178,17 +179,83 @@ __device__ __forceinline__ void run_steps(Lane& L, const BlockArgs& a, const flo
   (step<MODE, Js>(L, a, Us, row, row_ok), ...);
 }
 
+// LDS of one column-loop workgroup: the U block, 1/U_jj, and the previous
+// block's errors of its 16 rows.
+constexpr int QUANT_LDS = B * B * 4 + B * 4 + 16 * B * 4;
+
+// One workgroup of the block: rows 16 wg .. 16 wg + 15.  With a.Eprev the
+// previous block's update of this block's columns, W[r, c0:c0+bw] -=
+// Eprev[r, :] U[c0-128:c0, c0:c0+bw], is applied to the rows in registers
+// first (the rest of that update runs beside this block, see quant_run).
 template <int MODE>
-__global__ __launch_bounds__(256) void k_quant_block(BlockArgs a) {
-  __shared__ __attribute__((aligned(16))) float Us[B][B];
-  __shared__ float rUd[B];
+__device__ __forceinline__ void quant_block_wg(const BlockArgs& a, int64_t wg, char* lds) {
+  float(*Us)[B] = reinterpret_cast<float(*)[B]>(lds);
+  float* rUd = reinterpret_cast<float*>(lds + B * B * 4);
+  float(*Es)[B] = reinterpret_cast<float(*)[B]>(lds + B * B * 4 + B * 4);
   const int tid = threadIdx.x;
   const int64_t c0 = a.c0, cols = a.cols;
+  const int lane = tid & 63;
+  const int64_t row = wg * 16 + (tid >> 6) * 4 + (lane >> 4);
+  const bool row_ok = row < a.rows;
+  const int t8 = 8 * (lane & 15);
+  const int64_t base = row * cols + c0 + t8;
+  const bool vec = a.bw == B && (cols & 3) == 0 && (reinterpret_cast<uintptr_t>(a.U) & 15) == 0;
+  float w[8];
+  if (vec && row_ok) {
+    const float4 w0 = *reinterpret_cast<const float4*>(a.Wf + base);
+    const float4 w1 = *reinterpret_cast<const float4*>(a.Wf + base + 4);
+    w[0] = w0.x; w[1] = w0.y; w[2] = w0.z; w[3] = w0.w;
+    w[4] = w1.x; w[5] = w1.y; w[6] = w1.z; w[7] = w1.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = (row_ok && t8 + i < a.bw) ? a.Wf[base + i] : 0.0f;
+  }
+  if (a.Eprev) {
+    // Us[k][m] = U[c0-128+k][c0+m] (the previous block's rows, all of them
+    // above this block), Es = the previous errors of the 16 rows
+    const int64_t cp = c0 - B;
+    for (int idx = tid; idx < B * B / 4; idx += 256) {
+      const int k = idx >> 5, m = 4 * (idx & 31);
+      float4 v;
+      if (vec) {
+        v = *reinterpret_cast<const float4*>(a.U + (cp + k) * cols + c0 + m);
+      } else {
+        const float* src = a.U + (cp + k) * cols + c0 + m;
+        v.x = m + 0 < a.bw ? src[0] : 0.0f;
+        v.y = m + 1 < a.bw ? src[1] : 0.0f;
+        v.z = m + 2 < a.bw ? src[2] : 0.0f;
+        v.w = m + 3 < a.bw ? src[3] : 0.0f;
+      }
+      *reinterpret_cast<float4*>(&Us[k][m]) = v;
+    }
+    for (int idx = tid; idx < 16 * B / 4; idx += 256) {
+      const int r = idx >> 5, k = 4 * (idx & 31);
+      const int64_t gr = wg * 16 + r;
+      *reinterpret_cast<float4*>(&Es[r][k]) =
+          gr < a.rows ? *reinterpret_cast<const float4*>(a.Eprev + gr * B + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+    const int rl = (tid >> 6) * 4 + (lane >> 4);
+#pragma unroll 8
+    for (int k = 0; k < B; ++k) {
+      const float e = Es[rl][k];
+      const float4 u0 = *reinterpret_cast<const float4*>(&Us[k][t8]);
+      const float4 u1 = *reinterpret_cast<const float4*>(&Us[k][t8 + 4]);
+      w[0] = fmaf(-e, u0.x, w[0]);
+      w[1] = fmaf(-e, u0.y, w[1]);
+      w[2] = fmaf(-e, u0.z, w[2]);
+      w[3] = fmaf(-e, u0.w, w[3]);
+      w[4] = fmaf(-e, u1.x, w[4]);
+      w[5] = fmaf(-e, u1.y, w[5]);
+      w[6] = fmaf(-e, u1.z, w[6]);
+      w[7] = fmaf(-e, u1.w, w[7]);
+    }
+    __syncthreads();
+  }
   // U block without its diagonal: Us[j][k] = U[c0+j][c0+k] for k > j inside
   // the block, else 0 (the feedback of step j reaches only k > j, so a column
   // keeps its decision-time value; 1/U_jj comes separately).  Whole blocks
   // with 16-byte rows load as 16 float4 per thread, all in flight at once.
-  const bool vec = a.bw == B && (cols & 3) == 0 && (reinterpret_cast<uintptr_t>(a.U) & 15) == 0;
   if (vec) {
     float4 v[B * B / 4 / 256];
 #pragma unroll
@@ -218,20 +285,9 @@ __global__ __launch_bounds__(256) void k_quant_block(BlockArgs a) {
   __syncthreads();
 
   Lane L;
-  const int lane = tid & 63;
   L.t = lane & 15;
-  const int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 6) * 4 + (lane >> 4);
-  const bool row_ok = row < a.rows;
-  const int64_t base = row * cols + c0 + 8 * L.t;
-  if (vec && row_ok) {
-    const float4 w0 = *reinterpret_cast<const float4*>(a.Wf + base);
-    const float4 w1 = *reinterpret_cast<const float4*>(a.Wf + base + 4);
-    L.w[0] = w0.x; L.w[1] = w0.y; L.w[2] = w0.z; L.w[3] = w0.w;
-    L.w[4] = w1.x; L.w[5] = w1.y; L.w[6] = w1.z; L.w[7] = w1.w;
-  } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) L.w[i] = (row_ok && 8 * L.t + i < a.bw) ? a.Wf[base + i] : 0.0f;
-  }
+  for (int i = 0; i < 8; ++i) L.w[i] = w[i];
 #pragma unroll
   for (int i = 0; i < 8; ++i) L.ru[i] = rUd[8 * L.t + i];
   L.un[0] = *reinterpret_cast<const float4*>(&Us[0][8 * L.t]);
@@ -318,6 +374,46 @@ __global__ __launch_bounds__(256) void k_quant_block(BlockArgs a) {
   *reinterpret_cast<float4*>(ep + 4) = make_float4(e[4], e[5], e[6], e[7]);
 }
 
+// One launch per 128-column block b: the column loop of block b (workgroups
+// 0 .. nq-1, each applying the previous block's update of its own columns
+// first) and, beside it, the rest of the previous block's trailing update,
+// W[:, c0+128:] -= E_{b-1} U[c0-128:c0, c0+128:], as GEMM tiles (workgroups
+// nq ..).  The two touch disjoint columns; a loop workgroup (latency bound)
+// and a GEMM tile fit on one CU together, so the GEMM fills the loop's idle
+// issue slots.
+template <int MODE, int TM>
+__global__ __launch_bounds__(256, 2) void k_quant_fused(BlockArgs a, GemmF32 far, int64_t nq, int far_tn) {
+  constexpr int LDS = QUANT_LDS > gemm_tile_lds<TM>() ? QUANT_LDS : gemm_tile_lds<TM>();
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
+  if ((int64_t)blockIdx.x < nq) {
+    quant_block_wg<MODE>(a, blockIdx.x, lds);
+  } else {
+    const int t = (int)(blockIdx.x - nq);
+    gemm_tile<TM, true>(far, t / far_tn, t % far_tn, 0, lds);
+  }
+}
+
+template <int MODE>
+hipError_t launch_block(const BlockArgs& a, const GemmF32& far, int64_t nq, hipStream_t stream) {
+  if (far.M > 0 && far.N > 0) {
+    const int64_t t128 = ((far.M + 127) / 128) * ((far.N + 127) / 128);
+    if (t128 < 256) {
+      const int tn = (far.N + 63) / 64;
+      const int64_t tiles = (int64_t)((far.M + 63) / 64) * tn;
+      hipLaunchKernelGGL((k_quant_fused<MODE, 64>), dim3((unsigned)(nq + tiles)), dim3(256), 0, stream, a, far, nq,
+                         tn);
+    } else {
+      const int tn = (far.N + 127) / 128;
+      const int64_t tiles = (int64_t)((far.M + 127) / 128) * tn;
+      hipLaunchKernelGGL((k_quant_fused<MODE, 128>), dim3((unsigned)(nq + tiles)), dim3(256), 0, stream, a, far, nq,
+                         tn);
+    }
+  } else {
+    hipLaunchKernelGGL((k_quant_fused<MODE, 64>), dim3((unsigned)nq), dim3(256), 0, stream, a, far, nq, 1);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t quant_run(const QuantArgs& q, hipStream_t stream) {
@@ -344,24 +440,47 @@ hipError_t quant_run(const QuantArgs& q, hipStream_t stream) {
   a.zeros = q.zeros;
   a.w_hat = q.w_hat;
   a.row_loss = q.row_loss;
-  a.E = q.E;
   const int mode = (q.groupsize == 32) ? GM_32 : (q.groupsize == 64) ? GM_64 : GM_BIG;
-  const dim3 grid((unsigned)((rows + 15) / 16));
-  for (int64_t c0 = 0; c0 < cols; c0 += B) {
+  // The previous block's update of later columns can run beside a block only
+  // when no group range reaches past the block being quantized: groups inside
+  // a block, or one group per row (its range is taken before any update).
+  const bool overlap = q.groupsize <= B || q.groupsize >= cols;
+  float* Ebuf[2] = {q.E, q.E + rows * B};
+  const int64_t nq = (rows + 15) / 16;
+  int64_t b = 0;
+  for (int64_t c0 = 0; c0 < cols; c0 += B, ++b) {
     a.c0 = c0;
     a.bw = (int)((cols - c0) < B ? (cols - c0) : B);
+    a.E = Ebuf[b & 1];
+    a.Eprev = (overlap && b > 0) ? Ebuf[(b - 1) & 1] : nullptr;
+    GemmF32 far{};
+    if (overlap && b > 0 && c0 + B < cols) {
+      far.A = a.Eprev;
+      far.lda = B;
+      far.B = q.U + (c0 - B) * cols + (c0 + B);
+      far.ldb = cols;
+      far.b_kmajor = 1;
+      far.C = q.Wf + c0 + B;
+      far.ldc = cols;
+      far.M = (int)rows;
+      far.N = (int)(cols - c0 - B);
+      far.K = B;
+      far.alpha = -1.0f;
+      far.beta = 1;
+      far.batch = 1;
+    }
+    hipError_t e;
     if (mode == GM_32)
-      hipLaunchKernelGGL(k_quant_block<GM_32>, grid, dim3(256), 0, stream, a);
+      e = launch_block<GM_32>(a, far, nq, stream);
     else if (mode == GM_64)
-      hipLaunchKernelGGL(k_quant_block<GM_64>, grid, dim3(256), 0, stream, a);
+      e = launch_block<GM_64>(a, far, nq, stream);
     else
-      hipLaunchKernelGGL(k_quant_block<GM_BIG>, grid, dim3(256), 0, stream, a);
-    hipError_t e = hipGetLastError();
+      e = launch_block<GM_BIG>(a, far, nq, stream);
     if (e != hipSuccess) return e;
     const int64_t c1 = c0 + B;
-    if (c1 < cols) {
+    if (!overlap && c1 < cols) {
       GemmF32 g{};
-      g.A = q.E;
+      g.A = a.E;
       g.lda = B;
       g.B = q.U + c0 * cols + c1;
       g.ldb = cols;
