@@ -36,9 +36,9 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE, WRITE_SIZE) scaled by the reading of a plain 1 GiB copy; the summary with
 # the commands is profiles/hbm_counters_q_proj_4096x4096_262144tok.md.  Valid only for the
 # kernel source they were taken on: a different k_hessian.hip reports traffic as null.
-SYRK_TRAFFIC = {"k_hessian_sha256": "ea329aff9f4ca68a07312eccd457ba9305defe043215c911fe0f6cbb7665411c",
+SYRK_TRAFFIC = {"k_hessian_sha256": "ddfdcb272daca0b53585eff954cce4bb57c1bae55e43b367de0940b8742ec691",
                 "workload": "q_proj_4096", "tokens": 262144,
-                "fetch_bytes": 14238888109.0, "write_bytes": 355773056.0}
+                "fetch_bytes": 12440508438.0, "write_bytes": 362195232.0}
 
 
 def syrk_traffic(workload, tokens):
