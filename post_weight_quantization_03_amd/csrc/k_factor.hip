@@ -13,7 +13,8 @@
 //  3. blocked right-looking Cholesky, nb = 128: k_potrf_diag factors the
 //     diagonal block; the panel below becomes L_ik = A_ik L_kk^-T by
 //     row-parallel forward substitution (k_trsm_rows) and the trailing lower
-//     tiles take A_ij -= L_ik L_jk^T (GEMM).  The inverses of the diagonal
+//     tiles take A_ij -= L_ik L_jk^T (GEMM), in the same launch as the factor
+//     of the next diagonal block (k_factor_step, look-ahead).  The inverses of the diagonal
 //     blocks are formed after the loop, all at once and off the loop's
 //     critical path (k_trsm_rows on identity rows).
 //  4. triangular inverse by doubling: with the 128-blocks of Minv inverted,
@@ -23,7 +24,7 @@
 //     dead flags in H's strictly lower triangle.
 #include <utility>
 
-#include "common.h"
+#include "gemm_tile.h"
 
 namespace gptq {
 namespace {
@@ -160,8 +161,10 @@ __device__ __forceinline__ bool block_vec(const float* A, int64_t n, int kb) {
   return kb == NB && (n & 3) == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
 }
 
-__global__ __launch_bounds__(256) void k_potrf_diag(float* A, int64_t n, int64_t k0, int* status) {
-  __shared__ float As[NB][LP];
+constexpr int POTRF_LDS = NB * LP * 4;
+
+__device__ __forceinline__ void potrf_diag(float* A, int64_t n, int64_t k0, int* status, char* lds) {
+  float(*As)[LP] = reinterpret_cast<float(*)[LP]>(lds);
   const int kb = (int)((n - k0) < NB ? (n - k0) : NB);
   const int tid = threadIdx.x;
   if (block_vec(A, n, kb)) {
@@ -212,6 +215,34 @@ __global__ __launch_bounds__(256) void k_potrf_diag(float* A, int64_t n, int64_t
       if (r < kb && q < kb) A[(k0 + r) * n + k0 + q] = q <= r ? As[r][q] : As[q][r];
     }
   }
+}
+
+__global__ __launch_bounds__(256) void k_potrf_diag(float* A, int64_t n, int64_t k0, int* status) {
+  __shared__ __attribute__((aligned(16))) char lds[POTRF_LDS];
+  potrf_diag(A, n, k0, status, lds);
+}
+
+// One step of the blocked factor with look-ahead: the trailing update of
+// block k, A22 -= L21 L21^T on lower tiles, beside the factor of block k+1.
+// Block k+1's diagonal block (A22's first 128 x 128 tile) has been updated by
+// a small launch before this one; workgroup 0 factors it while the other
+// workgroups update the remaining lower tiles (the first `skip` tiles of size
+// TM cover that block and are left out).
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+template <int TM>
+__global__ __launch_bounds__(256, 2) void k_factor_step(GemmF32 trail, int skip, float* A, int64_t n, int64_t k0n,
+                                                        int* status) {
+  __shared__ __attribute__((aligned(16))) char lds[cmax(POTRF_LDS, cmax(gemm_tile_lds<128>(), gemm_tile_lds<TM>()))];
+  if (blockIdx.x == 0) {
+    potrf_diag(A, n, k0n, status, lds);
+    return;
+  }
+  const int t = (int)blockIdx.x - 1 + skip;
+  int r = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
+  while ((r + 1) * (r + 2) / 2 <= t) ++r;
+  while (r * (r + 1) / 2 > t) --r;
+  gemm_tile<TM, false>(trail, r, t - r * (r + 1) / 2, 0, lds);
 }
 
 // ------------------------------------------------------------------ triangular solves
@@ -424,18 +455,19 @@ hipError_t factor_run(float* H, int64_t n, float damp, const FactorWs& ws, hipSt
     FCHECK(hipGetLastError());
   }
   const int64_t nk = (n + NB - 1) / NB;
+  hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, stream, ws.A, n, (int64_t)0, ws.status);
+  FCHECK(hipGetLastError());
   for (int64_t k = 0; k < nk; ++k) {
     const int64_t k0 = k * NB;
     const int64_t kb = (n - k0) < NB ? (n - k0) : NB;
-    hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, stream, ws.A, n, k0, ws.status);
-    FCHECK(hipGetLastError());
     const int64_t rest = n - k0 - kb;
     if (rest <= 0) break;
     // panel: A[k0+kb:, k0:k0+kb] <- A[..] L_kk^-T   (in place, a row per 16 lanes)
     hipLaunchKernelGGL(k_trsm_rows<false>, dim3((unsigned)((rest + 15) / 16)), dim3(256), 0, stream, ws.A,
                        ws.Minv, n, k0, k0 + kb, rest);
     FCHECK(hipGetLastError());
-    // trailing lower tiles: A22 -= L21 L21^T
+    // trailing lower tiles A22 -= L21 L21^T: first the 128 x 128 diagonal
+    // block of block k+1 alone, then the rest beside that block's factor
     GemmF32 t{};
     t.A = ws.A + (k0 + kb) * n + k0;
     t.lda = n;
@@ -451,7 +483,24 @@ hipError_t factor_run(float* H, int64_t n, float damp, const FactorWs& ws, hipSt
     t.beta = 1;
     t.tri = 1;
     t.batch = 1;
-    FCHECK(gemm_f32(t, stream));
+    {
+      GemmF32 d = t;
+      d.M = d.N = (int)(rest < NB ? rest : NB);
+      FCHECK(gemm_f32(d, stream));
+    }
+    const int64_t t128 = (rest + 127) / 128;
+    if (t128 * (t128 + 1) / 2 >= 256) {
+      const int64_t tiles = t128 * (t128 + 1) / 2;
+      hipLaunchKernelGGL(k_factor_step<128>, dim3((unsigned)(1 + tiles - 1)), dim3(256), 0, stream, t, 1, ws.A, n,
+                         k0 + kb, ws.status);
+    } else {
+      const int64_t t64 = (rest + 63) / 64;
+      const int64_t tiles = t64 * (t64 + 1) / 2;
+      const int64_t skip = tiles < 3 ? tiles : 3;
+      hipLaunchKernelGGL(k_factor_step<64>, dim3((unsigned)(1 + tiles - skip)), dim3(256), 0, stream, t, (int)skip,
+                         ws.A, n, k0 + kb, ws.status);
+    }
+    FCHECK(hipGetLastError());
   }
   // inverses of all diagonal blocks at once, into Minv's diagonal blocks
   hipLaunchKernelGGL(k_trsm_rows<true>, dim3(NB / 16, (unsigned)nk), dim3(256), 0, stream, ws.A, ws.Minv, n,
