@@ -48,6 +48,7 @@ struct GemmF32 {
   int klo_n;
   int khi_m;
   int batch;
+  int order;  // set by gemm_f32: 1 = tiles by ascending column, 2 = by descending row (longest K first)
 };
 hipError_t gemm_f32(const GemmF32& g, hipStream_t stream);
 

@@ -45,6 +45,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_f32(GemmF32 g) {
     while (r * (r + 1) / 2 > t) --r;
     tm = r;
     tn = t - r * (r + 1) / 2;
+  } else if (g.order) {
+    // K limited by the tile's column (klo_n) or row (khi_m): tiles with the
+    // longest K go first, so the last ones to start are the short ones
+    const int mt = (g.M + TM - 1) / TM;
+    const int t = blockIdx.x;
+    tn = t / mt;
+    tm = t % mt;
+    if (g.order == 2) {
+      const int nt = (g.N + TM - 1) / TM;
+      tm = mt - 1 - t / nt;
+      tn = t % nt;
+    }
   } else {
     tn = blockIdx.x;
     tm = blockIdx.y;
@@ -58,6 +70,8 @@ hipError_t launch(const GemmF32& g, hipStream_t stream) {
   dim3 grid;
   if (g.tri)
     grid = dim3((unsigned)(tm * (tm + 1) / 2), 1, (unsigned)g.batch);
+  else if (g.order)
+    grid = dim3((unsigned)(tm * tn), 1, (unsigned)g.batch);
   else
     grid = dim3((unsigned)tn, (unsigned)tm, (unsigned)g.batch);
   if (g.b_kmajor)
@@ -69,8 +83,14 @@ hipError_t launch(const GemmF32& g, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t gemm_f32(const GemmF32& g, hipStream_t stream) {
+hipError_t gemm_f32(const GemmF32& g_in, hipStream_t stream) {
+  GemmF32 g = g_in;
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
+  // triangular K ranges: small tiles, longest K first, to balance the round
+  if (!g.tri && g.C != g.A && (g.klo_n || g.khi_m)) {
+    g.order = g.klo_n ? 1 : 2;
+    return launch<64>(g, stream);
+  }
   const int64_t tm = (g.M + 127) / 128, tn = (g.N + 127) / 128;
   const int64_t tiles = (g.tri ? tm * (tm + 1) / 2 : tm * tn) * g.batch;
   // In place (C is A, as in the factor's panel product): a tile reads whole
