@@ -27,13 +27,16 @@
 // fp32 path (v_mfma_f32_32x32x2_f32), 128x128 tiles for fp32 activations: a
 // lane supplies one k, so X stays token-major in LDS.
 //
-// Work items are (tile, token split) with item = tile * S + split.  Blocks are
-// dispatched to the 8 XCDs round robin, so with S a multiple of 8 every XCD
-// works on its own token range and streams only that part of X through its
-// L2.  With one split an item adds 2*acc to H directly; with S splits each
-// item stores its partial tile and the last of the S items of a tile to finish
-// (per-tile arrival counter) sums the partials in split order and writes H,
-// so the result does not depend on scheduling.
+// Work items are (tile, token range).  Blocks are dispatched to the 8 XCDs
+// round robin, so with S = 8 token splits and split = block % 8 every XCD
+// works on its own eighth of the tokens and streams only that part of X
+// through its L2.  With one split an item adds 2*acc to H directly.  With S
+// splits each item stores its partial tile, and a second kernel sums every
+// tile's partials in a fixed order and adds twice the sum to H, so the result
+// does not depend on scheduling.  Tiles that would make up a last, mostly
+// empty round of an XCD run as shorter token pieces instead, so that round
+// keeps every CU busy.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -44,17 +47,62 @@ namespace {
 struct SyrkArgs {
   const void* X;
   float* H;
-  float* part;     // [T * S][tile * tile] (S > 1)
-  int* counters;   // [T] (S > 1)
+  float* part;     // partial tiles, [slots][tile * tile] (S > 1)
   int64_t ldx;
   int n, tokens;
   int nbt;         // tiles per dimension
   int T;           // upper tiles
   int S;           // token splits
   int tps;         // tokens per split
+  int full;        // tiles computed whole per split; tiles full .. T-1 run in pieces
+  int P;           // pieces per split of those tiles
+  int tpp;         // tokens per piece
   int h_vec;       // H rows are 16-byte aligned (n % 4 == 0, aligned base)
   int h_vec_x;     // X rows are 16-byte aligned (ldx % 8 == 0, aligned base): direct loads allowed
 };
+
+// Work item b -> (tile, token range, partial slot).  Split s = b % S: with
+// S = 8 the dispatcher's round robin over the 8 XCDs sends every item of
+// split s to the same XCD, which then streams only that eighth of X through
+// its L2.  Units u = b / S below `full` are whole tiles (u = tile).  The last
+// T - full tiles would leave most CUs of an XCD idle in a final partial
+// round, so each of their splits is cut into P token pieces, giving
+// (T - full) * P short items per XCD instead.  Slots: whole tiles tile * S + s;
+// pieced tiles after them, (tile, s, piece) in token order.
+struct Item {
+  int tile, slot, t0, t1;
+};
+
+__device__ __forceinline__ Item decode_item(const SyrkArgs& a, int b) {
+  Item it;
+  const int s = b % a.S, u = b / a.S;
+  const int t0 = s * a.tps, t1 = min(a.tokens, t0 + a.tps);
+  if (u < a.full) {
+    it.tile = u;
+    it.slot = u * a.S + s;
+    it.t0 = t0;
+    it.t1 = t1;
+  } else {
+    const int L = a.T - a.full, v = u - a.full;
+    const int k = v % L, piece = v / L;
+    it.tile = a.full + k;
+    it.slot = a.full * a.S + (k * a.S + s) * a.P + piece;
+    it.t0 = min(t1, t0 + piece * a.tpp);
+    it.t1 = min(t1, it.t0 + a.tpp);
+  }
+  return it;
+}
+
+// Partial slots of a tile, in summation order.
+__device__ __forceinline__ void tile_slots(const SyrkArgs& a, int tile, int& first, int& count) {
+  if (tile < a.full) {
+    first = tile * a.S;
+    count = a.S;
+  } else {
+    first = a.full * a.S + (tile - a.full) * a.S * a.P;
+    count = a.S * a.P;
+  }
+}
 
 // Off-diagonal tiles first (row-major), the cheaper diagonal tiles last: the
 // dispatcher hands items out in order, so the last partial round of work
@@ -86,89 +134,138 @@ __device__ __forceinline__ void decode_upper(int t, int nbt, int& I, int& J) {
 }
 
 // acc[i][j] is the 32x32 block (i, j) of this wave's (32 WB) x (32 WB) quarter.
+// H += 2 acc on the upper triangle, mirrored into the lower one.  The 16 H
+// values a lane adds to in one block are loaded together, one block ahead of
+// the block being stored: loaded one at a time, each load would wait out a
+// full memory round trip before its store (the compiler cannot move a load
+// above a store that might alias it), which under the streaming load of the
+// other workgroups costs hundreds of microseconds per tile.
+template <int TILE, int WB>
+__device__ __forceinline__ void load_block(const SyrkArgs& a, int I, int J, int b, int lane, int wm, int wn,
+                                           float (&h)[16]) {
+  const int n = a.n;
+  const int i = b / WB, j = b % WB;
+  const int gc = J * TILE + wn * 32 * WB + 32 * j + acc_col(lane);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int gr = I * TILE + wm * 32 * WB + 32 * i + acc_row(r, lane);
+    h[r] = (gr < n && gc < n && gr <= gc) ? a.H[(int64_t)gr * n + gc] : 0.f;
+  }
+}
+
 template <int TILE, int WB>
 __device__ __forceinline__ void write_tile(const SyrkArgs& a, int I, int J, f32x16 (&acc)[WB][WB], int lane,
                                            int wm, int wn) {
   const int n = a.n;
   const bool vec_mirror = a.h_vec != 0;
+  float hc[16], hn[16];
+  load_block<TILE, WB>(a, I, J, 0, lane, wm, wn, hc);
 #pragma unroll
-  for (int i = 0; i < WB; ++i)
+  for (int b = 0; b < WB * WB; ++b) {
+    const int i = b / WB, j = b % WB;
+    if (b + 1 < WB * WB) load_block<TILE, WB>(a, I, J, b + 1, lane, wm, wn, hn);
+    const int gc = J * TILE + wn * 32 * WB + 32 * j + acc_col(lane);
 #pragma unroll
-    for (int j = 0; j < WB; ++j)
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int gr0 = I * TILE + wm * 32 * WB + 32 * i + acc_row(4 * r4, lane);
+      float v[4];
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int gr0 = I * TILE + wm * 32 * WB + 32 * i + acc_row(4 * r4, lane);
-        const int gc = J * TILE + wn * 32 * WB + 32 * j + acc_col(lane);
-        float v[4];
+      for (int e = 0; e < 4; ++e) {
+        const int gr = gr0 + e;
+        v[e] = hc[4 * r4 + e] + 2.0f * acc[i][j][4 * r4 + e];
+        if (gr < n && gc < n && gr <= gc) a.H[(int64_t)gr * n + gc] = v[e];
+      }
+      // mirror: rows gr0..gr0+3 of column gc become four consecutive floats of row gc
+      if (gc < n) {
+        float* m = a.H + (int64_t)gc * n + gr0;
+        if (vec_mirror && gr0 + 3 < gc && gr0 + 3 < n) {
+          *reinterpret_cast<float4*>(m) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int gr = gr0 + e;
-          v[e] = 0.f;
-          if (gr < n && gc < n && gr <= gc) {
-            float* p = a.H + (int64_t)gr * n + gc;
-            v[e] = *p + 2.0f * acc[i][j][4 * r4 + e];
-            *p = v[e];
-          }
-        }
-        // mirror: rows gr0..gr0+3 of column gc become four consecutive floats of row gc
-        if (gc < n) {
-          float* m = a.H + (int64_t)gc * n + gr0;
-          if (vec_mirror && gr0 + 3 < gc && gr0 + 3 < n) {
-            *reinterpret_cast<float4*>(m) = make_float4(v[0], v[1], v[2], v[3]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (gr0 + e < gc && gr0 + e < n) m[e] = v[e];
-          }
+          for (int e = 0; e < 4; ++e)
+            if (gr0 + e < gc && gr0 + e < n) m[e] = v[e];
         }
       }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) hc[r] = hn[r];
+  }
 }
 
-// Split-K bookkeeping: store this item's partial; the last arrival reduces.
-// Returns true when this workgroup must write H with acc = sum of partials.
-// Partial layout: float4 k4 of thread tid at [(k4 * 256 + tid) * 4].
+// Split tokens: each item stores its partial tile, thread-major (float4 k of
+// thread tid at [(k * 256 + tid) * 4]), and k_syrk_reduce sums the partials.
 template <int TILE, int WB>
-__device__ __forceinline__ bool splitk_reduce(const SyrkArgs& a, int tile, int s, f32x16 (&acc)[WB][WB]) {
-  constexpr int PARTIAL = TILE * TILE;
+__device__ __forceinline__ void store_partial(const SyrkArgs& a, int slot, f32x16 (&acc)[WB][WB]) {
   constexpr int NV = WB * WB * 4;  // float4s per thread
-  __shared__ int last;
-  const int tid = threadIdx.x;
-  float4* mine = reinterpret_cast<float4*>(a.part + ((int64_t)tile * a.S + s) * PARTIAL);
+  float4* mine = reinterpret_cast<float4*>(a.part + (int64_t)slot * TILE * TILE);
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     const int i = k / (4 * WB), j = (k / 4) % WB, r4 = k % 4;
-    mine[k * 256 + tid] = make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2],
-                                      acc[i][j][4 * r4 + 3]);
+    mine[k * 256 + threadIdx.x] = make_float4(acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2],
+                                              acc[i][j][4 * r4 + 3]);
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = atomicAdd(a.counters + tile, 1);
-    last = (prev == a.S - 1);
-  }
-  __syncthreads();
-  if (!last) return false;
-  __threadfence();
+}
+
+// H += 2 * (sum of a tile's partials, in slot order), mirrored.  Workgroup
+// (tile, k) takes float4 k of every thread of the producing workgroup, so
+// thread tid recovers that thread's (wave, lane) and with it the H
+// coordinates of the four values, as write_tile does.  Each thread has eight
+// partial loads in flight at a time; the whole chip runs the reduction, so it
+// is bound by HBM bandwidth rather than by one workgroup's memory latency.
+template <int TILE, int WB>
+__global__ __launch_bounds__(256) void k_syrk_reduce(SyrkArgs a) {
+  constexpr int PARTIAL4 = TILE * TILE / 4;
+  const int tile = blockIdx.x, k = blockIdx.y, tid = threadIdx.x;
+  int I, J;
+  if constexpr (TILE == 256)
+    decode_offdiag_first(tile, a.nbt, I, J);
+  else
+    decode_upper(tile, a.nbt, I, J);
+  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  if (I == J && wm > wn) return;  // quarter below the diagonal: not computed
+  const int i = k / (4 * WB), j = (k / 4) % WB, r4 = k % 4;
+  int first, count;
+  tile_slots(a, tile, first, count);
+  const float4* p = reinterpret_cast<const float4*>(a.part) + (int64_t)first * PARTIAL4 + k * 256 + tid;
+  float sum[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int q0 = 0; q0 < count; q0 += 8) {
+    float4 v[8];
 #pragma unroll
-  for (int i = 0; i < WB; ++i)
+    for (int u = 0; u < 8; ++u) v[u] = p[(int64_t)min(q0 + u, count - 1) * PARTIAL4];
 #pragma unroll
-    for (int j = 0; j < WB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  for (int q = 0; q < a.S; ++q) {
-    const float4* pq = reinterpret_cast<const float4*>(a.part + ((int64_t)tile * a.S + q) * PARTIAL) + tid;
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int i = k / (4 * WB), j = (k / 4) % WB, r4 = k % 4;
-      const float4 v = pq[k * 256];
-      acc[i][j][4 * r4] += v.x;
-      acc[i][j][4 * r4 + 1] += v.y;
-      acc[i][j][4 * r4 + 2] += v.z;
-      acc[i][j][4 * r4 + 3] += v.w;
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = q0 + u < count;
+      sum[0] += ok ? v[u].x : 0.f;
+      sum[1] += ok ? v[u].y : 0.f;
+      sum[2] += ok ? v[u].z : 0.f;
+      sum[3] += ok ? v[u].w : 0.f;
     }
   }
-  if (tid == 0) a.counters[tile] = 0;  // ready for the next call
-  return true;
+  const int n = a.n;
+  const int gr0 = I * TILE + wm * 32 * WB + 32 * i + acc_row(4 * r4, lane);
+  const int gc = J * TILE + wn * 32 * WB + 32 * j + acc_col(lane);
+  float h[4], v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int gr = gr0 + e;
+    h[e] = (gr < n && gc < n && gr <= gc) ? a.H[(int64_t)gr * n + gc] : 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int gr = gr0 + e;
+    v[e] = h[e] + 2.0f * sum[e];
+    if (gr < n && gc < n && gr <= gc) a.H[(int64_t)gr * n + gc] = v[e];
+  }
+  if (gc < n) {
+    float* m = a.H + (int64_t)gc * n + gr0;
+    if (a.h_vec && gr0 + 3 < gc && gr0 + 3 < n) {
+      *reinterpret_cast<float4*>(m) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (gr0 + e < gc && gr0 + e < n) m[e] = v[e];
+    }
+  }
 }
 
 // ------------------------------------------------------------------ bf16 path
@@ -343,13 +440,11 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
   __shared__ __attribute__((aligned(16))) char B2[2 * STAGEB];
   __shared__ __attribute__((aligned(16))) char B3[2 * STAGEB];
 
-  const int item = blockIdx.x;
-  const int tile = item / a.S, s = item % a.S;
+  const Item it = decode_item(a, blockIdx.x);
   int I, J;
-  decode_offdiag_first(tile, a.nbt, I, J);
+  decode_offdiag_first(it.tile, a.nbt, I, J);
   const bool diag = (I == J);
-  const int t0 = s * a.tps;
-  const int t1 = min(a.tokens, t0 + a.tps);
+  const int t0 = it.t0, t1 = it.t1;
   const int nst = t1 > t0 ? (t1 - t0 + KB - 1) / KB : 0;
 
   // wave index through readfirstlane: provably uniform, so per-wave branches
@@ -515,10 +610,10 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
     }
   }
 
-  if (a.S > 1) {
-    if (!splitk_reduce<TB, 4>(a, tile, s, acc)) return;
-  }
-  if (!idle) write_tile<TB, 4>(a, I, J, acc, lane, wm, wn);
+  if (a.S > 1)
+    store_partial<TB, 4>(a, it.slot, acc);
+  else if (!idle)
+    write_tile<TB, 4>(a, I, J, acc, lane, wm, wn);
 }
 
 // ------------------------------------------------------------------ fp32 path
@@ -559,13 +654,11 @@ __global__ __launch_bounds__(256) void k_syrk_f32(SyrkArgs a) {
   __shared__ __attribute__((aligned(16))) float As[2][KT_F32][F32_PITCH];
   __shared__ __attribute__((aligned(16))) float Bs[2][KT_F32][F32_PITCH];
 
-  const int item = blockIdx.x;
-  const int tile = item / a.S, s = item % a.S;
+  const Item it = decode_item(a, blockIdx.x);
   int I, J;
-  decode_upper(tile, a.nbt, I, J);
+  decode_upper(it.tile, a.nbt, I, J);
   const bool diag = (I == J);
-  const int t0 = s * a.tps;
-  const int t1 = min(a.tokens, t0 + a.tps);
+  const int t0 = it.t0, t1 = it.t1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const float* X = static_cast<const float*>(a.X);
@@ -614,24 +707,31 @@ __global__ __launch_bounds__(256) void k_syrk_f32(SyrkArgs a) {
     }
   }
 
-  if (a.S > 1) {
-    if (!splitk_reduce<TF, 2>(a, tile, s, acc)) return;
-  }
-  write_tile<TF, 2>(a, I, J, acc, lane, wm, wn);
-}
-
-__global__ void k_zero_i32(int* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
+  if (a.S > 1)
+    store_partial<TF, 2>(a, it.slot, acc);
+  else
+    write_tile<TF, 2>(a, I, J, acc, lane, wm, wn);
 }
 
 struct Plan {
-  int tile, nbt, T, S, tps;
+  int tile, nbt, T, S, tps, full, P, tpp;
+  int64_t slots;
 };
 
+int cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || cus <= 0)
+    return 256;
+  return cus;
+}
+
 // Work decomposition.  bf16: with fewer than three upper tiles per CU the
-// tokens are split 8 ways (one split per XCD), else not at all.  fp32 (small
-// problems): enough items for the chip with at least 512 tokens per split.
+// tokens are split 8 ways (one split per XCD), else not at all.  A split runs
+// on the CUs of one XCD: whole tiles go out in full rounds of cus/8, and the
+// tiles left over for a last partial round are cut into token pieces so that
+// they fill that round.  fp32 (small problems): enough items for the chip
+// with at least 512 tokens per split.
 Plan plan(int64_t n, int64_t tokens, gptq_dtype dt) {
   Plan p{};
   p.tile = dt == GPTQ_BF16 ? TB : TF;
@@ -654,6 +754,20 @@ Plan plan(int64_t n, int64_t tokens, gptq_dtype dt) {
   if (s < 1) s = 1;
   p.S = (int)s;
   p.tps = (int)per;
+  p.full = p.T;
+  p.P = 1;
+  p.tpp = p.tps;
+  if (dt == GPTQ_BF16 && p.S == 8) {
+    const int per_xcd = std::max(1, cu_count() / 8);
+    const int left = p.T % per_xcd;
+    const int pieces = left > 0 ? per_xcd / left : 1;
+    if (left > 0 && pieces > 1 && p.tps / pieces >= 4 * KB) {
+      p.full = p.T - left;
+      p.P = pieces;
+      p.tpp = (p.tps / pieces + KB - 1) / KB * KB;
+    }
+  }
+  p.slots = (int64_t)p.full * p.S + (int64_t)(p.T - p.full) * p.S * p.P;
   return p;
 }
 
@@ -663,8 +777,7 @@ size_t hessian_workspace(int64_t n, int64_t tokens, gptq_dtype dt) {
   if (n <= 0 || tokens <= 0) return 0;
   const Plan p = plan(n, tokens, dt);
   if (p.S == 1) return 0;
-  return align_up((size_t)p.T * p.S * p.tile * p.tile * sizeof(float), 256) +
-         align_up((size_t)p.T * sizeof(int), 256);
+  return align_up((size_t)p.slots * p.tile * p.tile * sizeof(float), 256);
 }
 
 int hessian_launch(float* H, int64_t n, const void* X, gptq_dtype dt, int64_t tokens, int64_t ldx, void* ws,
@@ -680,28 +793,29 @@ int hessian_launch(float* H, int64_t n, const void* X, gptq_dtype dt, int64_t to
   a.T = p.T;
   a.S = p.S;
   a.tps = p.tps;
+  a.full = p.full;
+  a.P = p.P;
+  a.tpp = p.tpp;
   a.h_vec = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(H) & 15) == 0);
   if (p.S > 1) {
     if (ws_bytes < hessian_workspace(n, tokens, dt) || ws == nullptr) return GPTQ_EWORKSPACE;
     a.part = static_cast<float*>(ws);
-    a.counters = reinterpret_cast<int*>(static_cast<char*>(ws) +
-                                        align_up((size_t)p.T * p.S * p.tile * p.tile * sizeof(float), 256));
-    hipLaunchKernelGGL(k_zero_i32, dim3((p.T + 255) / 256), dim3(256), 0, stream, a.counters, p.T);
-    if (hipGetLastError() != hipSuccess) return GPTQ_EHIP;
   }
-  const dim3 grid((unsigned)(p.T * p.S));
+  const dim3 grid((unsigned)((p.full + (p.T - p.full) * p.P) * p.S));
   if (dt == GPTQ_BF16) {
     a.h_vec_x = (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
     if (a.h_vec_x && n % TB == 0 && tokens % KB == 0)
       hipLaunchKernelGGL(k_syrk_bf16<true>, grid, dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL(k_syrk_bf16<false>, grid, dim3(256), 0, stream, a);
+    if (p.S > 1) hipLaunchKernelGGL((k_syrk_reduce<TB, 4>), dim3(p.T, 64), dim3(256), 0, stream, a);
   } else {
     const bool vec = (ldx % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
     if (vec)
       hipLaunchKernelGGL(k_syrk_f32<true>, grid, dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL(k_syrk_f32<false>, grid, dim3(256), 0, stream, a);
+    if (p.S > 1) hipLaunchKernelGGL((k_syrk_reduce<TF, 2>), dim3(p.T, 16), dim3(256), 0, stream, a);
   }
   return hipGetLastError() == hipSuccess ? GPTQ_OK : GPTQ_EHIP;
 }

@@ -33,7 +33,10 @@ def _lib_loaded():
     (300, 1000, True, 1, 0),       # ragged n and tokens, several tiles
     (300, 1000, False, 3, 0),      # fp32, three chunks
     (257, 777, True, 2, 3),        # odd n, padded row stride (unaligned path)
-    (512, 8192, True, 1, 0),       # split over tokens with the in-kernel reduction
+    (512, 8192, True, 1, 0),       # split over tokens, partials summed by the reduction kernel
+    (512, 16384, True, 1, 0),      # every tile cut into token pieces (3 tiles, 10 pieces per split)
+    (2048, 8192, True, 1, 0),      # 32 whole tiles per split, the last 4 in 8 pieces each
+    (2048, 8200, True, 1, 0),      # the same with ragged pieces and an empty last piece
     (130, 40, True, 1, 0),         # fewer tokens than one LDS stage
 ])
 def test_hessian_parity(n, tokens, bf16, chunks, pad):
