@@ -32,13 +32,14 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes per Hessian launch on this workload, from two rocprofv3 counter passes
-# (FETCH_SIZE, WRITE_SIZE) scaled by the reading of a plain 1 GiB copy; the summary with
-# the commands is profiles/hbm_counters_q_proj_4096x4096_262144tok.md.  Valid only for the
-# kernel source they were taken on: a different k_hessian.hip reports traffic as null.
-SYRK_TRAFFIC = {"k_hessian_sha256": "ddfdcb272daca0b53585eff954cce4bb57c1bae55e43b367de0940b8742ec691",
+# HBM bytes per Hessian accumulation call on this workload (k_syrk_bf16 and k_syrk_reduce
+# together), from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by the reading
+# of a plain 1 GiB copy; the summary with the commands is
+# profiles/hbm_counters_q_proj_4096x4096_262144tok.md.  Valid only for the kernel source they
+# were taken on: a different k_hessian.hip reports traffic as null.
+SYRK_TRAFFIC = {"k_hessian_sha256": "f33214ee2f7a0fcaa4f3c5367aa86162d706f7974f5f2f1fe3dc9b6ca33f64a6",
                 "workload": "q_proj_4096", "tokens": 262144,
-                "fetch_bytes": 12440508438.0, "write_bytes": 362195232.0}
+                "fetch_bytes": 9211036048.0, "write_bytes": 492678805.0}
 
 
 def syrk_traffic(workload, tokens):
@@ -215,7 +216,8 @@ def main():
         "stage_tflops": {"hessian_bf16_mfma": hess_tflops,
                          "factor_and_quantize_f32": (alg["factor_flop"] + alg["quantize_flop"]) / t_q / 1e12},
         "quantize_only_layers_per_s": 1.0 / (t_q + t_p),
-        "roofline": {"bound": "mfma", "kernel": "k_syrk_bf16 (Hessian)", "achieved": hess_tflops,
+        "roofline": {"bound": "mfma", "kernel": "k_syrk_bf16 + k_syrk_reduce (one Hessian call)",
+                     "achieved": hess_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": hess_tflops / PEAK_BF16_TFLOPS,
                      "traffic": syrk_traffic(args.workload, tokens),
                      "algorithmic_bytes": alg["x_bytes"] + 4.0 * cols * cols},
