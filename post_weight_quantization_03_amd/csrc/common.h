@@ -92,8 +92,11 @@ struct QuantArgs {
   float* row_loss;
   float* Wf;  // [rows, cols] working copy
   float* E;   // [2][rows, 128] scaled errors of the current and the previous block
+  uint16_t* Usplit;  // [3][cols, cols] bf16 planes of U for the split trailing GEMM, or null
   int64_t G;
 };
+// Bytes of the U planes quant_run needs (0 when no trailing update runs split).
+size_t quant_split_bytes(int64_t cols, int64_t groupsize);
 hipError_t quant_run(const QuantArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------------------

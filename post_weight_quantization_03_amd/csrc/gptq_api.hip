@@ -11,7 +11,7 @@ constexpr int VERSION = 100;  // 0.1.0
 constexpr int64_t MAX_DIM = (int64_t)1 << 30;
 
 struct QuantLayout {
-  size_t status, lam, dead, loss, Wf, E, A, Minv, T, total;
+  size_t status, lam, dead, loss, Wf, E, Us, A, Minv, T, total;
   int64_t tmax;
 };
 
@@ -42,6 +42,10 @@ QuantLayout layout(int64_t rows, int64_t cols, const gptq_params* p) {
   L.loss = take((size_t)rows * sizeof(float));
   L.Wf = take((size_t)rows * cols * sizeof(float));
   L.E = take((size_t)rows * 128 * sizeof(float) * 2);  // this block's errors and the previous block's
+  {
+    const size_t ub = quant_split_bytes(cols, p->groupsize == -1 ? cols : p->groupsize);
+    L.Us = ub ? take(ub) : 0;
+  }
   if (!(p->flags & GPTQ_H_IS_FACTOR)) {
     int64_t tmax = 0;
     factor_scratch_floats(cols, &tmax);
@@ -153,6 +157,7 @@ int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t rows, int64_t
   q.row_loss = loss;
   q.Wf = reinterpret_cast<float*>(ws + L.Wf);
   q.E = reinterpret_cast<float*>(ws + L.E);
+  q.Usplit = quant_split_bytes(cols, g) ? reinterpret_cast<uint16_t*>(ws + L.Us) : nullptr;
   q.G = G;
   e = quant_run(q, stream);
   if (e != hipSuccess) return GPTQ_EHIP;

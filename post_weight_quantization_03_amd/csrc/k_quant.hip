@@ -6,7 +6,9 @@
 //                  q = clamp(rint(w_j / s) + z, 0, maxq), w^ = s (q - z),
 //                  e_j = (w_j - w^) / U_jj, w_k -= e_j U_jk (k in the block)
 //                writing codes, grid, w^, row loss and E (the block's e_j).
-// Then the trailing update W[:, c1:] -= E U[c0:c1, c1:] as an fp32 MFMA GEMM.
+// Then the trailing update W[:, c1:] -= E U[c0:c1, c1:]: in fp32 accuracy on
+// bf16 MFMA with three-way split operands (sgemm_tile.h) when it runs beside
+// the next block, else as an fp32 MFMA GEMM.
 //
 // Layout of k_quant_block: a 64-lane wave holds 4 rows, 16 lanes per row; lane
 // t of a row owns columns 8t .. 8t+7 of the block in registers.  At step j the
@@ -20,6 +22,7 @@
 #include <utility>
 
 #include "gemm_tile.h"
+#include "sgemm_tile.h"
 
 namespace gptq {
 namespace {
@@ -62,6 +65,20 @@ struct BlockArgs {
   float* E;            // this block's scaled errors [rows, 128]
   const float* Eprev;  // the previous block's, when its update of this block is applied here (else null)
 };
+
+// U's upper triangle -> three bf16 planes (the split GEMM's B operand).
+__global__ void k_split_u(const float* U, int64_t n, uint16_t* P) {
+  const int64_t plane = n * n;
+  for (int64_t i = blockIdx.y; i < n; i += gridDim.y) {
+    for (int64_t j = i + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n; j += (int64_t)gridDim.x * blockDim.x) {
+      __bf16 h1, h2, h3;
+      split3(U[i * n + j], h1, h2, h3);
+      P[i * n + j] = __builtin_bit_cast(uint16_t, h1);
+      P[plane + i * n + j] = __builtin_bit_cast(uint16_t, h2);
+      P[2 * plane + i * n + j] = __builtin_bit_cast(uint16_t, h3);
+    }
+  }
+}
 
 template <int O>
 __device__ __forceinline__ float row_bcast(float v) {
@@ -380,41 +397,38 @@ __device__ __forceinline__ void quant_block_wg(const BlockArgs& a, int64_t wg, c
 // W[:, c0+128:] -= E_{b-1} U[c0-128:c0, c0+128:], as GEMM tiles (workgroups
 // nq ..).  The two touch disjoint columns; a loop workgroup (latency bound)
 // and a GEMM tile fit on one CU together, so the GEMM fills the loop's idle
-// issue slots.
-template <int MODE, int TM>
-__global__ __launch_bounds__(256, 2) void k_quant_fused(BlockArgs a, GemmF32 far, int64_t nq, int far_tn) {
-  constexpr int LDS = QUANT_LDS > gemm_tile_lds<TM>() ? QUANT_LDS : gemm_tile_lds<TM>();
+// issue slots.  The tiles run the split-bf16 GEMM (sgemm_tile.h).
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void k_quant_fused(BlockArgs a, SplitGemm far, int64_t nq, int far_tn) {
+  constexpr int LDS = QUANT_LDS > SGEMM_LDS ? QUANT_LDS : SGEMM_LDS;
   __shared__ __attribute__((aligned(16))) char lds[LDS];
   if ((int64_t)blockIdx.x < nq) {
     quant_block_wg<MODE>(a, blockIdx.x, lds);
   } else {
     const int t = (int)(blockIdx.x - nq);
-    gemm_tile<TM, true>(far, t / far_tn, t % far_tn, 0, lds);
+    sgemm_tile(far, t / far_tn, t % far_tn, lds);
   }
 }
 
 template <int MODE>
-hipError_t launch_block(const BlockArgs& a, const GemmF32& far, int64_t nq, hipStream_t stream) {
+hipError_t launch_block(const BlockArgs& a, const SplitGemm& far, int64_t nq, hipStream_t stream) {
+  int tn = 1;
+  int64_t tiles = 0;
   if (far.M > 0 && far.N > 0) {
-    const int64_t t128 = ((far.M + 127) / 128) * ((far.N + 127) / 128);
-    if (t128 < 256) {
-      const int tn = (far.N + 63) / 64;
-      const int64_t tiles = (int64_t)((far.M + 63) / 64) * tn;
-      hipLaunchKernelGGL((k_quant_fused<MODE, 64>), dim3((unsigned)(nq + tiles)), dim3(256), 0, stream, a, far, nq,
-                         tn);
-    } else {
-      const int tn = (far.N + 127) / 128;
-      const int64_t tiles = (int64_t)((far.M + 127) / 128) * tn;
-      hipLaunchKernelGGL((k_quant_fused<MODE, 128>), dim3((unsigned)(nq + tiles)), dim3(256), 0, stream, a, far, nq,
-                         tn);
-    }
-  } else {
-    hipLaunchKernelGGL((k_quant_fused<MODE, 64>), dim3((unsigned)nq), dim3(256), 0, stream, a, far, nq, 1);
+    tn = (far.N + STM - 1) / STM;
+    tiles = (int64_t)((far.M + STM - 1) / STM) * tn;
   }
+  hipLaunchKernelGGL((k_quant_fused<MODE>), dim3((unsigned)(nq + tiles)), dim3(256), 0, stream, a, far, nq, tn);
   return hipGetLastError();
 }
 
 }  // namespace
+
+size_t quant_split_bytes(int64_t cols, int64_t groupsize) {
+  const bool overlap = groupsize <= B || groupsize >= cols;
+  if (!overlap || cols <= 2 * B) return 0;
+  return (size_t)3 * cols * cols * sizeof(uint16_t);
+}
 
 hipError_t quant_run(const QuantArgs& q, hipStream_t stream) {
   const int64_t rows = q.rows, cols = q.cols;
@@ -446,6 +460,14 @@ hipError_t quant_run(const QuantArgs& q, hipStream_t stream) {
   // a block, or one group per row (its range is taken before any update).
   const bool overlap = q.groupsize <= B || q.groupsize >= cols;
   float* Ebuf[2] = {q.E, q.E + rows * B};
+  if (overlap && cols > 2 * B) {
+    if (!q.Usplit) return hipErrorInvalidValue;
+    const unsigned gx = (unsigned)((cols + 255) / 256 < 16 ? (cols + 255) / 256 : 16);
+    hipLaunchKernelGGL(k_split_u, dim3(gx, (unsigned)(cols < 65535 ? cols : 65535)), dim3(256), 0, stream, q.U,
+                       cols, q.Usplit);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int64_t nq = (rows + 15) / 16;
   int64_t b = 0;
   for (int64_t c0 = 0; c0 < cols; c0 += B, ++b) {
@@ -453,21 +475,17 @@ hipError_t quant_run(const QuantArgs& q, hipStream_t stream) {
     a.bw = (int)((cols - c0) < B ? (cols - c0) : B);
     a.E = Ebuf[b & 1];
     a.Eprev = (overlap && b > 0) ? Ebuf[(b - 1) & 1] : nullptr;
-    GemmF32 far{};
+    SplitGemm far{};
     if (overlap && b > 0 && c0 + B < cols) {
       far.A = a.Eprev;
-      far.lda = B;
-      far.B = q.U + (c0 - B) * cols + (c0 + B);
-      far.ldb = cols;
-      far.b_kmajor = 1;
+      for (int p = 0; p < 3; ++p) far.B[p] = q.Usplit + (int64_t)p * cols * cols + (c0 - B) * cols + (c0 + B);
       far.C = q.Wf + c0 + B;
+      far.lda = B;
+      far.ldb = cols;
       far.ldc = cols;
       far.M = (int)rows;
       far.N = (int)(cols - c0 - B);
       far.K = B;
-      far.alpha = -1.0f;
-      far.beta = 1;
-      far.batch = 1;
     }
     hipError_t e;
     if (mode == GM_32)
