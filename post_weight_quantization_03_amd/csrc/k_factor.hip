@@ -50,6 +50,24 @@ __global__ __launch_bounds__(1024) void k_damp_stats(const float* H, int64_t n, 
   if (threadIdx.x == 0) *lam = (float)((double)damp * part[0] / (double)n);
 }
 
+// A[i][j] = H_d[n-1-i][n-1-j] for j <= i, four columns a thread: the source
+// is the float4 of row n-1-i ending at column n-1-j, read backwards.  Chunks
+// reaching past the diagonal also write A's upper triangle, which nothing reads.
+// Needs n % 4 == 0 and 16-byte aligned H and A.
+__global__ void k_reverse_damped4(const float* H, int64_t n, const uint8_t* dead, const float* lam, float* A) {
+  const float l = *lam;
+  for (int64_t i = blockIdx.y; i < n; i += gridDim.y) {
+    const int64_t si = n - 1 - i;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; 4 * q <= i; q += (int64_t)gridDim.x * blockDim.x) {
+      const float4 v = *reinterpret_cast<const float4*>(H + si * n + (n - 4 - 4 * q));
+      float o[4] = {v.w, v.z, v.y, v.x};
+      const int64_t e = i - 4 * q;  // the diagonal, if in this chunk
+      if (e < 4) o[e] = (dead[si] ? 1.0f : o[e]) + l;
+      *reinterpret_cast<float4*>(A + i * n + 4 * q) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
 // A[i][j] = H_d[n-1-i][n-1-j] for j <= i; rows in blockIdx.y, columns in grid-stride x.
 __global__ void k_reverse_damped(const float* H, int64_t n, const uint8_t* dead, const float* lam, float* A) {
   const float l = *lam;
@@ -380,6 +398,32 @@ __global__ __launch_bounds__(256) void k_trsm_rows(float* A, float* Minv, int64_
   }
 }
 
+// U[i][j] = Minv[n-1-i][n-1-j] for j >= i into H, four columns a thread (the
+// chunk holding the diagonal element by element, so H[i][j < i] keeps its
+// dead flags); dead flags into H[i][i-1] and H[n-1][0].  Needs n % 4 == 0 and
+// 16-byte aligned Minv and H.
+__global__ void k_write_factor4(const float* Minv, int64_t n, const uint8_t* dead, float* H) {
+  for (int64_t i = blockIdx.y; i < n; i += gridDim.y) {
+    const int64_t si = n - 1 - i;
+    for (int64_t q = i / 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; 4 * q < n;
+         q += (int64_t)gridDim.x * blockDim.x) {
+      const float4 v = *reinterpret_cast<const float4*>(Minv + si * n + (n - 4 - 4 * q));
+      const float o[4] = {v.w, v.z, v.y, v.x};
+      if (4 * q >= i) {
+        *reinterpret_cast<float4*>(H + i * n + 4 * q) = make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * q + e >= i) H[i * n + 4 * q + e] = o[e];
+      }
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      if (i >= 1) H[i * n + i - 1] = dead[i] ? 1.0f : 0.0f;
+      if (i == n - 1 && n >= 3) H[i * n + 0] = dead[0] ? 1.0f : 0.0f;
+    }
+  }
+}
+
 // U[i][j] = Minv[n-1-i][n-1-j] for j >= i, written into H; dead flags into the
 // strictly lower slots H[i][i-1] (column i >= 1) and H[n-1][0] (column 0).
 __global__ void k_write_factor(const float* Minv, int64_t n, const uint8_t* dead, float* H) {
@@ -452,12 +496,19 @@ hipError_t dead_from_factor(const float* H, int64_t n, uint8_t* dead, hipStream_
 hipError_t factor_run(float* H, int64_t n, float damp, const FactorWs& ws, hipStream_t stream) {
   hipLaunchKernelGGL(k_damp_stats, dim3(1), dim3(1024), 0, stream, (const float*)H, n, damp, ws.dead, ws.lam);
   FCHECK(hipGetLastError());
-  {
-    const unsigned gx = (unsigned)((n + 255) / 256 < 16 ? (n + 255) / 256 : 16);
-    hipLaunchKernelGGL(k_reverse_damped, dim3(gx, (unsigned)(n < 65535 ? n : 65535)), dim3(256), 0, stream, (const float*)H, n,
+  const bool vec4 = (n % 4) == 0 && (reinterpret_cast<uintptr_t>(H) & 15) == 0 &&
+                    (reinterpret_cast<uintptr_t>(ws.A) & 15) == 0 && (reinterpret_cast<uintptr_t>(ws.Minv) & 15) == 0;
+  const unsigned gy = (unsigned)(n < 65535 ? n : 65535);
+  if (vec4) {
+    const unsigned gx = (unsigned)((n / 4 + 255) / 256);
+    hipLaunchKernelGGL(k_reverse_damped4, dim3(gx, gy), dim3(256), 0, stream, (const float*)H, n,
                        (const uint8_t*)ws.dead, (const float*)ws.lam, ws.A);
-    FCHECK(hipGetLastError());
+  } else {
+    const unsigned gx = (unsigned)((n + 255) / 256 < 16 ? (n + 255) / 256 : 16);
+    hipLaunchKernelGGL(k_reverse_damped, dim3(gx, gy), dim3(256), 0, stream, (const float*)H, n,
+                       (const uint8_t*)ws.dead, (const float*)ws.lam, ws.A);
   }
+  FCHECK(hipGetLastError());
   const int64_t nk = (n + NB - 1) / NB;
   hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, stream, ws.A, n, (int64_t)0, ws.status);
   FCHECK(hipGetLastError());
@@ -569,12 +620,16 @@ hipError_t factor_run(float* H, int64_t n, float damp, const FactorWs& ws, hipSt
       FCHECK(gemm_f32(g2, stream));
     }
   }
-  {
-    const unsigned gx = (unsigned)((n + 255) / 256 < 16 ? (n + 255) / 256 : 16);
-    hipLaunchKernelGGL(k_write_factor, dim3(gx, (unsigned)(n < 65535 ? n : 65535)), dim3(256), 0, stream, (const float*)ws.Minv, n,
+  if (vec4) {
+    const unsigned gx = (unsigned)((n / 4 + 255) / 256);
+    hipLaunchKernelGGL(k_write_factor4, dim3(gx, gy), dim3(256), 0, stream, (const float*)ws.Minv, n,
                        (const uint8_t*)ws.dead, H);
-    FCHECK(hipGetLastError());
+  } else {
+    const unsigned gx = (unsigned)((n + 255) / 256 < 16 ? (n + 255) / 256 : 16);
+    hipLaunchKernelGGL(k_write_factor, dim3(gx, gy), dim3(256), 0, stream, (const float*)ws.Minv, n,
+                       (const uint8_t*)ws.dead, H);
   }
+  FCHECK(hipGetLastError());
   return hipSuccess;
 }
 

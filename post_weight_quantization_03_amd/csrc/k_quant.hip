@@ -31,6 +31,38 @@ constexpr int B = 128;
 
 enum GroupMode { GM_BIG = 0, GM_32 = 1, GM_64 = 2 };
 
+// Eight columns a thread; needs cols % 8 == 0, W 16-byte aligned (bf16) or
+// 32-byte (fp32), Wf 32-byte aligned.
+__global__ void k_stage_w8(const void* W, int is_bf16, int64_t rows, int64_t cols, const uint8_t* dead,
+                           float* Wf) {
+  const int64_t chunks = rows * cols / 8;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < chunks; q += stride) {
+    const int64_t i = 8 * q, c = i % cols;
+    float v[8];
+    if (is_bf16) {
+      const uint4 b = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(W) + i);
+      const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(w[e] << 16);
+        v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      }
+    } else {
+      const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(W) + i);
+      const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(W) + i + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    const uint2 d = *reinterpret_cast<const uint2*>(dead + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if ((((e < 4 ? d.x : d.y) >> (8 * (e & 3))) & 0xff) != 0) v[e] = 0.0f;
+    *reinterpret_cast<float4*>(Wf + i) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(Wf + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
 __global__ void k_stage_w(const void* W, int is_bf16, int64_t rows, int64_t cols, const uint8_t* dead,
                           float* Wf) {
   const int64_t total = rows * cols;
@@ -65,6 +97,34 @@ struct BlockArgs {
   float* E;            // this block's scaled errors [rows, 128]
   const float* Eprev;  // the previous block's, when its update of this block is applied here (else null)
 };
+
+// U's upper triangle -> three bf16 planes (the split GEMM's B operand), eight
+// columns a thread; the chunk holding the diagonal also fills the planes'
+// lower triangle, which nothing reads.  Needs n % 8 == 0 and 16-byte aligned U.
+__global__ void k_split_u8(const float* U, int64_t n, uint16_t* P) {
+  const int64_t plane = n * n;
+  for (int64_t i = blockIdx.y; i < n; i += gridDim.y) {
+    for (int64_t q = i / 8 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; 8 * q < n;
+         q += (int64_t)gridDim.x * blockDim.x) {
+      const float4 a = *reinterpret_cast<const float4*>(U + i * n + 8 * q);
+      const float4 b = *reinterpret_cast<const float4*>(U + i * n + 8 * q + 4);
+      const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint32_t w[3][4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        __bf16 h[2][3];
+        split3(x[2 * e], h[0][0], h[0][1], h[0][2]);
+        split3(x[2 * e + 1], h[1][0], h[1][1], h[1][2]);
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+          w[p][e] = (uint32_t)__builtin_bit_cast(uint16_t, h[0][p]) | ((uint32_t)__builtin_bit_cast(uint16_t, h[1][p]) << 16);
+      }
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+        *reinterpret_cast<uint4*>(P + p * plane + i * n + 8 * q) = make_uint4(w[p][0], w[p][1], w[p][2], w[p][3]);
+    }
+  }
+}
 
 // U's upper triangle -> three bf16 planes (the split GEMM's B operand).
 __global__ void k_split_u(const float* U, int64_t n, uint16_t* P) {
@@ -434,10 +494,19 @@ hipError_t quant_run(const QuantArgs& q, hipStream_t stream) {
   const int64_t rows = q.rows, cols = q.cols;
   {
     const int64_t total = rows * cols;
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(k_stage_w, dim3((unsigned)blocks), dim3(256), 0, stream, q.W, q.w_dtype == GPTQ_BF16 ? 1 : 0,
-                       rows, cols, q.dead, q.Wf);
+    const int is_bf16 = q.w_dtype == GPTQ_BF16 ? 1 : 0;
+    const uintptr_t wa = reinterpret_cast<uintptr_t>(q.W);
+    if (cols % 8 == 0 && (wa & (is_bf16 ? 15 : 31)) == 0 && (reinterpret_cast<uintptr_t>(q.Wf) & 31) == 0) {
+      int64_t blocks = (total / 8 + 255) / 256;
+      if (blocks > 16384) blocks = 16384;
+      hipLaunchKernelGGL(k_stage_w8, dim3((unsigned)blocks), dim3(256), 0, stream, q.W, is_bf16, rows, cols, q.dead,
+                         q.Wf);
+    } else {
+      int64_t blocks = (total + 255) / 256;
+      if (blocks > 65536) blocks = 65536;
+      hipLaunchKernelGGL(k_stage_w, dim3((unsigned)blocks), dim3(256), 0, stream, q.W, is_bf16, rows, cols, q.dead,
+                         q.Wf);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -462,9 +531,14 @@ hipError_t quant_run(const QuantArgs& q, hipStream_t stream) {
   float* Ebuf[2] = {q.E, q.E + rows * B};
   if (overlap && cols > 2 * B) {
     if (!q.Usplit) return hipErrorInvalidValue;
-    const unsigned gx = (unsigned)((cols + 255) / 256 < 16 ? (cols + 255) / 256 : 16);
-    hipLaunchKernelGGL(k_split_u, dim3(gx, (unsigned)(cols < 65535 ? cols : 65535)), dim3(256), 0, stream, q.U,
-                       cols, q.Usplit);
+    const unsigned gy = (unsigned)(cols < 65535 ? cols : 65535);
+    if (cols % 8 == 0 && (reinterpret_cast<uintptr_t>(q.U) & 15) == 0) {
+      const unsigned gx = (unsigned)((cols / 8 + 255) / 256);
+      hipLaunchKernelGGL(k_split_u8, dim3(gx, gy), dim3(256), 0, stream, q.U, cols, q.Usplit);
+    } else {
+      const unsigned gx = (unsigned)((cols + 255) / 256 < 16 ? (cols + 255) / 256 : 16);
+      hipLaunchKernelGGL(k_split_u, dim3(gx, gy), dim3(256), 0, stream, q.U, cols, q.Usplit);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
