@@ -90,20 +90,33 @@ __global__ void k_reverse_damped(const float* H, int64_t n, const uint8_t* dead,
 // ------------------------------------------------------------------ diagonal block
 
 // Cholesky of the diagonal block A[k0:k0+kb, k0:k0+kb] (lower triangle in,
-// kb <= 128, padded with the identity beyond kb).  The block is written back
-// as L in the lower triangle and L^T in the strict upper triangle, so the
-// triangular solves below read rows of L^T contiguously.
+// kb <= 128, padded with the identity beyond kb).  The block goes back as L^T
+// in its upper triangle, diagonal included: the triangular solves and inverses
+// read rows of L^T only, and the block's strict lower triangle is unspecified
+// afterwards.
 //
 // 16-column panels, right-looking.  A panel is factored wave-synchronously in
-// registers: each wave carries the panel's 16 diagonal rows in lanes 0..15
-// (the same in every wave) and 48 rows below it in lanes 16..63, a row per
-// lane, the panel's 16 values of the row in 16 VGPRs.  Step c takes the pivot
-// from lane c with readlane, scales column c (one multiply per lane) and
-// subtracts l_i l_j from the panel's later columns j, l_j read from lane j
-// with readlane: no barrier, no LDS inside a panel.  Rows of a lane above the
-// diagonal collect garbage in their upper entries, which no other lane ever
-// reads.  The trailing lower 16x16 tiles then take A_ij -= L_i L_j^T on
-// v_mfma_f32_16x16x4f32 from LDS.  Two barriers per panel.
+// registers: each wave it needs carries the panel's 16 diagonal rows in lanes
+// 0..15 (the same in every such wave) and 48 rows below them in lanes 16..63,
+// a row per lane, the row's 16 panel values in 16 VGPRs.  The panel is
+// eliminated unscaled: step c reads the pivot d_c = a_cc from lane c and the
+// entries a_jc of the later diagonal rows from lanes j with readlane, and
+// every lane subtracts (a_ic / d_c) a_jc from its column j.  A step's
+// dependent chain is readlane, reciprocal, multiply, FMA; the scaling of
+// column c by 1/sqrt(d_c) into L waits for the end of the panel.  No barrier
+// and no LDS traffic inside a panel.  The diagonal rows' lanes collect
+// garbage in their entries above the diagonal, which no step reads.
+//
+// The panel's L then goes to LDS twice: in place (for the trailing update)
+// and transposed into the block's upper triangle (a lane's row becomes a
+// column there, so consecutive lanes write consecutive addresses).  The
+// trailing lower 16x16 tiles take A_ij -= L_i L_j^T on
+// v_mfma_f32_16x16x4f32, each wave loading all of its tiles' operands before
+// its first MFMA.  Two barriers per panel.
+//
+// A pivot that is not positive and finite makes its diagonal entry
+// d * rsq(d) NaN (0 * inf, inf * 0, or rsq of a negative), so one check of
+// L's diagonal at the end finds it.
 constexpr int PB = 16;      // panel width
 constexpr int LP = NB + 1;  // LDS pitch: a column read by 16 lanes hits 16 banks
 
@@ -111,65 +124,96 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
+// waves holding rows of panel P: 48 rows below the diagonal rows per wave
 template <int P>
-__device__ __forceinline__ void potrf_panel(float (*As)[LP], int kb, int wave, int lane, bool& bad) {
+constexpr int panel_waves() {
+  return (NB - PB * (P + 1) + 47) / 48 > 1 ? (NB - PB * (P + 1) + 47) / 48 : 1;
+}
+
+template <int P>
+__device__ __forceinline__ void potrf_panel(float (*As)[LP], int wave, int lane) {
+  if (wave >= panel_waves<P>()) return;
   const int row = lane < PB ? PB * P + lane : PB * P + PB + 48 * wave + (lane - PB);
-  const bool act = wave < 3 && row < NB;
+  const bool act = row < NB;
   float a[PB];
 #pragma unroll
   for (int c = 0; c < PB; ++c) a[c] = act ? As[row][PB * P + c] : 0.0f;
+  float piv[PB];
 #pragma unroll
   for (int c = 0; c < PB; ++c) {
     const float d = readlane_f(a[c], c);
-    const bool ok = d > 0.0f && d < INFINITY;
-    bad |= (PB * P + c < kb) && !ok;
-    const float rl = __builtin_amdgcn_rsqf(ok ? d : 1.0f);
-    const float l = a[c] * rl;
-    a[c] = l;
+    piv[c] = d;
+    float s[PB];
 #pragma unroll
-    for (int j = c + 1; j < PB; ++j) a[j] = fmaf(-l, readlane_f(l, j), a[j]);
+    for (int j = c + 1; j < PB; ++j) s[j] = readlane_f(a[c], j);
+    const float t = a[c] * __builtin_amdgcn_rcpf(d);
+#pragma unroll
+    for (int j = c + 1; j < PB; ++j) a[j] = fmaf(-t, s[j], a[j]);
   }
-  // the diagonal rows once (wave 0), their lower part only
-  if (act && (wave == 0 || lane >= PB)) {
 #pragma unroll
-    for (int c = 0; c < PB; ++c)
-      if (lane >= PB || c <= lane) As[row][PB * P + c] = a[c];
+  for (int c = 0; c < PB; ++c) a[c] *= __builtin_amdgcn_rsqf(piv[c]);
+  // rows below the diagonal rows from every wave; the diagonal rows (their
+  // lower part) once, from wave 0
+  if (act && (lane >= PB || wave == 0)) {
+#pragma unroll
+    for (int c = 0; c < PB; ++c) {
+      if (lane >= PB || c <= lane) {
+        As[row][PB * P + c] = a[c];
+        As[PB * P + c][row] = a[c];
+      }
+    }
   }
 }
 
 template <int P>
 __device__ __forceinline__ void potrf_update(float (*As)[LP], int wave, int lane) {
-  constexpr int T0 = P + 1, NT = NB / PB - T0, NTILES = NT * (NT + 1) / 2;
+  constexpr int T0 = P + 1, NT = NB / PB - T0, NTILES = NT * (NT + 1) / 2, U = (NTILES + 3) / 4;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
   const int i16 = lane & 15, g = lane >> 4;
-  for (int t = wave; t < NTILES; t += 4) {
-    int ti = 0;
-    while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
-    const int tj = t - ti * (ti + 1) / 2 + T0;
-    ti += T0;
-    // v_mfma_f32_16x16x4f32: lane supplies A[i16][g] and B[g][i16]; holds
-    // D[4g + r][i16]
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    f32x4 acc;
+  // v_mfma_f32_16x16x4f32: lane supplies A[i16][g] and B[g][i16] and holds
+  // D[4g + r][i16].  Tile t of the lower triangle (row-major over tile rows
+  // T0..7) goes to wave t % 4; a wave with fewer tiles repeats its last one
+  // and does not store it.
+  int ti[U], tj[U];
+  f32x4 acc[U];
+  float av[U][PB / 4], bv[U][PB / 4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = As[PB * ti + 4 * g + r][PB * tj + i16];
+  for (int u = 0; u < U; ++u) {
+    const int t = wave + 4 * u < NTILES ? wave + 4 * u : NTILES - 1;
+    int r = 0;
+    while ((r + 1) * (r + 2) / 2 <= t) ++r;
+    ti[u] = r + T0;
+    tj[u] = t - r * (r + 1) / 2 + T0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[u][q] = As[PB * ti[u] + 4 * g + q][PB * tj[u] + i16];
 #pragma unroll
     for (int kk = 0; kk < PB / 4; ++kk) {
-      const int k = PB * P + 4 * kk + g;
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-As[PB * ti + i16][k], As[PB * tj + i16][k], acc, 0, 0, 0);
+      av[u][kk] = As[PB * ti[u] + i16][PB * P + 4 * kk + g];
+      bv[u][kk] = As[PB * tj[u] + i16][PB * P + 4 * kk + g];
     }
+  }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) As[PB * ti + 4 * g + r][PB * tj + i16] = acc[r];
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int kk = 0; kk < PB / 4; ++kk)
+      acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(-av[u][kk], bv[u][kk], acc[u], 0, 0, 0);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (wave + 4 * u < NTILES) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) As[PB * ti[u] + 4 * g + q][PB * tj[u] + i16] = acc[u][q];
+    }
   }
 }
 
 template <int P>
-__device__ __forceinline__ void potrf_step(float (*As)[LP], int kb, int wave, int lane, bool& bad) {
-  potrf_panel<P>(As, kb, wave, lane, bad);
+__device__ __forceinline__ void potrf_step(float (*As)[LP], int wave, int lane) {
+  potrf_panel<P>(As, wave, lane);
   __syncthreads();
   if constexpr (P + 1 < NB / PB) {
     potrf_update<P>(As, wave, lane);
     __syncthreads();
-    potrf_step<P + 1>(As, kb, wave, lane, bad);
+    potrf_step<P + 1>(As, wave, lane);
   }
 }
 
@@ -212,25 +256,24 @@ __device__ __forceinline__ void potrf_diag(float* A, int64_t n, int64_t k0, int*
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  bool bad = false;
-  potrf_step<0>(As, kb, wave, lane, bad);
-  if (bad && threadIdx.x == 0) raise_status(status, GPTQ_ENOTPD);
-  __syncthreads();
+  potrf_step<0>(As, wave, lane);
+  if (tid < kb) {
+    const float d = As[tid][tid];
+    if (!(d > 0.0f && d < INFINITY)) raise_status(status, GPTQ_ENOTPD);
+  }
+  // L^T: chunks that reach the diagonal or lie above it
   if (block_vec(A, n, kb)) {
 #pragma unroll 4
     for (int i = 0; i < NB * NB / 4 / 256; ++i) {
       const int idx = tid + 256 * i, r = idx >> 5, q = 4 * (idx & 31);
-      float4 v;
-      v.x = q + 0 <= r ? As[r][q + 0] : As[q + 0][r];
-      v.y = q + 1 <= r ? As[r][q + 1] : As[q + 1][r];
-      v.z = q + 2 <= r ? As[r][q + 2] : As[q + 2][r];
-      v.w = q + 3 <= r ? As[r][q + 3] : As[q + 3][r];
-      *reinterpret_cast<float4*>(A + (k0 + r) * n + k0 + q) = v;
+      if (q + 3 >= r)
+        *reinterpret_cast<float4*>(A + (k0 + r) * n + k0 + q) =
+            make_float4(As[r][q + 0], As[r][q + 1], As[r][q + 2], As[r][q + 3]);
     }
   } else {
     for (int idx = tid; idx < NB * NB; idx += 256) {
       const int r = idx >> 7, q = idx & (NB - 1);
-      if (r < kb && q < kb) A[(k0 + r) * n + k0 + q] = q <= r ? As[r][q] : As[q][r];
+      if (q >= r && q < kb) A[(k0 + r) * n + k0 + q] = As[r][q];
     }
   }
 }
