@@ -257,13 +257,21 @@ __device__ __forceinline__ void run_steps(Lane& L, const BlockArgs& a, const flo
 }
 
 // LDS of one column-loop workgroup: the U block, 1/U_jj, and the previous
-// block's errors of its 16 rows.
+// block's update of its 16 rows.
 constexpr int QUANT_LDS = B * B * 4 + B * 4 + 16 * B * 4;
 
 // One workgroup of the block: rows 16 wg .. 16 wg + 15.  With a.Eprev the
 // previous block's update of this block's columns, W[r, c0:c0+bw] -=
-// Eprev[r, :] U[c0-128:c0, c0:c0+bw], is applied to the rows in registers
-// first (the rest of that update runs beside this block, see quant_run).
+// Eprev[r, :] U[c0-128:c0, c0:c0+bw], is applied to the rows first (the rest
+// of that update runs beside this block, see quant_run).  It runs on
+// v_mfma_f32_16x16x4f32 with both operands straight from global memory
+// (both are read by every workgroup of the launch, so they come from L2):
+// wave v owns columns 32v .. 32v+31 as two 16-column tiles, and lane (i, g)
+// (i = lane % 16, g = lane / 16) supplies k = 32g + kk at step kk, an order
+// of k the sum does not care about, which makes its 32 values of E one
+// contiguous run.  The product reaches the loop's layout through LDS.  The
+// U block of the loop is loaded before that update, so its latency hides
+// under it.
 template <int MODE>
 __device__ __forceinline__ void quant_block_wg(const BlockArgs& a, int64_t wg, char* lds) {
   float(*Us)[B] = reinterpret_cast<float(*)[B]>(lds);
@@ -287,68 +295,61 @@ __device__ __forceinline__ void quant_block_wg(const BlockArgs& a, int64_t wg, c
 #pragma unroll
     for (int i = 0; i < 8; ++i) w[i] = (row_ok && t8 + i < a.bw) ? a.Wf[base + i] : 0.0f;
   }
+  // loads first: E and U operands of the previous block's update, then the
+  // U block of this one
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int i16 = lane & 15, g = lane >> 4, wv = tid >> 6;
+  float ea[32], ub[2][32];
   if (a.Eprev) {
-    // Us[k][m] = U[c0-128+k][c0+m] (the previous block's rows, all of them
-    // above this block), Es = the previous errors of the 16 rows
-    const int64_t cp = c0 - B;
-    for (int idx = tid; idx < B * B / 4; idx += 256) {
-      const int k = idx >> 5, m = 4 * (idx & 31);
-      float4 v;
-      if (vec) {
-        v = *reinterpret_cast<const float4*>(a.U + (cp + k) * cols + c0 + m);
-      } else {
-        const float* src = a.U + (cp + k) * cols + c0 + m;
-        v.x = m + 0 < a.bw ? src[0] : 0.0f;
-        v.y = m + 1 < a.bw ? src[1] : 0.0f;
-        v.z = m + 2 < a.bw ? src[2] : 0.0f;
-        v.w = m + 3 < a.bw ? src[3] : 0.0f;
+    const int64_t er = wg * 16 + i16, cp = c0 - B;
+    if (er < a.rows) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(a.Eprev + er * B + 32 * g + 4 * q);
+        ea[4 * q + 0] = v.x; ea[4 * q + 1] = v.y; ea[4 * q + 2] = v.z; ea[4 * q + 3] = v.w;
       }
-      *reinterpret_cast<float4*>(&Us[k][m]) = v;
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 32; ++kk) ea[kk] = 0.0f;
     }
-    for (int idx = tid; idx < 16 * B / 4; idx += 256) {
-      const int r = idx >> 5, k = 4 * (idx & 31);
-      const int64_t gr = wg * 16 + r;
-      *reinterpret_cast<float4*>(&Es[r][k]) =
-          gr < a.rows ? *reinterpret_cast<const float4*>(a.Eprev + gr * B + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int col = 32 * wv + 16 * h + i16;
+      const bool ok = col < a.bw;
+      const float* src = a.U + (cp + 32 * g) * cols + c0 + (ok ? col : 0);
+#pragma unroll
+      for (int kk = 0; kk < 32; ++kk) ub[h][kk] = ok ? src[kk * cols] : 0.0f;
     }
-    __syncthreads();
-    const int rl = (tid >> 6) * 4 + (lane >> 4);
-#pragma unroll 8
-    for (int k = 0; k < B; ++k) {
-      const float e = Es[rl][k];
-      const float4 u0 = *reinterpret_cast<const float4*>(&Us[k][t8]);
-      const float4 u1 = *reinterpret_cast<const float4*>(&Us[k][t8 + 4]);
-      w[0] = fmaf(-e, u0.x, w[0]);
-      w[1] = fmaf(-e, u0.y, w[1]);
-      w[2] = fmaf(-e, u0.z, w[2]);
-      w[3] = fmaf(-e, u0.w, w[3]);
-      w[4] = fmaf(-e, u1.x, w[4]);
-      w[5] = fmaf(-e, u1.y, w[5]);
-      w[6] = fmaf(-e, u1.z, w[6]);
-      w[7] = fmaf(-e, u1.w, w[7]);
-    }
-    __syncthreads();
   }
   // U block without its diagonal: Us[j][k] = U[c0+j][c0+k] for k > j inside
   // the block, else 0 (the feedback of step j reaches only k > j, so a column
   // keeps its decision-time value; 1/U_jj comes separately).  Whole blocks
   // with 16-byte rows load as 16 float4 per thread, all in flight at once.
+  float4 uv[B * B / 4 / 256];
   if (vec) {
-    float4 v[B * B / 4 / 256];
 #pragma unroll
     for (int i = 0; i < B * B / 4 / 256; ++i) {
       const int idx = tid + 256 * i, j = idx >> 5, k = 4 * (idx & 31);
-      v[i] = *reinterpret_cast<const float4*>(a.U + (c0 + j) * cols + c0 + k);
+      uv[i] = *reinterpret_cast<const float4*>(a.U + (c0 + j) * cols + c0 + k);
     }
+  }
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  if (a.Eprev) {
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[kk], ub[h][kk], acc[h], 0, 0, 0);
+  }
+  if (vec) {
 #pragma unroll
     for (int i = 0; i < B * B / 4 / 256; ++i) {
       const int idx = tid + 256 * i, j = idx >> 5, k = 4 * (idx & 31);
-      float4 w = v[i];
-      w.x = k + 0 > j ? w.x : 0.0f;
-      w.y = k + 1 > j ? w.y : 0.0f;
-      w.z = k + 2 > j ? w.z : 0.0f;
-      w.w = k + 3 > j ? w.w : 0.0f;
-      *reinterpret_cast<float4*>(&Us[j][k]) = w;
+      float4 u = uv[i];
+      u.x = k + 0 > j ? u.x : 0.0f;
+      u.y = k + 1 > j ? u.y : 0.0f;
+      u.z = k + 2 > j ? u.z : 0.0f;
+      u.w = k + 3 > j ? u.w : 0.0f;
+      *reinterpret_cast<float4*>(&Us[j][k]) = u;
     }
   } else {
     for (int idx = tid; idx < B * B; idx += 256) {
@@ -359,7 +360,21 @@ __device__ __forceinline__ void quant_block_wg(const BlockArgs& a, int64_t wg, c
     }
   }
   if (tid < B) rUd[tid] = tid < a.bw ? 1.0f / a.U[(c0 + tid) * cols + c0 + tid] : 0.0f;
+  if (a.Eprev) {
+    // tile h holds D[4g + r][i16] for columns 32 wv + 16 h + i16
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Es[4 * g + r][32 * wv + 16 * h + i16] = acc[h][r];
+  }
   __syncthreads();
+  if (a.Eprev) {
+    const int rl = (tid >> 6) * 4 + (lane >> 4);
+    const float4 d0 = *reinterpret_cast<const float4*>(&Es[rl][t8]);
+    const float4 d1 = *reinterpret_cast<const float4*>(&Es[rl][t8 + 4]);
+    w[0] -= d0.x; w[1] -= d0.y; w[2] -= d0.z; w[3] -= d0.w;
+    w[4] -= d1.x; w[5] -= d1.y; w[6] -= d1.z; w[7] -= d1.w;
+  }
 
   Lane L;
   L.t = lane & 15;
