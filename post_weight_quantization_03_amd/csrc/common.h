@@ -64,12 +64,10 @@ struct FactorWs {
   int* status;      // device int32
   float* lam;       // device: lambda (float)
   uint8_t* dead;    // device [n]
-  float* A;         // [n, n] reversed damped Hessian -> lower Cholesky factor (off-diagonal blocks)
-  float* Minv;      // [n, n] inverse of that factor (lower)
-  float* T;         // [tmax, tmax] scratch for the triangular inverse
-  int64_t tmax;
+  float* A;         // [n, n] reversed damped Hessian -> L below the diagonal blocks, L^-T above
+  float* Lt;        // [ceil(n / 128), 128, 128] L_kk^T of each diagonal block
 };
-size_t factor_scratch_floats(int64_t n, int64_t* tmax);
+size_t factor_scratch_floats(int64_t n);  // floats of FactorWs::Lt
 // H (fp32 [n, n]) -> damped, factored; U written back to H's upper triangle, dead flags to the
 // strictly lower slots.  Status (ENOTPD) is raised on the device.
 hipError_t factor_run(float* H, int64_t n, float damp, const FactorWs& ws, hipStream_t stream);

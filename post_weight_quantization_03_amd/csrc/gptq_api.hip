@@ -11,8 +11,7 @@ constexpr int VERSION = 100;  // 0.1.0
 constexpr int64_t MAX_DIM = (int64_t)1 << 30;
 
 struct QuantLayout {
-  size_t status, lam, dead, loss, Wf, E, Us, A, Minv, T, total;
-  int64_t tmax;
+  size_t status, lam, dead, loss, Wf, E, Us, A, Lt, total;
 };
 
 bool params_ok(const gptq_params* p, int64_t cols, int* why) {
@@ -47,12 +46,8 @@ QuantLayout layout(int64_t rows, int64_t cols, const gptq_params* p) {
     L.Us = ub ? take(ub) : 0;
   }
   if (!(p->flags & GPTQ_H_IS_FACTOR)) {
-    int64_t tmax = 0;
-    factor_scratch_floats(cols, &tmax);
-    L.tmax = tmax;
     L.A = take((size_t)cols * cols * sizeof(float));
-    L.Minv = take((size_t)cols * cols * sizeof(float));
-    L.T = take((size_t)(tmax > 0 ? tmax : 1) * sizeof(float));
+    L.Lt = take(factor_scratch_floats(cols) * sizeof(float));
   }
   L.total = off;
   return L;
@@ -134,9 +129,7 @@ int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t rows, int64_t
     f.lam = reinterpret_cast<float*>(ws + L.lam);
     f.dead = dead;
     f.A = reinterpret_cast<float*>(ws + L.A);
-    f.Minv = reinterpret_cast<float*>(ws + L.Minv);
-    f.T = reinterpret_cast<float*>(ws + L.T);
-    f.tmax = L.tmax;
+    f.Lt = reinterpret_cast<float*>(ws + L.Lt);
     e = factor_run(H, cols, p->damp, f, stream);
   }
   if (e != hipSuccess) return GPTQ_EHIP;

@@ -9,19 +9,22 @@
 //
 //  1. k_damp_stats     one workgroup: dead columns (H_ii == 0 -> 1), lambda =
 //                      damp * mean(diag) (fp64 sum in a fixed order).
-//  2. k_reverse_damped A = P H_d P, lower triangle, fp32.
-//  3. blocked right-looking Cholesky, nb = 128: k_potrf_diag factors the
-//     diagonal block; the panel below becomes L_ik = A_ik L_kk^-T by
-//     row-parallel forward substitution (k_trsm_rows) and the trailing lower
-//     tiles take A_ij -= L_ik L_jk^T (GEMM), in the same launch as the factor
-//     of the next diagonal block (k_factor_step, look-ahead).  The inverses of the diagonal
-//     blocks are formed after the loop, all at once and off the loop's
-//     critical path (k_trsm_rows on identity rows).
-//  4. triangular inverse by doubling: with the 128-blocks of Minv inverted,
-//     each level joins pairs of inverted diagonal blocks,
-//     [P 0; C Q]^-1 = [P^-1 0; -Q^-1 C P^-1 Q^-1], as two batched GEMMs.
-//  5. k_write_factor   U[i][j] = Minv[n-1-i][n-1-j] for i <= j into H, plus the
-//     dead flags in H's strictly lower triangle.
+//  2. k_reverse_damped A = P H_d P in the lower triangle, zeros above, fp32.
+//  3. blocked right-looking Cholesky, nb = 128, with the triangular inverse
+//     folded in.  Per block k: k_trsm_block solves every row of block column
+//     k against L_kk (the panel below, L_ik = A_ik L_kk^-T; the rows of the
+//     block, L_kk^-T itself; the rows above, the block column k of L^-T, which
+//     accumulates in A's upper triangle); then one GEMM takes all rows of the
+//     columns right of block k, A[r][j] -= A[r][k0:c1] L[j][k0:c1]^T: below c1
+//     the Cholesky trailing update, above it the next term of the inverse's
+//     right-looking block forward substitution, X_ij -= L_ik X_kj in the
+//     transposed layout.  That GEMM runs in the same launch as the factor of
+//     block k+1 (k_factor_step, look-ahead; k_potrf_diag factors a diagonal
+//     block and hands L^T to the solves in a buffer of its own).  The
+//     inverse's work thus fills the CUs that the Cholesky's late, narrow
+//     steps leave idle, and nothing of it is left after the loop.
+//  4. k_write_factor   U[i][j] = Y[n-1-j][n-1-i] for i <= j into H (Y = L^-T,
+//     A's upper triangle), plus the dead flags in H's strictly lower triangle.
 #include <utility>
 
 #include "gemm_tile.h"
@@ -50,36 +53,42 @@ __global__ __launch_bounds__(1024) void k_damp_stats(const float* H, int64_t n, 
   if (threadIdx.x == 0) *lam = (float)((double)damp * part[0] / (double)n);
 }
 
-// A[i][j] = H_d[n-1-i][n-1-j] for j <= i, four columns a thread: the source
-// is the float4 of row n-1-i ending at column n-1-j, read backwards.  Chunks
-// reaching past the diagonal also write A's upper triangle, which nothing reads.
+// A[i][j] = H_d[n-1-i][n-1-j] for j <= i and 0 above the diagonal (where the
+// factor accumulates the transposed inverse), four columns a thread: the
+// source is the float4 of row n-1-i ending at column n-1-j, read backwards.
 // Needs n % 4 == 0 and 16-byte aligned H and A.
 __global__ void k_reverse_damped4(const float* H, int64_t n, const uint8_t* dead, const float* lam, float* A) {
   const float l = *lam;
   for (int64_t i = blockIdx.y; i < n; i += gridDim.y) {
     const int64_t si = n - 1 - i;
-    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; 4 * q <= i; q += (int64_t)gridDim.x * blockDim.x) {
-      const float4 v = *reinterpret_cast<const float4*>(H + si * n + (n - 4 - 4 * q));
-      float o[4] = {v.w, v.z, v.y, v.x};
-      const int64_t e = i - 4 * q;  // the diagonal, if in this chunk
-      if (e < 4) o[e] = (dead[si] ? 1.0f : o[e]) + l;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; 4 * q < n; q += (int64_t)gridDim.x * blockDim.x) {
+      float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (4 * q <= i) {
+        const float4 v = *reinterpret_cast<const float4*>(H + si * n + (n - 4 - 4 * q));
+        o[0] = v.w; o[1] = v.z; o[2] = v.y; o[3] = v.x;
+        const int64_t e = i - 4 * q;  // the diagonal, if in this chunk
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          if (f == e) o[f] = (dead[si] ? 1.0f : o[f]) + l;
+          if (f > e) o[f] = 0.0f;
+        }
+      }
       *reinterpret_cast<float4*>(A + i * n + 4 * q) = make_float4(o[0], o[1], o[2], o[3]);
     }
   }
 }
 
-// A[i][j] = H_d[n-1-i][n-1-j] for j <= i; rows in blockIdx.y, columns in grid-stride x.
 __global__ void k_reverse_damped(const float* H, int64_t n, const uint8_t* dead, const float* lam, float* A) {
   const float l = *lam;
   for (int64_t i = blockIdx.y; i < n; i += gridDim.y) {
   const int64_t si = n - 1 - i;
-  for (int64_t j = blockIdx.x * blockDim.x + threadIdx.x; j <= i; j += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += (int64_t)gridDim.x * blockDim.x) {
     const int64_t sj = n - 1 - j;
-    float v;
+    float v = 0.0f;
     if (j == i) {
       const float d = H[si * n + si];
       v = (dead[si] ? 1.0f : d) + l;
-    } else {
+    } else if (j < i) {
       v = H[si * n + sj];  // sj > si: the upper triangle of H
     }
     A[i * n + j] = v;
@@ -90,10 +99,10 @@ __global__ void k_reverse_damped(const float* H, int64_t n, const uint8_t* dead,
 // ------------------------------------------------------------------ diagonal block
 
 // Cholesky of the diagonal block A[k0:k0+kb, k0:k0+kb] (lower triangle in,
-// kb <= 128, padded with the identity beyond kb).  The block goes back as L^T
-// in its upper triangle, diagonal included: the triangular solves and inverses
-// read rows of L^T only, and the block's strict lower triangle is unspecified
-// afterwards.
+// kb <= 128, padded with the identity beyond kb).  L^T goes to a 128 x 128
+// buffer of its own (row-major, zeros below the diagonal, the identity past
+// kb), from which the triangular solves of the block read it; A is not
+// written.
 //
 // 16-column panels, right-looking.  A panel is factored wave-synchronously in
 // registers: each wave it needs carries the panel's 16 diagonal rows in lanes
@@ -225,7 +234,7 @@ __device__ __forceinline__ bool block_vec(const float* A, int64_t n, int kb) {
 
 constexpr int POTRF_LDS = NB * LP * 4;
 
-__device__ __forceinline__ void potrf_diag(float* A, int64_t n, int64_t k0, int* status, char* lds) {
+__device__ __forceinline__ void potrf_diag(const float* A, int64_t n, int64_t k0, float* Lt, int* status, char* lds) {
   float(*As)[LP] = reinterpret_cast<float(*)[LP]>(lds);
   const int kb = (int)((n - k0) < NB ? (n - k0) : NB);
   const int tid = threadIdx.x;
@@ -261,71 +270,79 @@ __device__ __forceinline__ void potrf_diag(float* A, int64_t n, int64_t k0, int*
     const float d = As[tid][tid];
     if (!(d > 0.0f && d < INFINITY)) raise_status(status, GPTQ_ENOTPD);
   }
-  // L^T: chunks that reach the diagonal or lie above it
-  if (block_vec(A, n, kb)) {
+  // L^T, whole rows
 #pragma unroll 4
-    for (int i = 0; i < NB * NB / 4 / 256; ++i) {
-      const int idx = tid + 256 * i, r = idx >> 5, q = 4 * (idx & 31);
-      if (q + 3 >= r)
-        *reinterpret_cast<float4*>(A + (k0 + r) * n + k0 + q) =
-            make_float4(As[r][q + 0], As[r][q + 1], As[r][q + 2], As[r][q + 3]);
-    }
-  } else {
-    for (int idx = tid; idx < NB * NB; idx += 256) {
-      const int r = idx >> 7, q = idx & (NB - 1);
-      if (q >= r && q < kb) A[(k0 + r) * n + k0 + q] = As[r][q];
-    }
+  for (int i = 0; i < NB * NB / 4 / 256; ++i) {
+    const int idx = tid + 256 * i, r = idx >> 5, q = 4 * (idx & 31);
+    float4 v;
+    v.x = q + 0 >= r ? As[r][q + 0] : 0.0f;
+    v.y = q + 1 >= r ? As[r][q + 1] : 0.0f;
+    v.z = q + 2 >= r ? As[r][q + 2] : 0.0f;
+    v.w = q + 3 >= r ? As[r][q + 3] : 0.0f;
+    *reinterpret_cast<float4*>(Lt + r * NB + q) = v;
   }
 }
 
-__global__ __launch_bounds__(256) void k_potrf_diag(float* A, int64_t n, int64_t k0, int* status) {
+__global__ __launch_bounds__(256) void k_potrf_diag(const float* A, int64_t n, int64_t k0, float* Lt, int* status) {
   __shared__ __attribute__((aligned(16))) char lds[POTRF_LDS];
-  potrf_diag(A, n, k0, status, lds);
+  potrf_diag(A, n, k0, Lt, status, lds);
 }
 
-// One step of the blocked factor with look-ahead: the trailing update of
-// block k, A22 -= L21 L21^T on lower tiles, beside the factor of block k+1.
-// Block k+1's diagonal block (A22's first 128 x 128 tile) has been updated by
-// a small launch before this one; workgroup 0 factors it while the other
-// workgroups update the remaining lower tiles (the first `skip` tiles of size
-// TM cover that block and are left out).
+// One step of the blocked factor with look-ahead, block k (columns
+// [k0, c1)): one GEMM over all rows and the columns right of the block,
+//   A[r][j] -= A[r][k0:c1] L[j][k0:c1]^T   (r in [0, n), j in [c1, n)),
+// beside the factor of block k+1.  Rows r >= c1 are the Cholesky trailing
+// update A22 -= L21 L21^T, lower tiles only.  Rows r < c1 accumulate the
+// inverse: there A[r][k0:c1] holds finished entries of L^-T (transposed
+// inverse, upper triangle), and A[r][j] the running sums that the solve of
+// block column j finishes.  Block k+1's diagonal block has been updated by a
+// small launch before this one; workgroup 0 factors it while the other
+// workgroups take the tiles: the lower tiles of the trailing matrix first
+// (the first `skip` cover that diagonal block and are left out), then the
+// rectangle above c1 (`rrows` tile rows of `nt` tiles), row-major.
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // More than half of the CU's LDS per workgroup: one workgroup per CU, so the
 // diagonal factor never shares its CU with a tile (sharing one made the factor
 // up to 1.9x slower; the tiles lose less than that gains).
 template <int TM>
-__global__ __launch_bounds__(256) void k_factor_step(GemmF32 trail, int skip, float* A, int64_t n, int64_t k0n,
-                                                     int* status) {
+__global__ __launch_bounds__(256) void k_factor_step(GemmF32 g, int skip, int ntri, int rrows, int nt, const float* A,
+                                                     int64_t n, int64_t k0n, float* Lt, int* status) {
   __shared__ __attribute__((aligned(16))) char
       lds[cmax(96 * 1024, cmax(POTRF_LDS, cmax(gemm_tile_lds<128>(), gemm_tile_lds<TM>())))];
   if (blockIdx.x == 0) {
-    potrf_diag(A, n, k0n, status, lds);
+    potrf_diag(A, n, k0n, Lt, status, lds);
     return;
   }
-  const int t = (int)blockIdx.x - 1 + skip;
-  int r = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
-  while ((r + 1) * (r + 2) / 2 <= t) ++r;
-  while (r * (r + 1) / 2 > t) --r;
-  gemm_tile<TM, false>(trail, r, t - r * (r + 1) / 2, 0, lds);
+  const int u = (int)blockIdx.x - 1;
+  if (u < ntri - skip) {
+    const int t = u + skip;
+    int r = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
+    while ((r + 1) * (r + 2) / 2 <= t) ++r;
+    while (r * (r + 1) / 2 > t) --r;
+    gemm_tile<TM, false>(g, rrows + r, t - r * (r + 1) / 2, 0, lds);
+  } else {
+    const int v = u - (ntri - skip);
+    gemm_tile<TM, false>(g, v / nt, v % nt, 0, lds);
+  }
 }
 
 // ------------------------------------------------------------------ triangular solves
 
-// Rows y = b L^-T for the diagonal block's L (read as L^T from the block's
-// upper triangle, diagonal from the block), i.e. L y^T = b^T by forward
-// substitution, right-looking: y_j = b_j / L_jj, then b_m -= y_j L_mj for m > j.
-// The same layout as the column loop: a 64-lane wave holds 4 rows, 16 lanes a
-// row, 8 consecutive columns per lane; y_j reaches the row's lanes by a DPP
-// row broadcast; L^T sits in LDS without its diagonal, and the row of step
-// j+1 is read during step j.  Column j is final after step j, so y is formed
-// after the loop as b * (1 / L_jj).
+// Rows y = b L^-T for block k's L, i.e. L y^T = b^T by forward substitution,
+// right-looking: y_j = b_j / L_jj, then b_m -= y_j L_mj for m > j.  L^T comes
+// from the factor's buffer.  The same layout as the column loop: a 64-lane wave
+// holds 4 rows, 16 lanes a row, 8 consecutive columns per lane; y_j reaches
+// the row's lanes by a DPP row broadcast; L^T sits in LDS without its
+// diagonal, and the row of step j+1 is read during step j.  Column j is final
+// after step j, so y is formed after the loop as b * (1 / L_jj).
 //
-// IDENT = false: the panel below the block, rows [r0, r0 + rows) of A at
-//   columns [k0, k0 + 128), solved in place (L_ik = A_ik L_kk^-T).
-// IDENT = true: b = e_r for r = 0 .. 127 of diagonal block blockIdx.y: y is
-//   row r of L^-T, i.e. column r of L^-1, stored into the same block of Minv
-//   (lower, zeros above the diagonal).
+// One launch takes every row of block column k (columns [k0, k0 + kb)):
+//   rows below the block: the panel, L_ik = A_ik L_kk^-T, in place;
+//   rows above it: the block column of the transposed inverse, finished in
+//     place from the sums the earlier steps accumulated there;
+//   rows of the block: b = e_r, y = row r of L_kk^-T, written over the
+//     block's row r (zeros left of the diagonal).
 template <int O>
 __device__ __forceinline__ float row_bcast(float v) {
   return __builtin_amdgcn_update_dpp(0.0f, v, 0x150 + O, 0xf, 0xf, false);
@@ -358,22 +375,18 @@ __device__ __forceinline__ void trsm_steps(TrsmLane& L, const float (*Lt)[NB], s
   (trsm_step<Js>(L, Lt), ...);
 }
 
-template <bool IDENT>
-__global__ __launch_bounds__(256) void k_trsm_rows(float* A, float* Minv, int64_t n, int64_t k0_, int64_t r0,
-                                                   int64_t rows) {
+__global__ __launch_bounds__(256) void k_trsm_block(float* A, const float* Ltk, int64_t n, int64_t k0, int kb) {
   __shared__ __attribute__((aligned(16))) float Lt[NB][NB];
   __shared__ float rL[NB];
-  const int64_t k0 = IDENT ? (int64_t)blockIdx.y * NB : k0_;
-  const int kb = (int)((n - k0) < NB ? (n - k0) : NB);
   const int tid = threadIdx.x;
-  // Lt[j][m] = L[m][j] for m > j (the block's upper triangle), else 0
-  if (block_vec(A, n, kb)) {
+  // Lt[j][m] = L[m][j] for m > j, else 0 (the buffer holds zeros below its diagonal)
+  {
     constexpr int PER = NB * NB / 4 / 256;
     float4 v[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int idx = tid + 256 * i, j = idx >> 5, m = 4 * (idx & 31);
-      v[i] = *reinterpret_cast<const float4*>(A + (k0 + j) * n + k0 + m);
+      v[i] = *reinterpret_cast<const float4*>(Ltk + j * NB + m);
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -385,30 +398,19 @@ __global__ __launch_bounds__(256) void k_trsm_rows(float* A, float* Minv, int64_
       w.w = m + 3 > j ? w.w : 0.0f;
       *reinterpret_cast<float4*>(&Lt[j][m]) = w;
     }
-  } else {
-    for (int idx = tid; idx < NB * NB / 4; idx += 256) {
-      const int j = idx >> 5, m = 4 * (idx & 31);
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (j < kb) {
-        const float* src = A + (k0 + j) * n + k0 + m;
-        v.x = (m + 0 > j && m + 0 < kb) ? src[0] : 0.0f;
-        v.y = (m + 1 > j && m + 1 < kb) ? src[1] : 0.0f;
-        v.z = (m + 2 > j && m + 2 < kb) ? src[2] : 0.0f;
-        v.w = (m + 3 > j && m + 3 < kb) ? src[3] : 0.0f;
-      }
-      *reinterpret_cast<float4*>(&Lt[j][m]) = v;
-    }
   }
-  if (tid < NB) rL[tid] = tid < kb ? 1.0f / A[(k0 + tid) * (n + 1)] : 0.0f;
+  if (tid < NB) rL[tid] = tid < kb ? 1.0f / Ltk[tid * (NB + 1)] : 0.0f;
   __syncthreads();
 
   TrsmLane L;
   const int lane = tid & 63;
   L.t = lane & 15;
-  const int64_t rr = (int64_t)blockIdx.x * 16 + (tid >> 6) * 4 + (lane >> 4);
-  const bool ok = IDENT ? rr < kb : rr < rows;
-  const int64_t grow = r0 + rr;
-  if (!IDENT && ok && block_vec(A, n, kb)) {
+  const int64_t grow = (int64_t)blockIdx.x * 16 + (tid >> 6) * 4 + (lane >> 4);
+  const bool ok = grow < n;
+  const bool ident = grow >= k0 && grow < k0 + kb;
+  const int rr = (int)(grow - k0);
+  const bool vec = kb == NB && (n & 3) == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
+  if (ok && !ident && vec) {
     const float4 b0 = *reinterpret_cast<const float4*>(A + grow * n + k0 + 8 * L.t);
     const float4 b1 = *reinterpret_cast<const float4*>(A + grow * n + k0 + 8 * L.t + 4);
     L.b[0] = b0.x; L.b[1] = b0.y; L.b[2] = b0.z; L.b[3] = b0.w;
@@ -417,10 +419,10 @@ __global__ __launch_bounds__(256) void k_trsm_rows(float* A, float* Minv, int64_
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int c = 8 * L.t + i;
-      if constexpr (IDENT)
-        L.b[i] = (ok && c == rr) ? 1.0f : 0.0f;
+      if (ident)
+        L.b[i] = c == rr ? 1.0f : 0.0f;
       else
-        L.b[i] = ok ? A[grow * n + k0 + c] : 0.0f;
+        L.b[i] = (ok && c < kb) ? A[grow * n + k0 + c] : 0.0f;
     }
   }
 #pragma unroll
@@ -429,54 +431,43 @@ __global__ __launch_bounds__(256) void k_trsm_rows(float* A, float* Minv, int64_
   L.un[1] = *reinterpret_cast<const float4*>(&Lt[0][8 * L.t + 4]);
   trsm_steps(L, Lt, std::make_integer_sequence<int, NB>{});
   if (!ok) return;
+  float y[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = 8 * L.t + i;
-    const float y = L.b[i] * L.ru[i];
-    if constexpr (IDENT) {
-      if (c < kb) Minv[(k0 + c) * n + k0 + rr] = (c >= rr) ? y : 0.0f;
-    } else {
-      A[grow * n + k0 + c] = y;
-    }
+  for (int i = 0; i < 8; ++i) y[i] = (ident && 8 * L.t + i < rr) ? 0.0f : L.b[i] * L.ru[i];
+  if (vec) {
+    *reinterpret_cast<float4*>(A + grow * n + k0 + 8 * L.t) = make_float4(y[0], y[1], y[2], y[3]);
+    *reinterpret_cast<float4*>(A + grow * n + k0 + 8 * L.t + 4) = make_float4(y[4], y[5], y[6], y[7]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (8 * L.t + i < kb) A[grow * n + k0 + 8 * L.t + i] = y[i];
   }
 }
 
-// U[i][j] = Minv[n-1-i][n-1-j] for j >= i into H, four columns a thread (the
-// chunk holding the diagonal element by element, so H[i][j < i] keeps its
-// dead flags); dead flags into H[i][i-1] and H[n-1][0].  Needs n % 4 == 0 and
-// 16-byte aligned Minv and H.
-__global__ void k_write_factor4(const float* Minv, int64_t n, const uint8_t* dead, float* H) {
-  for (int64_t i = blockIdx.y; i < n; i += gridDim.y) {
-    const int64_t si = n - 1 - i;
-    for (int64_t q = i / 4 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; 4 * q < n;
-         q += (int64_t)gridDim.x * blockDim.x) {
-      const float4 v = *reinterpret_cast<const float4*>(Minv + si * n + (n - 4 - 4 * q));
-      const float o[4] = {v.w, v.z, v.y, v.x};
-      if (4 * q >= i) {
-        *reinterpret_cast<float4*>(H + i * n + 4 * q) = make_float4(o[0], o[1], o[2], o[3]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (4 * q + e >= i) H[i * n + 4 * q + e] = o[e];
-      }
-    }
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-      if (i >= 1) H[i * n + i - 1] = dead[i] ? 1.0f : 0.0f;
-      if (i == n - 1 && n >= 3) H[i * n + 0] = dead[0] ? 1.0f : 0.0f;
-    }
+// U[i][j] = Y[n-1-j][n-1-i] for j >= i into H, with Y = L^-T the upper
+// triangle of A (U = P L^-1 P), by 64 x 64 tiles transposed through LDS: both
+// the reads of Y and the writes of H run along rows.  Tiles on the diagonal
+// also write the dead flags of their rows into H[i][i-1], and H[n-1][0] for
+// column 0.
+__global__ __launch_bounds__(256) void k_write_factor(const float* Y, int64_t n, const uint8_t* dead, float* H) {
+  __shared__ float T[64][65];
+  const int64_t I0 = (int64_t)blockIdx.y * 64, J0 = (int64_t)blockIdx.x * 64;
+  if (J0 + 63 < I0) return;
+  const int64_t yr0 = n - J0 - 64, yc0 = n - I0 - 64;  // negative at a ragged edge
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int k = ty; k < 64; k += 4) {
+    const int64_t yr = yr0 + k, yc = yc0 + tx;
+    T[k][tx] = (yr >= 0 && yc >= 0) ? Y[yr * n + yc] : 0.0f;
   }
-}
-
-// U[i][j] = Minv[n-1-i][n-1-j] for j >= i, written into H; dead flags into the
-// strictly lower slots H[i][i-1] (column i >= 1) and H[n-1][0] (column 0).
-__global__ void k_write_factor(const float* Minv, int64_t n, const uint8_t* dead, float* H) {
-  for (int64_t i = blockIdx.y; i < n; i += gridDim.y) {
-    for (int64_t j = i + blockIdx.x * blockDim.x + threadIdx.x; j < n; j += (int64_t)gridDim.x * blockDim.x)
-      H[i * n + j] = Minv[(n - 1 - i) * n + (n - 1 - j)];
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-      if (i >= 1) H[i * n + i - 1] = dead[i] ? 1.0f : 0.0f;
-      if (i == n - 1 && n >= 3) H[i * n + 0] = dead[0] ? 1.0f : 0.0f;
-    }
+  __syncthreads();
+  for (int a = ty; a < 64; a += 4) {
+    const int64_t i = I0 + a, j = J0 + tx;
+    if (i < n && j < n && j >= i) H[i * n + j] = T[63 - tx][63 - a];
+  }
+  if (I0 == J0 && ty == 0) {
+    const int64_t i = I0 + tx;
+    if (i >= 1 && i < n) H[i * n + i - 1] = dead[i] ? 1.0f : 0.0f;
+    if (i == n - 1 && n >= 3) H[i * n + 0] = dead[0] ? 1.0f : 0.0f;
   }
 }
 
@@ -498,21 +489,7 @@ __global__ void k_copy_status(const int* src, int32_t* dst) {
 
 }  // namespace
 
-// Scratch for the doubling levels: level s holds one s x s product per pair.
-static int64_t doubling_scratch(int64_t n) {
-  int64_t best = 0;
-  for (int64_t s = NB; s < n; s *= 2) {
-    const int64_t pairs = n / (2 * s) + ((n - (n / (2 * s)) * 2 * s - s) > 0 ? 1 : 0);
-    if (pairs * s * s > best) best = pairs * s * s;
-  }
-  return best;
-}
-
-size_t factor_scratch_floats(int64_t n, int64_t* tmax) {
-  const int64_t t = doubling_scratch(n);
-  if (tmax) *tmax = t;
-  return (size_t)(2 * n * n + t);
-}
+size_t factor_scratch_floats(int64_t n) { return (size_t)((n + NB - 1) / NB) * NB * NB; }
 
 hipError_t fill_i32(int* p, int64_t n, int v, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
@@ -540,7 +517,7 @@ hipError_t factor_run(float* H, int64_t n, float damp, const FactorWs& ws, hipSt
   hipLaunchKernelGGL(k_damp_stats, dim3(1), dim3(1024), 0, stream, (const float*)H, n, damp, ws.dead, ws.lam);
   FCHECK(hipGetLastError());
   const bool vec4 = (n % 4) == 0 && (reinterpret_cast<uintptr_t>(H) & 15) == 0 &&
-                    (reinterpret_cast<uintptr_t>(ws.A) & 15) == 0 && (reinterpret_cast<uintptr_t>(ws.Minv) & 15) == 0;
+                    (reinterpret_cast<uintptr_t>(ws.A) & 15) == 0;
   const unsigned gy = (unsigned)(n < 65535 ? n : 65535);
   if (vec4) {
     const unsigned gx = (unsigned)((n / 4 + 255) / 256);
@@ -553,126 +530,70 @@ hipError_t factor_run(float* H, int64_t n, float damp, const FactorWs& ws, hipSt
   }
   FCHECK(hipGetLastError());
   const int64_t nk = (n + NB - 1) / NB;
-  hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, stream, ws.A, n, (int64_t)0, ws.status);
+  hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, stream, (const float*)ws.A, n, (int64_t)0, ws.Lt,
+                     ws.status);
   FCHECK(hipGetLastError());
+  const unsigned grows = (unsigned)((n + 15) / 16);
   for (int64_t k = 0; k < nk; ++k) {
     const int64_t k0 = k * NB;
     const int64_t kb = (n - k0) < NB ? (n - k0) : NB;
-    const int64_t rest = n - k0 - kb;
-    if (rest <= 0) break;
-    // panel: A[k0+kb:, k0:k0+kb] <- A[..] L_kk^-T   (in place, a row per 16 lanes)
-    hipLaunchKernelGGL(k_trsm_rows<false>, dim3((unsigned)((rest + 15) / 16)), dim3(256), 0, stream, ws.A,
-                       ws.Minv, n, k0, k0 + kb, rest);
+    const int64_t c1 = k0 + kb, rest = n - c1;
+    // block column k: the panel below, the inverse above, L_kk^-T on its rows
+    hipLaunchKernelGGL(k_trsm_block, dim3(grows), dim3(256), 0, stream, ws.A, (const float*)(ws.Lt + k * NB * NB), n,
+                       k0, (int)kb);
     FCHECK(hipGetLastError());
-    // trailing lower tiles A22 -= L21 L21^T: first the 128 x 128 diagonal
-    // block of block k+1 alone, then the rest beside that block's factor
+    if (rest <= 0) break;
+    // A[r][j] -= A[r][k0:c1] L[j][k0:c1]^T for every row r and the columns j >= c1
     GemmF32 t{};
-    t.A = ws.A + (k0 + kb) * n + k0;
+    t.A = ws.A + k0;
     t.lda = n;
-    t.B = ws.A + (k0 + kb) * n + k0;
+    t.B = ws.A + c1 * n + k0;
     t.ldb = n;
-    t.b_kmajor = 0;  // B(k, c) = L21[c][k]
-    t.C = ws.A + (k0 + kb) * n + (k0 + kb);
+    t.b_kmajor = 0;  // B(k, j) = L[c1 + j][k0 + k]
+    t.C = ws.A + c1;
     t.ldc = n;
-    t.M = (int)rest;
+    t.M = (int)n;
     t.N = (int)rest;
     t.K = (int)kb;
     t.alpha = -1.0f;
     t.beta = 1;
-    t.tri = 1;
     t.batch = 1;
     {
+      // look-ahead: the diagonal block of block k+1 alone
       GemmF32 d = t;
+      d.A = ws.A + c1 * n + k0;
+      d.C = ws.A + c1 * n + c1;
       d.M = d.N = (int)(rest < NB ? rest : NB);
+      d.tri = 1;
       FCHECK(gemm_f32(d, stream));
     }
-    const int64_t t128 = (rest + 127) / 128;
-    if (t128 * (t128 + 1) / 2 >= 256) {
-      const int64_t tiles = t128 * (t128 + 1) / 2;
-      hipLaunchKernelGGL(k_factor_step<128>, dim3((unsigned)(1 + tiles - 1)), dim3(256), 0, stream, t, 1, ws.A, n,
-                         k0 + kb, ws.status);
+    // the rest beside block k+1's factor, in 128- or 64-tiles, whichever takes
+    // fewer rounds of the CUs (one workgroup per CU, a 128-tile ~3x a 64-tile)
+    const int64_t n128 = (rest + 127) / 128, n64 = (rest + 63) / 64;
+    const int64_t tiles128 = (c1 / 128) * n128 + n128 * (n128 + 1) / 2 - 1;
+    const int64_t tiles64 = (c1 / 64) * n64 + n64 * (n64 + 1) / 2 - (n64 * (n64 + 1) / 2 < 3 ? n64 * (n64 + 1) / 2 : 3);
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess || cus < 2) cus = 256;
+    const int64_t slots = cus - 1;
+    float* Ltn = ws.Lt + (k + 1) * NB * NB;
+    if (((tiles128 + slots - 1) / slots) * 3 <= (tiles64 + slots - 1) / slots) {
+      const int ntri = (int)(n128 * (n128 + 1) / 2);
+      hipLaunchKernelGGL(k_factor_step<128>, dim3((unsigned)(1 + tiles128)), dim3(256), 0, stream, t, 1, ntri,
+                         (int)(c1 / 128), (int)n128, (const float*)ws.A, n, c1, Ltn, ws.status);
     } else {
-      const int64_t t64 = (rest + 63) / 64;
-      const int64_t tiles = t64 * (t64 + 1) / 2;
-      const int64_t skip = tiles < 3 ? tiles : 3;
-      hipLaunchKernelGGL(k_factor_step<64>, dim3((unsigned)(1 + tiles - skip)), dim3(256), 0, stream, t, (int)skip,
-                         ws.A, n, k0 + kb, ws.status);
+      const int ntri = (int)(n64 * (n64 + 1) / 2);
+      const int skip = ntri < 3 ? ntri : 3;
+      hipLaunchKernelGGL(k_factor_step<64>, dim3((unsigned)(1 + tiles64)), dim3(256), 0, stream, t, skip, ntri,
+                         (int)(c1 / 64), (int)n64, (const float*)ws.A, n, c1, Ltn, ws.status);
     }
     FCHECK(hipGetLastError());
   }
-  // inverses of all diagonal blocks at once, into Minv's diagonal blocks
-  hipLaunchKernelGGL(k_trsm_rows<true>, dim3(NB / 16, (unsigned)nk), dim3(256), 0, stream, ws.A, ws.Minv, n,
-                     (int64_t)0, (int64_t)0, (int64_t)0);
-  FCHECK(hipGetLastError());
-  // triangular inverse by doubling over the 128-blocks already inverted in Minv
-  for (int64_t s = NB; s < n; s *= 2) {
-    const int64_t pairs_full = n / (2 * s);
-    const int64_t a_last = pairs_full * 2 * s;  // start of a ragged pair, if any
-    const int64_t s2_last = n - a_last - s;      // bottom size of that pair (<= 0: none)
-    for (int pass = 0; pass < 2; ++pass) {
-      const int64_t cnt = pass == 0 ? pairs_full : (s2_last > 0 ? 1 : 0);
-      if (cnt == 0) continue;
-      const int64_t a = pass == 0 ? 0 : a_last;
-      const int64_t s2 = pass == 0 ? s : s2_last;
-      // T = L21 * P      (s2 x s) = (s2 x s)(s x s), P lower
-      GemmF32 g1{};
-      g1.A = ws.A + (a + s) * n + a;
-      g1.lda = n;
-      g1.sA = 2 * s * n + 2 * s;
-      g1.B = ws.Minv + a * n + a;
-      g1.ldb = n;
-      g1.sB = 2 * s * n + 2 * s;
-      g1.b_kmajor = 1;
-      g1.C = ws.T;
-      g1.ldc = s;
-      g1.sC = 0;
-      g1.M = (int)s2;
-      g1.N = (int)s;
-      g1.K = (int)s;
-      g1.alpha = 1.0f;
-      g1.beta = 0;
-      g1.klo_n = 1;
-      g1.batch = 1;
-      // M21 = -Q * T     (s2 x s) = (s2 x s2)(s2 x s), Q lower
-      GemmF32 g2{};
-      g2.A = ws.Minv + (a + s) * n + (a + s);
-      g2.lda = n;
-      g2.sA = 2 * s * n + 2 * s;
-      g2.B = ws.T;
-      g2.ldb = s;
-      g2.sB = 0;
-      g2.b_kmajor = 1;
-      g2.C = ws.Minv + (a + s) * n + a;
-      g2.ldc = n;
-      g2.sC = 2 * s * n + 2 * s;
-      g2.M = (int)s2;
-      g2.N = (int)s;
-      g2.K = (int)s2;
-      g2.alpha = -1.0f;
-      g2.beta = 0;
-      g2.khi_m = 1;
-      g2.batch = 1;
-      // each pair m has its own s x s slice of T
-      g1.C = ws.T + (pass == 0 ? 0 : pairs_full * s * s);
-      g1.sC = s * s;
-      g2.B = g1.C;
-      g2.sB = s * s;
-      g1.batch = (int)cnt;
-      g2.batch = (int)cnt;
-      FCHECK(gemm_f32(g1, stream));
-      FCHECK(gemm_f32(g2, stream));
-    }
-  }
-  if (vec4) {
-    const unsigned gx = (unsigned)((n / 4 + 255) / 256);
-    hipLaunchKernelGGL(k_write_factor4, dim3(gx, gy), dim3(256), 0, stream, (const float*)ws.Minv, n,
+  {
+    const unsigned nt = (unsigned)((n + 63) / 64);
+    hipLaunchKernelGGL(k_write_factor, dim3(nt, nt), dim3(256), 0, stream, (const float*)ws.A, n,
                        (const uint8_t*)ws.dead, H);
-  } else {
-    const unsigned gx = (unsigned)((n + 255) / 256 < 16 ? (n + 255) / 256 : 16);
-    hipLaunchKernelGGL(k_write_factor, dim3(gx, gy), dim3(256), 0, stream, (const float*)ws.Minv, n,
-                       (const uint8_t*)ws.dead, H);
+    FCHECK(hipGetLastError());
   }
-  FCHECK(hipGetLastError());
   return hipSuccess;
 }
 
