@@ -202,9 +202,9 @@ __device__ __forceinline__ void potrf_update(float (*As)[LP], int wave, int lane
     }
   }
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+  for (int kk = 0; kk < PB / 4; ++kk)
 #pragma unroll
-    for (int kk = 0; kk < PB / 4; ++kk)
+    for (int u = 0; u < U; ++u)
       acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(-av[u][kk], bv[u][kk], acc[u], 0, 0, 0);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -297,33 +297,33 @@ __global__ __launch_bounds__(256) void k_potrf_diag(const float* A, int64_t n, i
 // inverse, upper triangle), and A[r][j] the running sums that the solve of
 // block column j finishes.  Block k+1's diagonal block has been updated by a
 // small launch before this one; workgroup 0 factors it while the other
-// workgroups take the tiles: the lower tiles of the trailing matrix first
-// (the first `skip` cover that diagonal block and are left out), then the
-// rectangle above c1 (`rrows` tile rows of `nt` tiles), row-major.
+// workgroups take the 128-tiles: the lower tiles of the trailing matrix but
+// its first (that diagonal block), then the rectangle above c1 (`rrows` tile
+// rows of `nt` tiles), row-major.  (64-tiles, which fill the CUs more evenly
+// when the tiles are few, measured slower here: with K = 128 a tile is mostly
+// its fixed costs.)
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // More than half of the CU's LDS per workgroup: one workgroup per CU, so the
 // diagonal factor never shares its CU with a tile (sharing one made the factor
 // up to 1.9x slower; the tiles lose less than that gains).
-template <int TM>
-__global__ __launch_bounds__(256) void k_factor_step(GemmF32 g, int skip, int ntri, int rrows, int nt, const float* A,
+__global__ __launch_bounds__(256) void k_factor_step(GemmF32 g, int ntri, int rrows, int nt, const float* A,
                                                      int64_t n, int64_t k0n, float* Lt, int* status) {
-  __shared__ __attribute__((aligned(16))) char
-      lds[cmax(96 * 1024, cmax(POTRF_LDS, cmax(gemm_tile_lds<128>(), gemm_tile_lds<TM>())))];
+  __shared__ __attribute__((aligned(16))) char lds[cmax(96 * 1024, cmax(POTRF_LDS, gemm_tile_lds<128>()))];
   if (blockIdx.x == 0) {
     potrf_diag(A, n, k0n, Lt, status, lds);
     return;
   }
   const int u = (int)blockIdx.x - 1;
-  if (u < ntri - skip) {
-    const int t = u + skip;
+  if (u < ntri - 1) {
+    const int t = u + 1;
     int r = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
     while ((r + 1) * (r + 2) / 2 <= t) ++r;
     while (r * (r + 1) / 2 > t) --r;
-    gemm_tile<TM, false>(g, rrows + r, t - r * (r + 1) / 2, 0, lds);
+    gemm_tile<128, false>(g, rrows + r, t - r * (r + 1) / 2, 0, lds);
   } else {
-    const int v = u - (ntri - skip);
-    gemm_tile<TM, false>(g, v / nt, v % nt, 0, lds);
+    const int v = u - (ntri - 1);
+    gemm_tile<128, false>(g, v / nt, v % nt, 0, lds);
   }
 }
 
@@ -567,25 +567,11 @@ hipError_t factor_run(float* H, int64_t n, float damp, const FactorWs& ws, hipSt
       d.tri = 1;
       FCHECK(gemm_f32(d, stream));
     }
-    // the rest beside block k+1's factor, in 128- or 64-tiles, whichever takes
-    // fewer rounds of the CUs (one workgroup per CU, a 128-tile ~3x a 64-tile)
-    const int64_t n128 = (rest + 127) / 128, n64 = (rest + 63) / 64;
-    const int64_t tiles128 = (c1 / 128) * n128 + n128 * (n128 + 1) / 2 - 1;
-    const int64_t tiles64 = (c1 / 64) * n64 + n64 * (n64 + 1) / 2 - (n64 * (n64 + 1) / 2 < 3 ? n64 * (n64 + 1) / 2 : 3);
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, 0) != hipSuccess || cus < 2) cus = 256;
-    const int64_t slots = cus - 1;
-    float* Ltn = ws.Lt + (k + 1) * NB * NB;
-    if (((tiles128 + slots - 1) / slots) * 3 <= (tiles64 + slots - 1) / slots) {
-      const int ntri = (int)(n128 * (n128 + 1) / 2);
-      hipLaunchKernelGGL(k_factor_step<128>, dim3((unsigned)(1 + tiles128)), dim3(256), 0, stream, t, 1, ntri,
-                         (int)(c1 / 128), (int)n128, (const float*)ws.A, n, c1, Ltn, ws.status);
-    } else {
-      const int ntri = (int)(n64 * (n64 + 1) / 2);
-      const int skip = ntri < 3 ? ntri : 3;
-      hipLaunchKernelGGL(k_factor_step<64>, dim3((unsigned)(1 + tiles64)), dim3(256), 0, stream, t, skip, ntri,
-                         (int)(c1 / 64), (int)n64, (const float*)ws.A, n, c1, Ltn, ws.status);
-    }
+    // the rest beside block k+1's factor
+    const int64_t nt = (rest + 127) / 128, ntri = nt * (nt + 1) / 2, rrows = c1 / 128;
+    hipLaunchKernelGGL(k_factor_step, dim3((unsigned)(1 + rrows * nt + ntri - 1)), dim3(256), 0, stream, t,
+                       (int)ntri, (int)rrows, (int)nt, (const float*)ws.A, n, c1, ws.Lt + (k + 1) * NB * NB,
+                       ws.status);
     FCHECK(hipGetLastError());
   }
   {
