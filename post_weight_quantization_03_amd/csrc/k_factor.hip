@@ -327,6 +327,70 @@ __global__ __launch_bounds__(256) void k_factor_step(GemmF32 g, int ntri, int rr
   }
 }
 
+// Look-ahead update of block k+1's diagonal block, D -= P P^T, with P =
+// A[c1:c1+kb1, k0:k0+128] (that block's rows of the panel just solved) and D =
+// A[c1:c1+kb1, c1:c1+kb1]: lower 32 x 32 tiles, the diagonal tiles whole.  One
+// workgroup per tile; its four waves split K = 128 in quarters of 16
+// v_mfma_f32_32x32x2_f32 steps, lane half h of step s taking k = 32w + 16h + s
+// (the order of k is free), so a lane's operands are four contiguous float4
+// of each row, all in flight at once with the workgroup's elements of D.  The
+// quarters are summed through LDS in a fixed order.  On the factor's critical
+// path, so it is built for latency.
+__global__ __launch_bounds__(256) void k_diag_update(float* A, int64_t n, int64_t k0, int64_t c1, int kb1) {
+  __shared__ float part[4][32 * 32];
+  const int t = blockIdx.x;
+  int ti = 0;
+  while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+  const int tj = t - ti * (ti + 1) / 2;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, j = lane & 31;
+  const int ra = 32 * ti + j, rb = 32 * tj + j;
+  const int kq = 32 * w + 16 * h;
+  const bool vec = (n & 3) == 0 && (k0 & 3) == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
+  float a[16], b[16];
+  if (vec) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 va = ra < kb1 ? *reinterpret_cast<const float4*>(A + (c1 + ra) * n + k0 + kq + 4 * q)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 vb = rb < kb1 ? *reinterpret_cast<const float4*>(A + (c1 + rb) * n + k0 + kq + 4 * q)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+      a[4 * q + 0] = va.x; a[4 * q + 1] = va.y; a[4 * q + 2] = va.z; a[4 * q + 3] = va.w;
+      b[4 * q + 0] = vb.x; b[4 * q + 1] = vb.y; b[4 * q + 2] = vb.z; b[4 * q + 3] = vb.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      a[e] = ra < kb1 ? A[(c1 + ra) * n + k0 + kq + e] : 0.0f;
+      b[e] = rb < kb1 ? A[(c1 + rb) * n + k0 + kq + e] : 0.0f;
+    }
+  }
+  // this thread's four elements of D, read now so that their latency hides too
+  float dv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid + 256 * q, gi = 32 * ti + (e >> 5), gj = 32 * tj + (e & 31);
+    dv[q] = (gi < kb1 && gj < kb1) ? A[(c1 + gi) * n + c1 + gj] : 0.0f;
+  }
+  // two accumulators (even and odd steps), added at the end
+  f32x16 acc0, acc1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; e += 2) {
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e + 1], b[e + 1], acc1, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) part[w][acc_row(r, lane) * 32 + j] = acc0[r] + acc1[r];
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid + 256 * q, gi = 32 * ti + (e >> 5), gj = 32 * tj + (e & 31);
+    const float sum = ((part[0][e] + part[1][e]) + part[2][e]) + part[3][e];
+    if (gi < kb1 && gj < kb1) A[(c1 + gi) * n + c1 + gj] = dv[q] - sum;
+  }
+}
+
 // ------------------------------------------------------------------ triangular solves
 
 // Rows y = b L^-T for block k's L, i.e. L y^T = b^T by forward substitution,
@@ -560,12 +624,10 @@ hipError_t factor_run(float* H, int64_t n, float damp, const FactorWs& ws, hipSt
     t.batch = 1;
     {
       // look-ahead: the diagonal block of block k+1 alone
-      GemmF32 d = t;
-      d.A = ws.A + c1 * n + k0;
-      d.C = ws.A + c1 * n + c1;
-      d.M = d.N = (int)(rest < NB ? rest : NB);
-      d.tri = 1;
-      FCHECK(gemm_f32(d, stream));
+      const int kb1 = (int)(rest < NB ? rest : NB), t32 = (kb1 + 31) / 32;
+      hipLaunchKernelGGL(k_diag_update, dim3((unsigned)(t32 * (t32 + 1) / 2)), dim3(256), 0, stream, ws.A, n, k0, c1,
+                         kb1);
+      FCHECK(hipGetLastError());
     }
     // the rest beside block k+1's factor
     const int64_t nt = (rest + 127) / 128, ntri = nt * (nt + 1) / 2, rrows = c1 / 128;
