@@ -40,7 +40,7 @@ QuantLayout layout(int64_t rows, int64_t cols, const gptq_params* p) {
   L.dead = take((size_t)cols);
   L.loss = take((size_t)rows * sizeof(float));
   L.Wf = take((size_t)rows * cols * sizeof(float));
-  L.E = take((size_t)rows * 128 * sizeof(float) * 2);  // this block's errors and the previous block's
+  L.E = take((size_t)rows * ((cols + 127) / 128) * 128 * sizeof(float));  // every block's errors
   {
     const size_t ub = quant_split_bytes(cols, p->groupsize == -1 ? cols : p->groupsize);
     L.Us = ub ? take(ub) : 0;

@@ -28,6 +28,7 @@ namespace gptq {
 namespace {
 
 constexpr int B = 128;
+constexpr int64_t LAZY = 4;  // blocks per group of the trailing update's second level
 
 enum GroupMode { GM_BIG = 0, GM_32 = 1, GM_64 = 2 };
 
@@ -94,8 +95,9 @@ struct BlockArgs {
   uint8_t* zeros;
   float* w_hat;
   float* row_loss;
-  float* E;            // this block's scaled errors [rows, 128]
+  float* E;            // this block's scaled errors: E[r * ldE + j], j < 128
   const float* Eprev;  // the previous block's, when its update of this block is applied here (else null)
+  int64_t ldE;
 };
 
 // U's upper triangle -> three bf16 planes (the split GEMM's B operand), eight
@@ -305,7 +307,7 @@ __device__ __forceinline__ void quant_block_wg(const BlockArgs& a, int64_t wg, c
     if (er < a.rows) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(a.Eprev + er * B + 32 * g + 4 * q);
+        const float4 v = *reinterpret_cast<const float4*>(a.Eprev + er * a.ldE + 32 * g + 4 * q);
         ea[4 * q + 0] = v.x; ea[4 * q + 1] = v.y; ea[4 * q + 2] = v.z; ea[4 * q + 3] = v.w;
       }
     } else {
@@ -461,39 +463,51 @@ __device__ __forceinline__ void quant_block_wg(const BlockArgs& a, int64_t wg, c
     for (int i = 0; i < 8; ++i)
       if (8 * L.t + i < a.bw) hp[i] = wh[i];
   }
-  float* ep = a.E + row * B + 8 * L.t;
+  float* ep = a.E + row * a.ldE + 8 * L.t;
   *reinterpret_cast<float4*>(ep) = make_float4(e[0], e[1], e[2], e[3]);
   *reinterpret_cast<float4*>(ep + 4) = make_float4(e[4], e[5], e[6], e[7]);
 }
 
 // One launch per 128-column block b: the column loop of block b (workgroups
 // 0 .. nq-1, each applying the previous block's update of its own columns
-// first) and, beside it, the rest of the previous block's trailing update,
-// W[:, c0+128:] -= E_{b-1} U[c0-128:c0, c0+128:], as GEMM tiles (workgroups
-// nq ..).  The two touch disjoint columns; a loop workgroup (latency bound)
-// and a GEMM tile fit on one CU together, so the GEMM fills the loop's idle
-// issue slots.  The tiles run the split-bf16 GEMM (sgemm_tile.h).
+// first) and, beside it, up to two jobs of the trailing update as split-bf16
+// GEMM tiles (sgemm_tile.h, workgroups nq ..).  All of them touch columns past
+// block b and read errors of blocks before b, so nothing in one launch
+// depends on another part of it; a loop workgroup (latency bound) and a GEMM
+// tile fit on one CU together, so the GEMM fills the loop's idle issue slots.
+struct FarJobs {
+  SplitGemm g[2];
+  int tn[2];      // tile columns of each job
+  int start[3];   // first tile of each job; start[2] = all tiles
+};
+
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void k_quant_fused(BlockArgs a, SplitGemm far, int64_t nq, int far_tn) {
+__global__ __launch_bounds__(256, 2) void k_quant_fused(BlockArgs a, FarJobs far, int64_t nq) {
   constexpr int LDS = QUANT_LDS > SGEMM_LDS ? QUANT_LDS : SGEMM_LDS;
   __shared__ __attribute__((aligned(16))) char lds[LDS];
   if ((int64_t)blockIdx.x < nq) {
     quant_block_wg<MODE>(a, blockIdx.x, lds);
   } else {
     const int t = (int)(blockIdx.x - nq);
-    sgemm_tile(far, t / far_tn, t % far_tn, lds);
+    const int j = t < far.start[1] ? 0 : 1;
+    const int u = t - far.start[j];
+    sgemm_tile(far.g[j], u / far.tn[j], u % far.tn[j], lds);
   }
 }
 
 template <int MODE>
-hipError_t launch_block(const BlockArgs& a, const SplitGemm& far, int64_t nq, hipStream_t stream) {
-  int tn = 1;
+hipError_t launch_block(const BlockArgs& a, FarJobs far, int64_t nq, hipStream_t stream) {
   int64_t tiles = 0;
-  if (far.M > 0 && far.N > 0) {
-    tn = (far.N + STM - 1) / STM;
-    tiles = (int64_t)((far.M + STM - 1) / STM) * tn;
+  for (int j = 0; j < 2; ++j) {
+    far.start[j] = (int)tiles;
+    far.tn[j] = 1;
+    if (far.g[j].M > 0 && far.g[j].N > 0 && far.g[j].K > 0) {
+      far.tn[j] = (far.g[j].N + STM - 1) / STM;
+      tiles += (int64_t)((far.g[j].M + STM - 1) / STM) * far.tn[j];
+    }
   }
-  hipLaunchKernelGGL((k_quant_fused<MODE>), dim3((unsigned)(nq + tiles)), dim3(256), 0, stream, a, far, nq, tn);
+  far.start[2] = (int)tiles;
+  hipLaunchKernelGGL((k_quant_fused<MODE>), dim3((unsigned)(nq + tiles)), dim3(256), 0, stream, a, far, nq);
   return hipGetLastError();
 }
 
@@ -543,7 +557,9 @@ hipError_t quant_run(const QuantArgs& q, hipStream_t stream) {
   // when no group range reaches past the block being quantized: groups inside
   // a block, or one group per row (its range is taken before any update).
   const bool overlap = q.groupsize <= B || q.groupsize >= cols;
-  float* Ebuf[2] = {q.E, q.E + rows * B};
+  // errors of every block, kept for the whole layer: E_b = E[:, 128 b : 128 b + 128]
+  const int64_t nb = (cols + B - 1) / B, ldE = nb * B;
+  a.ldE = ldE;
   if (overlap && cols > 2 * B) {
     if (!q.Usplit) return hipErrorInvalidValue;
     const unsigned gy = (unsigned)(cols < 65535 ? cols : 65535);
@@ -562,19 +578,34 @@ hipError_t quant_run(const QuantArgs& q, hipStream_t stream) {
   for (int64_t c0 = 0; c0 < cols; c0 += B, ++b) {
     a.c0 = c0;
     a.bw = (int)((cols - c0) < B ? (cols - c0) : B);
-    a.E = Ebuf[b & 1];
-    a.Eprev = (overlap && b > 0) ? Ebuf[(b - 1) & 1] : nullptr;
-    SplitGemm far{};
-    if (overlap && b > 0 && c0 + B < cols) {
-      far.A = a.Eprev;
-      for (int p = 0; p < 3; ++p) far.B[p] = q.Usplit + (int64_t)p * cols * cols + (c0 - B) * cols + (c0 + B);
-      far.C = q.Wf + c0 + B;
-      far.lda = B;
-      far.ldb = cols;
-      far.ldc = cols;
-      far.M = (int)rows;
-      far.N = (int)(cols - c0 - B);
-      far.K = B;
+    a.E = q.E + b * B;
+    a.Eprev = (overlap && b > 0) ? q.E + (b - 1) * B : nullptr;
+    // The trailing update in two levels.  The errors of block e reach the
+    // column blocks of its own group of LAZY blocks (groups aligned at
+    // multiples of LAZY) beyond e + 1 right away, K = 128, in launch e + 1;
+    // block e + 1 itself is updated by the loop workgroups of that launch.
+    // Column blocks past the group receive the whole group at once, K =
+    // 128 LAZY, in the launch after the group's last block: W's far columns
+    // are read and written once per group instead of once per block.  Every
+    // pair (block e, column block j >= e + 2) is covered exactly once, before
+    // launch j, and no two jobs of one launch touch the same columns.
+    FarJobs far{};
+    if (overlap && b > 0) {
+      auto job = [&](SplitGemm& g, int64_t e0, int64_t ne, int64_t j0, int64_t j1) {  // blocks [e0, e0+ne) -> [j0, j1]
+        g.A = q.E + e0 * B;
+        for (int p = 0; p < 3; ++p) g.B[p] = q.Usplit + (int64_t)p * cols * cols + (e0 * B) * cols + j0 * B;
+        g.C = q.Wf + j0 * B;
+        g.lda = ldE;
+        g.ldb = cols;
+        g.ldc = cols;
+        g.M = (int)rows;
+        g.N = (int)((j1 + 1) * B < cols ? (j1 + 1 - j0) * B : cols - j0 * B);
+        g.K = (int)(ne * B);
+      };
+      if (b % LAZY == 0 && b + 1 < nb) job(far.g[0], b - LAZY, LAZY, b + 1, nb - 1);
+      const int64_t e = b - 1, gend = (e / LAZY + 1) * LAZY;  // last column block of e's group
+      const int64_t j1 = gend < nb - 1 ? gend : nb - 1;
+      if (e + 2 <= j1) job(far.g[1], e, 1, e + 2, j1);
     }
     hipError_t e;
     if (mode == GM_32)
@@ -588,7 +619,7 @@ hipError_t quant_run(const QuantArgs& q, hipStream_t stream) {
     if (!overlap && c1 < cols) {
       GemmF32 g{};
       g.A = a.E;
-      g.lda = B;
+      g.lda = ldE;
       g.B = q.U + c0 * cols + c1;
       g.ldb = cols;
       g.b_kmajor = 1;
