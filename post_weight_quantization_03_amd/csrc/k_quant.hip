@@ -28,7 +28,7 @@ namespace gptq {
 namespace {
 
 constexpr int B = 128;
-constexpr int64_t LAZY = 4;  // blocks per group of the trailing update's second level
+constexpr int64_t LAZY = 8;  // blocks per group of the trailing update's second level
 
 enum GroupMode { GM_BIG = 0, GM_32 = 1, GM_64 = 2 };
 
