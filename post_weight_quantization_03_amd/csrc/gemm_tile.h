@@ -169,6 +169,64 @@ __device__ __forceinline__ void stage_mfma(const char* buf, int wm, int wn, int 
   }
 }
 
+// x = h1 + h2 + h3 in bf16 terms (both differences exact in fp32); see
+// sgemm_tile.h for why six products of the terms keep fp32 accuracy.
+__device__ __forceinline__ void split3(float x, __bf16& h1, __bf16& h2, __bf16& h3) {
+  h1 = (__bf16)x;
+  const float r1 = x - (float)h1;
+  h2 = (__bf16)r1;
+  const float r2 = r1 - (float)h2;
+  h3 = (__bf16)r2;
+}
+
+// The stage's MFMAs on bf16 matrix cores with both fp32 operands split three
+// ways in registers (A m-major, B n-major, the same LDS layout): lane half h
+// supplies k = 8h .. 8h+7 of its row and column to v_mfma_f32_32x32x16_bf16,
+// exactly the 8 values of its two 16-byte reads; six products per block
+// pair, the small ones first.
+template <int TM>
+__device__ __forceinline__ void stage_mfma_split(const char* buf, int wm, int wn, int lane,
+                                                 f32x16 (&acc)[Geo<TM>::NB][Geo<TM>::NB]) {
+  constexpr int NB = Geo<TM>::NB, HALF = Geo<TM>::HALF;
+  const int j = lane & 31, h = lane >> 5;
+  bf16x8 a[NB][3], b[NB][3];
+#pragma unroll
+  for (int o = 0; o < 2; ++o) {
+    const char* S = o == 0 ? buf : buf + Geo<TM>::OPB;
+    const int w0 = o == 0 ? wm : wn;
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int row = w0 * HALF + 32 * q + j;
+      const float4 lo = *reinterpret_cast<const float4*>(S + mm_off(row, 2 * h));
+      const float4 hi = *reinterpret_cast<const float4*>(S + mm_off(row, 2 * h + 1));
+      const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        __bf16 h1, h2, h3;
+        split3(x[e], h1, h2, h3);
+        if (o == 0) {
+          a[q][0][e] = h1; a[q][1][e] = h2; a[q][2][e] = h3;
+        } else {
+          b[q][0][e] = h1; b[q][1][e] = h2; b[q][2][e] = h3;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj) {
+      f32x16 c = acc[bi][bj];
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi][2], b[bj][0], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi][1], b[bj][1], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi][0], b[bj][2], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi][1], b[bj][0], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi][0], b[bj][1], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[bi][0], b[bj][0], c, 0, 0, 0);
+      acc[bi][bj] = c;
+    }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_barrier() {
   if constexpr (N == 0)
@@ -193,13 +251,16 @@ __device__ __forceinline__ void issue_stage(DmaOp<TM>& da, DmaOp<TM>& db, char* 
 
 // stage s: queue s+3 into the buffer stage s-1 used, MFMAs on stage s,
 // retire stage s+2
-template <int TM, bool BKM>
+template <int TM, bool BKM, bool SPLIT>
 __device__ __forceinline__ void pipe_body(int s, int nst, const char* cur, char* nxt3, DmaOp<TM>& da,
                                           DmaOp<TM>& db, int wave, int wm, int wn, int lane,
                                           f32x16 (&acc)[Geo<TM>::NB][Geo<TM>::NB]) {
   const bool more = s + 3 < nst;
   if (more) issue_stage<TM>(da, db, nxt3, wave);
-  stage_mfma<TM, BKM>(cur, wm, wn, lane, acc);
+  if constexpr (SPLIT)
+    stage_mfma_split<TM>(cur, wm, wn, lane, acc);
+  else
+    stage_mfma<TM, BKM>(cur, wm, wn, lane, acc);
   if (more)
     wait_barrier<2 * Geo<TM>::LPW>();
   else
@@ -211,7 +272,7 @@ __device__ __forceinline__ void pipe_body(int s, int nst, const char* cur, char*
 // information: the compiler's wait insertion then only waits for loads into
 // the buffer being read (retired long before by the counted barriers) instead
 // of draining every direct load before each read.
-template <int TM, bool BKM>
+template <int TM, bool BKM, bool SPLIT>
 __device__ __forceinline__ void pipeline(char* __restrict__ S0, char* __restrict__ S1, char* __restrict__ S2,
                                          char* __restrict__ S3, DmaOp<TM>& da, DmaOp<TM>& db, int nst, int wave,
                                          int wm, int wn, int lane, f32x16 (&acc)[Geo<TM>::NB][Geo<TM>::NB]) {
@@ -231,13 +292,13 @@ __device__ __forceinline__ void pipeline(char* __restrict__ S0, char* __restrict
   else
     wait_barrier<0>();
   for (int s = 0; s < nst; s += 4) {
-    pipe_body<TM, BKM>(s, nst, S0, S3, da, db, wave, wm, wn, lane, acc);
+    pipe_body<TM, BKM, SPLIT>(s, nst, S0, S3, da, db, wave, wm, wn, lane, acc);
     if (s + 1 >= nst) break;
-    pipe_body<TM, BKM>(s + 1, nst, S1, S0, da, db, wave, wm, wn, lane, acc);
+    pipe_body<TM, BKM, SPLIT>(s + 1, nst, S1, S0, da, db, wave, wm, wn, lane, acc);
     if (s + 2 >= nst) break;
-    pipe_body<TM, BKM>(s + 2, nst, S2, S1, da, db, wave, wm, wn, lane, acc);
+    pipe_body<TM, BKM, SPLIT>(s + 2, nst, S2, S1, da, db, wave, wm, wn, lane, acc);
     if (s + 3 >= nst) break;
-    pipe_body<TM, BKM>(s + 3, nst, S3, S2, da, db, wave, wm, wn, lane, acc);
+    pipe_body<TM, BKM, SPLIT>(s + 3, nst, S3, S2, da, db, wave, wm, wn, lane, acc);
   }
 }
 
@@ -260,8 +321,11 @@ __device__ __forceinline__ int gemm_crow(int m0, int wm, int lane, int bi, int r
 
 // One TM x TM tile (tm, tn) of batch entry z; lds holds gemm_tile_lds<TM>()
 // bytes (16-byte aligned).  All 256 threads of the workgroup take part.
-template <int TM, bool BKM>
+// SPLIT (m-major A and n-major B only): the MFMAs run on bf16 matrix cores
+// with both operands split three ways (fp32 accuracy, stage_mfma_split).
+template <int TM, bool BKM, bool SPLIT = false>
 __device__ __forceinline__ void gemm_tile(const GemmF32& g, int tm, int tn, int z, char* lds) {
+  static_assert(!SPLIT || !BKM, "split operands need an n-major B");
   using G = Geo<TM>;
   constexpr int NB = G::NB, HALF = G::HALF;
   char* S0 = lds;
@@ -311,7 +375,7 @@ __device__ __forceinline__ void gemm_tile(const GemmF32& g, int tm, int tn, int 
     }
     DmaOp<TM> da = dma_mmajor<TM>(A, g.lda, m0, kbeg, wave, lane);
     DmaOp<TM> db = BKM ? dma_kmajor<TM>(B, g.ldb, kbeg, n0, wave, lane) : dma_mmajor<TM>(B, g.ldb, n0, kbeg, wave, lane);
-    pipeline<TM, BKM>(S0, S1, S2, S3, da, db, nst, wave, wm, wn, lane, acc);
+    pipeline<TM, BKM, SPLIT>(S0, S1, S2, S3, da, db, nst, wave, wm, wn, lane, acc);
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
@@ -342,7 +406,10 @@ __device__ __forceinline__ void gemm_tile(const GemmF32& g, int tm, int tn, int 
       else
         guarded_mmajor<TM>(B, g.ldb, n0, g.N, k0, kend, S0 + G::OPB);
       __syncthreads();
-      stage_mfma<TM, BKM>(S0, wm, wn, lane, acc);
+      if constexpr (SPLIT)
+        stage_mfma_split<TM>(S0, wm, wn, lane, acc);
+      else
+        stage_mfma<TM, BKM>(S0, wm, wn, lane, acc);
     }
   }
 

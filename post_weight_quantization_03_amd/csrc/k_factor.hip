@@ -299,9 +299,10 @@ __global__ __launch_bounds__(256) void k_potrf_diag(const float* A, int64_t n, i
 // small launch before this one; workgroup 0 factors it while the other
 // workgroups take the 128-tiles: the lower tiles of the trailing matrix but
 // its first (that diagonal block), then the rectangle above c1 (`rrows` tile
-// rows of `nt` tiles), row-major.  (64-tiles, which fill the CUs more evenly
-// when the tiles are few, measured slower here: with K = 128 a tile is mostly
-// its fixed costs.)
+// rows of `nt` tiles), row-major.  The tiles run on bf16 matrix cores with
+// both operands split three ways in registers (gemm_tile.h, fp32 accuracy).
+// (64-tiles, which fill the CUs more evenly when the tiles are few, measured
+// slower here: with K = 128 a tile is mostly its fixed costs.)
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // More than half of the CU's LDS per workgroup: one workgroup per CU, so the
@@ -320,10 +321,10 @@ __global__ __launch_bounds__(256) void k_factor_step(GemmF32 g, int ntri, int rr
     int r = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
     while ((r + 1) * (r + 2) / 2 <= t) ++r;
     while (r * (r + 1) / 2 > t) --r;
-    gemm_tile<128, false>(g, rrows + r, t - r * (r + 1) / 2, 0, lds);
+    gemm_tile<128, false, true>(g, rrows + r, t - r * (r + 1) / 2, 0, lds);
   } else {
     const int v = u - (ntri - 1);
-    gemm_tile<128, false>(g, v / nt, v % nt, 0, lds);
+    gemm_tile<128, false, true>(g, v / nt, v % nt, 0, lds);
   }
 }
 

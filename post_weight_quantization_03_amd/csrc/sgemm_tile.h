@@ -77,13 +77,6 @@ __device__ __forceinline__ bf16x8 sb_frag(const char* p) {
 }
 
 // fp32 -> three bf16 terms (round to nearest even each time).
-__device__ __forceinline__ void split3(float x, __bf16& h1, __bf16& h2, __bf16& h3) {
-  h1 = (__bf16)x;
-  const float r1 = x - (float)h1;
-  h2 = (__bf16)r1;
-  const float r2 = r1 - (float)h2;
-  h3 = (__bf16)r2;
-}
 
 // Direct loads of one stage (5 a wave).  A: 1 KB = 16 rows of 64 bytes
 // (the fp32 GEMM's dma_mmajor offsets); B: 1 KB = 4 k rows of one plane.
