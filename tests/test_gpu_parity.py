@@ -156,7 +156,10 @@ def test_quantize_linear256():
 
 @pytest.mark.parametrize("rows,cols,bits,g", [
     (37, 300, 4, 128), (37, 300, 3, -1), (64, 384, 2, 128), (16, 640, 4, 256),
-    (33, 256, 8, -1), (48, 320, 3, 64), (40, 256, 4, 32), (5, 130, 4, 128)])
+    (33, 256, 8, -1), (48, 320, 3, 64), (40, 256, 4, 32), (5, 130, 4, 128),
+    # several 128-blocks past a group of 8 (the trailing update's second level and
+    # the factor's folded inverse over many steps), ragged tails
+    (8, 1040, 2, 128), (24, 1300, 4, 128), (16, 2176, 4, 128)])
 def test_quantize_ragged_and_groups(rows, cols, bits, g):
     _lib_loaded()
     say(f"quantize rows={rows} cols={cols} bits={bits} g={g}")
