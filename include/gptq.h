@@ -111,6 +111,9 @@ int gptq_accumulate_hessian(float* H, int64_t n, const void* X, gptq_dtype x_dty
  * d_status: if non-NULL, a device int32 that receives the final status
  *   (GPTQ_OK or GPTQ_ENOTPD) and the call is fully asynchronous; if NULL the
  *   call synchronizes `stream` once at the end and returns that status.
+ *   With GPTQ_ENOTPD the outputs and H hold unspecified values (they may
+ *   be non-finite).  Argument errors (GPTQ_EINVAL, GPTQ_EWORKSPACE,
+ *   GPTQ_EUNSUPPORTED) are returned before any work and leave them untouched.
  * W, X and the outputs must not alias each other, H or the workspace.
  * rows == 0 or cols == 0: no work, GPTQ_OK.
  * ------------------------------------------------------------------------- */
