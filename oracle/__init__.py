@@ -13,6 +13,7 @@ Modules
               reached through a different route (trailing principal inverses
               instead of a Cholesky factor).
   pack_ref    LSB-first per-row bitstream packing and unpacking.
+  gemv_ref    dequantization of packed codes and the product y = W^ x.
 
 Parity pins: every function here is checked in ``tests/test_oracle_*.py``
 against closed forms, the hand-worked 4x8 example in ``tests/golden``,
@@ -34,3 +35,4 @@ from .gptq_ref import (  # noqa: F401
     rtn_ref,
 )
 from .pack_ref import pack_ref, unpack_ref  # noqa: F401
+from .gemv_ref import dequant_gemv_ref, dequant_ref  # noqa: F401
