@@ -134,6 +134,29 @@ int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t rows, int64_t
 int gptq_pack(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits, uint32_t* packed,
               gptq_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Dequantizing matrix-vector product y = W^ x over the quantizer's outputs, with
+ * w^[r, j] = scales[r, j / g] * (code[r, j] - zeros[r, j / g]) (g = cols when
+ * groupsize == -1): the packed codes as written by gptq_pack, and the scales
+ * and zeros as written by gptq_quantize_layer.  This is the inference side of
+ * the grid the OneComp hub article's quantizer table describes, as the
+ * OneComp release post's vLLM plugins consume it.
+ *   packed  uint32 [rows, cols*bits/32]   gptq_pack layout, dword aligned
+ *   scales  float  [rows, G]              G = ceil(cols / g)
+ *   zeros   uint8  [rows, G]
+ *   x       float  [cols]
+ *   y       float  [rows]                 written, not accumulated into
+ * Accumulation is fp32 in a fixed order (bit-reproducible run to run).
+ * bits in {2, 3, 4, 8}; (cols * bits) % 32 == 0; groupsize -1 or a positive
+ * multiple of 32 (else GPTQ_EUNSUPPORTED).  Pointers must be 4-byte aligned.
+ * rows == 0: no work.  cols == 0: y := 0 (the input pointers may then be
+ * NULL).  Argument errors return before any
+ * launch.  y must not alias the inputs.
+ * ------------------------------------------------------------------------- */
+int gptq_dequant_gemv(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
+                      int64_t cols, int32_t bits, int32_t groupsize, const float* x, float* y,
+                      gptq_stream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* gptq_status_string(int status);
 

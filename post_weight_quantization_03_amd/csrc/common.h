@@ -102,6 +102,11 @@ hipError_t quant_run(const QuantArgs& a, hipStream_t stream);
 hipError_t pack_launch(const uint8_t* codes, int64_t rows, int64_t cols, int bits, uint32_t* packed,
                        hipStream_t stream);
 
+// Dequantizing GEMV y = W^ x over packed codes (k_gemv.hip).
+bool dequant_gemv_supported(int64_t cols, int32_t bits, int32_t groupsize);
+hipError_t dequant_gemv(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
+                        int64_t cols, int32_t bits, int32_t groupsize, const float* x, float* y, hipStream_t stream);
+
 // Small utility kernels (k_factor.hip).
 hipError_t fill_i32(int* p, int64_t n, int v, hipStream_t stream);
 hipError_t copy_status(const int* src, int32_t* dst, hipStream_t stream);

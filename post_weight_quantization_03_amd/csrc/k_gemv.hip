@@ -1,0 +1,278 @@
+// y = W^ x straight from the quantizer's outputs: the packed codes (per row a
+// little-endian bitstream of b-bit codes, code i at stream bits [i b, (i+1) b)),
+// the fp32 group scales and the integer group zeros, w^ = s_g (q - z_g).
+//
+// HBM-bound: a row costs cols b / 8 bytes of codes plus its G scales and zeros,
+// and x is shared by every row.  The unit of work is a run of 32 codes, which
+// is b whole words and lies in one group (groups are multiples of 32 columns).
+// A workgroup stages x through LDS, a chunk at a time, read once from memory in
+// whole coalesced vectors.  A wave owns R rows and one of S column slices; its
+// lane l takes the runs l, l + 64, ... of the slice (so a wave's loads from a
+// row are contiguous), reads the run's 32 x values from LDS once and applies
+// them to its R rows:
+//   y_r += s_g (sum_i q_i x_i - z_g sum_i x_i).
+// Lanes meet in a butterfly over the wave, slices in LDS.  Accumulation is
+// fp32 in a fixed order, so results are reproducible.
+#include "common.h"
+
+namespace gptq {
+namespace {
+
+// dword-aligned vector loads (global loads of several dwords need only dword
+// alignment, so rows whose word count is not a multiple of 4 still load whole)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2), aligned(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4), aligned(4)));
+
+template <int BITS>
+__device__ __forceinline__ void load_run(const uint32_t* p, uint32_t (&w)[BITS]) {
+  if constexpr (BITS == 2) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else if constexpr (BITS == 3) {
+    w[0] = p[0]; w[1] = p[1]; w[2] = p[2];
+  } else {
+#pragma unroll
+    for (int j = 0; j < BITS; j += 4) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p + j);
+      w[j] = v.x; w[j + 1] = v.y; w[j + 2] = v.z; w[j + 3] = v.w;
+    }
+  }
+}
+
+__device__ __forceinline__ float byte_f(uint32_t v, int b) { return (float)((v >> (8 * b)) & 0xffu); }
+
+// Codes narrower than 5 bits convert two at a time: a byte holding q < 16 read
+// as an fp8 e4m3 value is a subnormal or the smallest binade, exactly q times a
+// power of two (q m / 8 2^(1 - bias) either way), so one pair conversion gives
+// two codes up to that factor.  code_unit() is the factor's inverse, exact.
+__device__ __forceinline__ float code_unit() { return 1.0f / __builtin_amdgcn_cvt_f32_fp8(1, 0); }
+
+// sum_i q_i x_i over one run: for 2 and 4 bits scaled by 1 / code_unit(), else
+// exact codes.  One mask isolates four codes in the four bytes of a word.
+template <int BITS>
+__device__ __forceinline__ float run_dot(const uint32_t (&w)[BITS], const float (&x)[32]) {
+  float acc = 0.0f;
+  if constexpr (BITS == 8) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc = fmaf(byte_f(w[j], b), x[4 * j + b], acc);
+  } else if constexpr (BITS == 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = w[j] & 0x0f0f0f0fu, hi = (w[j] >> 4) & 0x0f0f0f0fu;
+      // byte b of lo holds code 8j + 2b, of hi code 8j + 2b + 1
+      const auto l01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+      const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+      const auto l23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+      const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+      acc = fmaf(l01[0], x[8 * j + 0], acc);
+      acc = fmaf(h01[0], x[8 * j + 1], acc);
+      acc = fmaf(l01[1], x[8 * j + 2], acc);
+      acc = fmaf(h01[1], x[8 * j + 3], acc);
+      acc = fmaf(l23[0], x[8 * j + 4], acc);
+      acc = fmaf(h23[0], x[8 * j + 5], acc);
+      acc = fmaf(l23[1], x[8 * j + 6], acc);
+      acc = fmaf(h23[1], x[8 * j + 7], acc);
+    }
+  } else if constexpr (BITS == 2) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        // byte b of c holds code 16j + 4b + s
+        const uint32_t c = (w[j] >> (2 * s)) & 0x03030303u;
+        const auto c01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);
+        const auto c23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, true);
+        acc = fmaf(c01[0], x[16 * j + s], acc);
+        acc = fmaf(c01[1], x[16 * j + 4 + s], acc);
+        acc = fmaf(c23[0], x[16 * j + 8 + s], acc);
+        acc = fmaf(c23[1], x[16 * j + 12 + s], acc);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int bit = 3 * i, wi = bit >> 5, sh = bit & 31;
+      const uint32_t v = sh + 3 > 32 ? __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) : w[wi] >> sh;
+      acc = fmaf((float)(v & 7u), x[i], acc);
+    }
+  }
+  return acc;
+}
+
+// x goes through LDS in chunks of XCH runs, each run's 32 values in a row of XP
+// floats: the padding puts the rows of eight consecutive runs on different
+// banks, so the lanes' 16-byte reads of their runs do not collide.
+constexpr int XCH = 128;
+constexpr int XP = 36;
+
+// Template: R rows per wave, S waves share a row group (column slices).
+// gr = runs per group (any value above the last run when the row is one group).
+template <int BITS, int R, int S>
+__global__ __launch_bounds__(256) void k_dequant_gemv(const uint32_t* __restrict__ packed,
+                                                      const float* __restrict__ scales,
+                                                      const uint8_t* __restrict__ zeros, int64_t rows, int64_t cols,
+                                                      int64_t G, uint32_t gr, const float* __restrict__ x,
+                                                      float* __restrict__ y) {
+  constexpr int RG = 4 / S;              // row groups per workgroup
+  constexpr int IT = XCH / (64 * S);     // runs per lane per chunk
+  static_assert(IT >= 1 && IT * 64 * S == XCH, "chunk must be whole lane sweeps");
+  __shared__ __align__(16) float xs[XCH * XP];
+  __shared__ float part[RG][R][S];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rg = wave / S, cs = wave % S;
+  const int64_t r0 = ((int64_t)blockIdx.x * RG + rg) * R;
+  const int64_t wpr = cols * BITS / 32;  // words per row
+  const int64_t nfull = cols / 32, nrun = (cols + 31) / 32;
+  const float unit = (BITS == 2 || BITS == 4) ? code_unit() : 1.0f;
+  const uint32_t* prow[R];
+  const float* srow[R];
+  const uint8_t* zrow[R];
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    const int64_t r = r0 + q < rows ? r0 + q : rows - 1;  // rows past the end repeat the last, unwritten
+    prow[q] = packed + r * wpr;
+    srow[q] = scales + r * G;
+    zrow[q] = zeros + r * G;
+  }
+  // Operands of one run for the R rows: codes, scale, zero point.
+  struct Ops {
+    uint32_t w[R][BITS];
+    float s[R], z[R];
+  };
+  auto fetch = [&](int64_t k, Ops& o) {
+    if (k < nfull) {
+#pragma unroll
+      for (int q = 0; q < R; ++q) load_run<BITS>(prow[q] + BITS * k, o.w[q]);
+    } else {
+      // the last, partial run: m codes in m b / 32 whole words (x past cols is 0 in xs)
+      const int nw = (int)(cols - 32 * k) * BITS / 32;
+#pragma unroll
+      for (int q = 0; q < R; ++q)
+#pragma unroll
+        for (int j = 0; j < BITS; ++j) o.w[q][j] = j < nw ? prow[q][BITS * k + j] : 0u;
+    }
+    const uint32_t gk = (uint32_t)k / gr;
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      o.s[q] = srow[q][gk];
+      o.z[q] = (float)zrow[q][gk];
+    }
+  };
+  float yacc[R] = {};
+  Ops cur;
+  {
+    const int64_t k = (int64_t)cs * 64 + lane;
+    if (k < nrun) fetch(k, cur);
+  }
+  for (int64_t c0 = 0; c0 < nrun; c0 += XCH) {
+    __syncthreads();  // the previous chunk's reads of xs are done
+#pragma unroll
+    for (int j = 0; j < XCH * 32 / 1024; ++j) {
+      const int e = 4 * (threadIdx.x + 256 * j);  // float index within the chunk
+      const int64_t col = 32 * c0 + e;
+      // cols is a multiple of 4 (cols b is whole words), so a vector is all in or all out
+      const f32x4 v = col < cols ? *reinterpret_cast<const f32x4*>(x + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      *reinterpret_cast<float4*>(xs + (e >> 5) * XP + (e & 31)) = make_float4(v.x, v.y, v.z, v.w);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int kk = cs * 64 + lane + it * 64 * S;
+      const int64_t k = c0 + kk;
+      // the lane's next run (in this chunk or the first of the next) is in flight
+      // while this one is applied
+      Ops nxt;
+      if (k + 64 * S < nrun) fetch(k + 64 * S, nxt);
+      if (k < nrun) {
+        float xv[32];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float4 v = *reinterpret_cast<const float4*>(xs + kk * XP + 4 * i);
+          xv[4 * i] = v.x; xv[4 * i + 1] = v.y; xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
+        }
+        float sx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) sx += xv[i];
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+          yacc[q] = fmaf(cur.s[q], fmaf(run_dot<BITS>(cur.w[q], xv), unit, -cur.z[q] * sx), yacc[q]);
+      }
+      cur = nxt;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    float v = yacc[q];
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m, 64);
+    yacc[q] = v;
+  }
+  if constexpr (S == 1) {
+    if (lane < R) {
+      float v = yacc[0];
+#pragma unroll
+      for (int q = 1; q < R; ++q)
+        if (lane == q) v = yacc[q];
+      if (r0 + lane < rows) y[r0 + lane] = v;
+    }
+  } else {
+    if (lane == 0)
+#pragma unroll
+      for (int q = 0; q < R; ++q) part[rg][q][cs] = yacc[q];
+    __syncthreads();
+    if (threadIdx.x < RG * R) {
+      const int trg = threadIdx.x / R, tq = threadIdx.x % R;
+      float v = 0.0f;
+#pragma unroll
+      for (int c = 0; c < S; ++c) v += part[trg][tq][c];
+      const int64_t r = ((int64_t)blockIdx.x * RG + trg) * R + tq;
+      if (r < rows) y[r] = v;
+    }
+  }
+}
+
+template <int BITS, int R, int S>
+hipError_t launch(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows, int64_t cols,
+                  int64_t G, uint32_t gr, const float* x, float* y, hipStream_t stream) {
+  constexpr int64_t rows_per_wg = (4 / S) * R;
+  const unsigned grid = (unsigned)((rows + rows_per_wg - 1) / rows_per_wg);
+  hipLaunchKernelGGL((k_dequant_gemv<BITS, R, S>), dim3(grid), dim3(256), 0, stream, packed, scales, zeros, rows,
+                     cols, G, gr, x, y);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_bits(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows, int64_t cols,
+                       int64_t G, uint32_t gr, const float* x, float* y, hipStream_t stream) {
+  // Few rows: two rows a wave and the columns split over two waves, for enough
+  // workgroups to fill the chip; many rows: four rows a wave, x reused more.
+  if (rows < 8192) return launch<BITS, 2, 2>(packed, scales, zeros, rows, cols, G, gr, x, y, stream);
+  return launch<BITS, 4, 1>(packed, scales, zeros, rows, cols, G, gr, x, y, stream);
+}
+
+}  // namespace
+
+bool dequant_gemv_supported(int64_t cols, int32_t bits, int32_t groupsize) {
+  if (!(bits == 2 || bits == 3 || bits == 4 || bits == 8)) return false;
+  if ((cols * bits) % 32 != 0) return false;
+  return groupsize == -1 || (groupsize > 0 && groupsize % 32 == 0);
+}
+
+hipError_t dequant_gemv(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
+                        int64_t cols, int32_t bits, int32_t groupsize, const float* x, float* y, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  // cols == 0 still launches: no runs, every y is written as 0
+  const int64_t nrun = (cols + 31) / 32;
+  const int64_t G = groupsize == -1 ? 1 : (cols + groupsize - 1) / groupsize;
+  const uint32_t gr = groupsize == -1 ? (uint32_t)(nrun > 0 ? nrun : 1) : (uint32_t)(groupsize / 32);
+  switch (bits) {
+    case 2: return launch_bits<2>(packed, scales, zeros, rows, cols, G, gr, x, y, stream);
+    case 3: return launch_bits<3>(packed, scales, zeros, rows, cols, G, gr, x, y, stream);
+    case 4: return launch_bits<4>(packed, scales, zeros, rows, cols, G, gr, x, y, stream);
+    default: return launch_bits<8>(packed, scales, zeros, rows, cols, G, gr, x, y, stream);
+  }
+}
+
+}  // namespace gptq

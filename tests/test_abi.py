@@ -25,7 +25,7 @@ def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"gptq_hessian_workspace_bytes", "gptq_accumulate_hessian",
                           "gptq_quantize_workspace_bytes", "gptq_quantize_layer", "gptq_pack",
-                          "gptq_status_string", "gptq_version"}
+                          "gptq_dequant_gemv", "gptq_status_string", "gptq_version"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -87,6 +87,24 @@ def test_hessian_argument_errors_and_workspace():
 @pytest.mark.parametrize("bits,cols", [(3, 40), (4, 12), (5, 64), (2, 8)])
 def test_pack_argument_errors(bits, cols):
     assert g.lib().gptq_pack(FAKE, 4, cols, bits, FAKE, None) == g.GPTQ_EINVAL
+
+
+def _gemv(rows, cols, bits, groupsize, packed=FAKE, x=FAKE, y=FAKE):
+    return g.lib().gptq_dequant_gemv(packed, FAKE, FAKE, rows, cols, bits, groupsize, x, y, None)
+
+
+def test_dequant_gemv_argument_errors():
+    assert _gemv(8, 256, 5, 128) == g.GPTQ_EINVAL              # bits
+    assert _gemv(8, 256, 4, 0) == g.GPTQ_EINVAL                # groupsize 0
+    assert _gemv(8, 256, 4, -3) == g.GPTQ_EINVAL               # groupsize < -1
+    assert _gemv(8, 40, 3, -1) == g.GPTQ_EINVAL                # cols * bits not whole words
+    assert _gemv(8, 12, 4, -1) == g.GPTQ_EINVAL
+    assert _gemv(-1, 256, 4, 128) == g.GPTQ_EINVAL
+    assert _gemv(8, 256, 4, 48) == g.GPTQ_EUNSUPPORTED         # groups must be whole 32-code runs
+    assert _gemv(8, 256, 4, 128, packed=None) == g.GPTQ_EINVAL
+    assert _gemv(8, 256, 4, 128, y=None) == g.GPTQ_EINVAL
+    assert _gemv(8, 256, 4, 128, x=ctypes.c_void_p(0x1002)) == g.GPTQ_EINVAL  # misaligned
+    assert _gemv(0, 256, 4, 128, packed=None) == g.GPTQ_OK     # no rows: no work
 
 
 def test_product_path_has_no_oracle_import():
