@@ -157,6 +157,61 @@ def gemv_measure(g, torch, packed, scales, zeros, rows, cols, bits, groupsize, d
             "frac": gbs / PEAK_HBM_GBS, "weight_copies": copies}
 
 
+def hadamard_measure(g, torch, Wd, n, dev, copies=6, rounds=3):
+    """The fixed Hadamard rotation (block n) on this layer, outside the timed step:
+    W' = W Q from bf16 W (gptq_hadamard_rows) and H' = Q^T H Q in place
+    (gptq_hadamard_hessian), each over several copies larger than the last-level
+    cache together, queued behind a short device sleep and timed with HIP events."""
+    import ctypes
+    rows = Wd.shape[0]
+    block = n & -n
+    while block > 4096:
+        block //= 2
+    gen = torch.Generator(dev).manual_seed(2)
+    signs = torch.where(torch.rand(n, device=dev, generator=gen) < 0.5, -1.0, 1.0).float()
+    Ws = [Wd.clone() for _ in range(copies)]
+    Wo = [torch.empty((rows, n), dtype=torch.float32, device=dev) for _ in range(copies)]
+    Hs = []
+    for _ in range(copies):
+        a = torch.randn(n, n, device=dev, generator=gen)
+        Hs.append(a + a.T)
+    L = g.lib()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sp = ctypes.c_void_p(signs.data_ptr())
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(20_000_000)
+        e0.record()
+        for _ in range(rounds):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (rounds * copies)
+
+    def rot_w():
+        for a, b in zip(Ws, Wo):
+            if L.gptq_hadamard_rows(ctypes.c_void_p(a.data_ptr()), g.GPTQ_BF16, n, ctypes.c_void_p(b.data_ptr()), n,
+                                    rows, n, sp, block, st):
+                raise RuntimeError("gptq_hadamard_rows failed")
+
+    def rot_h():
+        for h in Hs:
+            if L.gptq_hadamard_hessian(ctypes.c_void_p(h.data_ptr()), n, sp, block, st):
+                raise RuntimeError("gptq_hadamard_hessian failed")
+
+    us_w, us_h = timed(rot_w), timed(rot_h)
+    bytes_w = rows * n * (2 + 4) + n * 4
+    bytes_h = 2 * n * n * 4 + n * 4
+    return {"kernels": "k_hadamard_rows, k_tile_pairs", "block": block,
+            "weights_us": us_w, "weights_algorithmic_bytes": bytes_w, "weights_GBs": bytes_w / us_w / 1e3,
+            "weights_frac": bytes_w / us_w / 1e3 / PEAK_HBM_GBS,
+            "hessian_us": us_h, "hessian_algorithmic_bytes": bytes_h, "hessian_GBs": bytes_h / us_h / 1e3,
+            "hessian_frac": bytes_h / us_h / 1e3 / PEAK_HBM_GBS}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -264,6 +319,7 @@ def main():
                      "algorithmic_bytes": alg["x_bytes"] + 4.0 * cols * cols},
         "input_generation_s": gen_s,
     }
+    rec["hadamard_rotation"] = hadamard_measure(g, torch, Wd, cols, dev)
     rec["dequant_gemv"] = gemv_measure(g, torch, packed, scales, zeros, rows, cols, bits, wl.groupsize, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(W_bits, X_bits, rows, cols, tokens, bits, args)

@@ -157,6 +157,33 @@ int gptq_dequant_gemv(const uint32_t* packed, const float* scales, const uint8_t
                       int64_t cols, int32_t bits, int32_t groupsize, const float* x, float* y,
                       gptq_stream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Fixed randomised Hadamard rotation, the untrained form of the rotation
+ * preprocessing on the OneComp hub article (rotations absorbed into the
+ * weights, Hadamard transforms applied online to activations):
+ *   Q = diag(signs) * blockdiag(H_b, ..., H_b) / sqrt(b),
+ * H_b the Sylvester Hadamard matrix of order b = block (H_1 = [1],
+ * H_2m = [[H_m, H_m], [H_m, -H_m]]), orthogonal when every sign is +-1.
+ * A layer y = W x becomes W' = W Q with inputs x' = Q^T x (W' x' = W x), and
+ * its Hessian H' = Q^T H Q; quantize W' against H'.
+ * block: a power of two, 1 <= block <= 4096, dividing n (else GPTQ_EINVAL).
+ * signs: device float [n].  Accumulation is fp32; log2(block) butterfly
+ * stages, the sign on input, 1/sqrt(block) on output.
+ * ------------------------------------------------------------------------- */
+
+/* out[r, :] = in[r, :] Q for r < rows (row strides ld_in, ld_out elements,
+ * >= n).  in is bf16 or fp32; out is fp32.  In place is allowed for fp32 input
+ * with out == in and ld_out == ld_in; otherwise the two must not overlap.
+ * Used for the weights (W -> W Q) and for activations or inputs (x^T -> x^T Q,
+ * which is (Q^T x)^T).  rows == 0 or n == 0: no work. */
+int gptq_hadamard_rows(const void* in, gptq_dtype in_dtype, int64_t ld_in, float* out, int64_t ld_out,
+                       int64_t rows, int64_t n, const float* signs, int32_t block, gptq_stream_t stream);
+
+/* H[n, n] := Q^T H Q in place, for a symmetric fp32 H (as written by
+ * gptq_accumulate_hessian).  The result is written in full and exactly
+ * symmetric (the lower triangle mirrors the upper).  No workspace. */
+int gptq_hadamard_hessian(float* H, int64_t n, const float* signs, int32_t block, gptq_stream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* gptq_status_string(int status);
 

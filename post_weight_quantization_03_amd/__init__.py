@@ -75,6 +75,10 @@ def lib():
     L.gptq_pack.restype = ctypes.c_int
     L.gptq_dequant_gemv.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, vp, vp]
     L.gptq_dequant_gemv.restype = ctypes.c_int
+    L.gptq_hadamard_rows.argtypes = [vp, ctypes.c_int, i64, vp, i64, i64, i64, vp, i32, vp]
+    L.gptq_hadamard_rows.restype = ctypes.c_int
+    L.gptq_hadamard_hessian.argtypes = [vp, i64, vp, i32, vp]
+    L.gptq_hadamard_hessian.restype = ctypes.c_int
     L.gptq_status_string.argtypes = [ctypes.c_int]
     L.gptq_status_string.restype = ctypes.c_char_p
     L.gptq_version.argtypes = []
@@ -204,6 +208,38 @@ def gptq_dequant_gemv(packed, scales, zeros, bits: int, groupsize: int, x, y, st
     if st:
         raise GptqError(st, "gptq_dequant_gemv")
     return y
+
+
+def gptq_hadamard_rows(inp, signs, block: int, out=None, stream=None):
+    """out [rows, n] fp32 = inp Q (inp bf16 or fp32 with unit column stride); out may be inp (fp32)."""
+    torch = _torch()
+    if inp.dim() != 2 or not inp.is_cuda or inp.stride(1) != 1:
+        raise ValueError("inp must be a 2-D device tensor with unit column stride")
+    rows, n = inp.shape
+    if out is None:
+        out = torch.empty((rows, n), dtype=torch.float32, device=inp.device)
+    if (out.dtype != torch.float32 or out.shape != (rows, n) or out.stride(1) != 1 or not out.is_cuda
+            or signs.dtype != torch.float32 or signs.shape != (n,)):
+        raise ValueError("shape or dtype mismatch")
+    _check_dev(signs)
+    st = lib().gptq_hadamard_rows(_ptr(inp), _dtype_code(inp), inp.stride(0), _ptr(out), out.stride(0), rows, n,
+                                  _ptr(signs), block, _stream(stream))
+    if st:
+        raise GptqError(st, "gptq_hadamard_rows")
+    return out
+
+
+def gptq_hadamard_hessian(H, signs, block: int, stream=None):
+    """H [n, n] fp32 := Q^T H Q in place."""
+    _check_dev(H, signs)
+    n = H.shape[0]
+    torch = _torch()
+    if H.dtype != torch.float32 or H.shape != (n, n) or signs.dtype != torch.float32 or signs.shape != (n,):
+        raise ValueError("shape or dtype mismatch")
+    st = lib().gptq_hadamard_hessian(_ptr(H), n, _ptr(signs), block, _stream(stream))
+    if st:
+        raise GptqError(st, "gptq_hadamard_hessian")
+    return H
 
 
 def quantize(W, H, params: Params, stream=None, want_what=True):

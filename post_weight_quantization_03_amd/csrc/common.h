@@ -107,6 +107,12 @@ bool dequant_gemv_supported(int64_t cols, int32_t bits, int32_t groupsize);
 hipError_t dequant_gemv(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
                         int64_t cols, int32_t bits, int32_t groupsize, const float* x, float* y, hipStream_t stream);
 
+// Fixed randomised Hadamard rotation (k_hadamard.hip).
+int64_t hadamard_chunks(int64_t n);
+hipError_t hadamard_rows(const void* in, bool in_bf16, int64_t ld_in, float* out, int64_t ld_out, int64_t rows,
+                         int64_t n, const float* signs, int block, hipStream_t stream);
+hipError_t hadamard_hessian(float* H, int64_t n, const float* signs, int block, hipStream_t stream);
+
 // Small utility kernels (k_factor.hip).
 hipError_t fill_i32(int* p, int64_t n, int v, hipStream_t stream);
 hipError_t copy_status(const int* src, int32_t* dst, hipStream_t stream);

@@ -192,4 +192,32 @@ int gptq_dequant_gemv(const uint32_t* packed, const float* scales, const uint8_t
              : GPTQ_EHIP;
 }
 
+static bool hadamard_block_ok(int64_t n, int32_t block) {
+  return block >= 1 && block <= 4096 && (block & (block - 1)) == 0 && n % block == 0;
+}
+
+int gptq_hadamard_rows(const void* in, gptq_dtype in_dtype, int64_t ld_in, float* out, int64_t ld_out,
+                       int64_t rows, int64_t n, const float* signs, int32_t block, gptq_stream_t stream) {
+  if (rows < 0 || n < 0 || rows > MAX_DIM || n > MAX_DIM) return GPTQ_EINVAL;
+  if (in_dtype != GPTQ_BF16 && in_dtype != GPTQ_F32) return GPTQ_EINVAL;
+  if (!hadamard_block_ok(n, block)) return GPTQ_EINVAL;
+  if (rows == 0 || n == 0) return GPTQ_OK;
+  if (!in || !out || !signs || ld_in < n || ld_out < n) return GPTQ_EINVAL;
+  if (static_cast<const void*>(out) == in && (in_dtype != GPTQ_F32 || ld_in != ld_out)) return GPTQ_EINVAL;
+  if (rows * hadamard_chunks(n) > INT32_MAX) return GPTQ_EUNSUPPORTED;
+  return hadamard_rows(in, in_dtype == GPTQ_BF16, ld_in, out, ld_out, rows, n, signs, block,
+                       (hipStream_t)stream) == hipSuccess
+             ? GPTQ_OK
+             : GPTQ_EHIP;
+}
+
+int gptq_hadamard_hessian(float* H, int64_t n, const float* signs, int32_t block, gptq_stream_t stream) {
+  if (n < 0 || n > MAX_DIM) return GPTQ_EINVAL;
+  if (!hadamard_block_ok(n, block)) return GPTQ_EINVAL;
+  if (n == 0) return GPTQ_OK;
+  if (!H || !signs) return GPTQ_EINVAL;
+  if (n * hadamard_chunks(n) > INT32_MAX || (n + 63) / 64 > 65535) return GPTQ_EUNSUPPORTED;
+  return hadamard_hessian(H, n, signs, block, (hipStream_t)stream) == hipSuccess ? GPTQ_OK : GPTQ_EHIP;
+}
+
 }  // extern "C"

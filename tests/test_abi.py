@@ -25,7 +25,8 @@ def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"gptq_hessian_workspace_bytes", "gptq_accumulate_hessian",
                           "gptq_quantize_workspace_bytes", "gptq_quantize_layer", "gptq_pack",
-                          "gptq_dequant_gemv", "gptq_status_string", "gptq_version"}
+                          "gptq_dequant_gemv", "gptq_hadamard_rows", "gptq_hadamard_hessian",
+                          "gptq_status_string", "gptq_version"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -105,6 +106,23 @@ def test_dequant_gemv_argument_errors():
     assert _gemv(8, 256, 4, 128, y=None) == g.GPTQ_EINVAL
     assert _gemv(8, 256, 4, 128, x=ctypes.c_void_p(0x1002)) == g.GPTQ_EINVAL  # misaligned
     assert _gemv(0, 256, 4, 128, packed=None) == g.GPTQ_OK     # no rows: no work
+
+
+def test_hadamard_argument_errors():
+    L = g.lib()
+    B, F = g.GPTQ_BF16, g.GPTQ_F32
+    assert L.gptq_hadamard_rows(FAKE, F, 256, FAKE, 256, 4, 256, FAKE, 3, None) == g.GPTQ_EINVAL     # block
+    assert L.gptq_hadamard_rows(FAKE, F, 256, FAKE, 256, 4, 256, FAKE, 8192, None) == g.GPTQ_EINVAL  # > 4096
+    assert L.gptq_hadamard_rows(FAKE, F, 96, FAKE, 96, 4, 96, FAKE, 64, None) == g.GPTQ_EINVAL       # 64 !| 96
+    assert L.gptq_hadamard_rows(FAKE, 7, 256, FAKE, 256, 4, 256, FAKE, 64, None) == g.GPTQ_EINVAL    # dtype
+    assert L.gptq_hadamard_rows(FAKE, F, 128, FAKE, 256, 4, 256, FAKE, 64, None) == g.GPTQ_EINVAL    # ld_in < n
+    assert L.gptq_hadamard_rows(FAKE, B, 256, FAKE, 256, 4, 256, FAKE, 64, None) == g.GPTQ_EINVAL    # bf16 in place
+    assert L.gptq_hadamard_rows(FAKE, F, 256, FAKE, 512, 4, 256, FAKE, 64, None) == g.GPTQ_EINVAL    # strides differ
+    assert L.gptq_hadamard_rows(FAKE, F, 256, None, 256, 4, 256, FAKE, 64, None) == g.GPTQ_EINVAL
+    assert L.gptq_hadamard_rows(None, F, 256, None, 256, 0, 256, None, 64, None) == g.GPTQ_OK        # no rows
+    assert L.gptq_hadamard_hessian(FAKE, 100, FAKE, 8, None) == g.GPTQ_EINVAL                        # 8 !| 100
+    assert L.gptq_hadamard_hessian(None, 128, FAKE, 8, None) == g.GPTQ_EINVAL
+    assert L.gptq_hadamard_hessian(None, 0, None, 1, None) == g.GPTQ_OK
 
 
 def test_product_path_has_no_oracle_import():
