@@ -9,11 +9,11 @@
 // row (chunks start at multiples of 4096, so every b-block lies in one chunk).
 // The Walsh-Hadamard transform of order b is a butterfly on each of the low
 // log2 b bits of the element index, and those butterflies commute, so the chunk
-// goes through three register passes of four bits each: a thread holds 16
-// elements whose indices differ exactly in bits 8-11, then 4-7, then 0-3, and
-// the elements move between passes through LDS (one pad word per 16 keeps the
-// strided reads on distinct banks).  Loads and stores are coalesced; the sign
-// is applied on load and 1/sqrt(b) on store.  HBM-bound.
+// goes through three register passes of four bits each (a thread holds 16
+// elements whose indices differ in four of the bits), and the elements move
+// between passes through padded LDS.  Aligned rows enter and leave in 16-byte
+// (fp32) or 8-byte (bf16) vectors per lane, others element by element; both are
+// coalesced.  The sign is applied on load and 1/sqrt(b) on store.  HBM-bound.
 //
 // Hessian.  H Q row-wise, an in-place transpose (tile pairs), Q^T H Q row-wise
 // again (H^T = H), then the upper triangle mirrored into the lower so the
@@ -25,17 +25,16 @@ namespace {
 
 constexpr int HCH = 4096;  // elements per chunk
 
-__device__ __forceinline__ int lidx(int e) { return e + (e >> 4); }
-
 __device__ __forceinline__ float to_f32(const float* p, int i) { return p[i]; }
 __device__ __forceinline__ float to_f32(const uint16_t* p, int i) { return __uint_as_float((uint32_t)p[i] << 16); }
 
-// Butterflies on register-index bits 0-3, which stand for element-index bits
-// base..base+3; only the element bits below kb (= log2 b) take part.
-__device__ __forceinline__ void stages16(float (&v)[16], int base, int kb) {
+// Butterflies on the four register-index bits; register bit r stands for
+// element-index bit eb[r], and only element bits below kb (= log2 b) take part.
+__device__ __forceinline__ void stages16(float (&v)[16], int eb0, int eb1, int eb2, int eb3, int kb) {
+  const int eb[4] = {eb0, eb1, eb2, eb3};
 #pragma unroll
   for (int bit = 0; bit < 4; ++bit) {
-    if (base + bit < kb) {
+    if (eb[bit] < kb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if (!(i & (1 << bit))) {
@@ -48,49 +47,120 @@ __device__ __forceinline__ void stages16(float (&v)[16], int base, int kb) {
   }
 }
 
+// Scalar form: any alignment.  A thread's 16 elements differ in element bits
+// 8-11, then 4-7, then 0-3; LDS index e + e / 16.
 template <typename InT>
+__device__ __forceinline__ void chunk_scalar(const InT* src, float* dst, const float* sg, int m, int kb, float scale,
+                                             float* buf) {
+  const int t = threadIdx.x;
+  auto li = [](int e) { return e + (e >> 4); };
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = t + 256 * i;
+    v[i] = e < m ? to_f32(src, e) * sg[e] : 0.0f;
+  }
+  stages16(v, 8, 9, 10, 11, kb);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) buf[li(t + 256 * i)] = v[i];
+  __syncthreads();
+  // each slot below is read and rewritten by the one thread that owns it
+  const int eb = (t & 15) + 256 * (t >> 4);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = buf[li(eb + 16 * i)];
+  stages16(v, 4, 5, 6, 7, kb);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) buf[li(eb + 16 * i)] = v[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = buf[li(16 * t + i)];
+  stages16(v, 0, 1, 2, 3, kb);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) buf[li(16 * t + i)] = v[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = t + 256 * i;
+    if (e < m) dst[e] = buf[li(e)] * scale;
+  }
+}
+
+typedef float f32x4a __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4a __attribute__((ext_vector_type(4)));
+
+// Vector form: rows 16-byte (fp32) or 8-byte (bf16) aligned, m a multiple of 4.
+// A thread's 16 elements are 4 consecutive ones in each of 4 segments 1024
+// apart (element bits 0-1 and 10-11), then differ in bits 2-5, then 6-9; the
+// chunk enters and leaves in whole vectors.  LDS index e + 4 (e / 64) keeps
+// each group of 4 contiguous and 16-byte aligned.
+template <typename InT>
+__device__ __forceinline__ void chunk_vector(const InT* src, float* dst, const float* sg, int m, int kb, float scale,
+                                             float* buf) {
+  const int t = threadIdx.x;
+  auto li = [](int e) { return e + 4 * (e >> 6); };
+  float v[16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * t + 1024 * j;
+    if (e < m) {
+      float a[4];
+      if constexpr (sizeof(InT) == 4) {
+        const f32x4a x = *reinterpret_cast<const f32x4a*>(src + e);
+        a[0] = x.x; a[1] = x.y; a[2] = x.z; a[3] = x.w;
+      } else {
+        const u16x4a x = *reinterpret_cast<const u16x4a*>(src + e);
+        a[0] = __uint_as_float((uint32_t)x.x << 16); a[1] = __uint_as_float((uint32_t)x.y << 16);
+        a[2] = __uint_as_float((uint32_t)x.z << 16); a[3] = __uint_as_float((uint32_t)x.w << 16);
+      }
+      const f32x4a d = *reinterpret_cast<const f32x4a*>(sg + e);
+      v[4 * j] = a[0] * d.x; v[4 * j + 1] = a[1] * d.y; v[4 * j + 2] = a[2] * d.z; v[4 * j + 3] = a[3] * d.w;
+    } else {
+      v[4 * j] = v[4 * j + 1] = v[4 * j + 2] = v[4 * j + 3] = 0.0f;
+    }
+  }
+  stages16(v, 0, 1, 10, 11, kb);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<float4*>(buf + li(4 * t + 1024 * j)) = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+  __syncthreads();
+  // register bits = element bits 2-5; thread = bits 0-1 and 6-11
+  const int e2 = (t & 3) + 64 * (t >> 2);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = buf[li(e2 + 4 * i)];
+  stages16(v, 2, 3, 4, 5, kb);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) buf[li(e2 + 4 * i)] = v[i];
+  __syncthreads();
+  // register bits = element bits 6-9; thread = bits 0-5 and 10-11
+  const int e3 = (t & 63) + 1024 * (t >> 6);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = buf[li(e3 + 64 * i)];
+  stages16(v, 6, 7, 8, 9, kb);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) buf[li(e3 + 64 * i)] = v[i];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * t + 1024 * j;
+    if (e < m) {
+      const float4 r = *reinterpret_cast<const float4*>(buf + li(e));
+      *reinterpret_cast<float4*>(dst + e) = make_float4(r.x * scale, r.y * scale, r.z * scale, r.w * scale);
+    }
+  }
+}
+
+template <typename InT, bool VEC>
 __global__ __launch_bounds__(256) void k_hadamard_rows(const InT* in, int64_t ld_in, float* out, int64_t ld_out,
                                                        int64_t n, int64_t nchunk, const float* __restrict__ signs,
                                                        int kb, float scale) {
-  __shared__ float buf[HCH + HCH / 16];
-  const int t = threadIdx.x;
+  __shared__ __align__(16) float buf[HCH + HCH / 16];
   const int64_t row = blockIdx.x / nchunk;
   const int64_t c0 = ((int64_t)blockIdx.x - row * nchunk) * HCH;
-  const InT* src = in + row * ld_in + c0;
-  float* dst = out + row * ld_out + c0;
   const int m = (int)(n - c0 < HCH ? n - c0 : HCH);  // valid elements; a multiple of b
-  float v[16];
-  // element t + 256 i: register index = element bits 8-11
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int e = t + 256 * i;
-    v[i] = e < m ? to_f32(src, e) * signs[c0 + e] : 0.0f;
-  }
-  stages16(v, 8, kb);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) buf[lidx(t + 256 * i)] = v[i];
-  __syncthreads();
-  // element (t & 15) + 16 i + 256 (t >> 4): register index = element bits 4-7.
-  // Each slot is read and rewritten by the one thread that owns it here.
-  const int eb = (t & 15) + 256 * (t >> 4);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = buf[lidx(eb + 16 * i)];
-  stages16(v, 4, kb);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) buf[lidx(eb + 16 * i)] = v[i];
-  __syncthreads();
-  // element 16 t + i: register index = element bits 0-3
-#pragma unroll
-  for (int i = 0; i < 16; ++i) v[i] = buf[lidx(16 * t + i)];
-  stages16(v, 0, kb);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) buf[lidx(16 * t + i)] = v[i];
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int e = t + 256 * i;
-    if (e < m) dst[e] = buf[lidx(e)] * scale;
-  }
+  if constexpr (VEC)
+    chunk_vector(in + row * ld_in + c0, out + row * ld_out + c0, signs + c0, m, kb, scale, buf);
+  else
+    chunk_scalar(in + row * ld_in + c0, out + row * ld_out + c0, signs + c0, m, kb, scale, buf);
 }
 
 // Tile pairs of a square matrix, one workgroup per unordered pair of 64 x 64
@@ -149,12 +219,28 @@ hipError_t hadamard_rows(const void* in, bool in_bf16, int64_t ld_in, float* out
   const unsigned grid = (unsigned)(rows * nchunk);
   const int kb = log2_exact(block);
   const float scale = (float)(1.0 / std::sqrt((double)block));
-  if (in_bf16)
-    hipLaunchKernelGGL(k_hadamard_rows<uint16_t>, dim3(grid), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(in), ld_in, out, ld_out, n, nchunk, signs, kb, scale);
-  else
-    hipLaunchKernelGGL(k_hadamard_rows<float>, dim3(grid), dim3(256), 0, stream, static_cast<const float*>(in),
-                       ld_in, out, ld_out, n, nchunk, signs, kb, scale);
+  const int64_t esz = in_bf16 ? 2 : 4;
+  auto al = [](const void* p, int64_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; };
+  // whole vectors: every row start aligned, and a chunk's valid length a multiple of 4
+  const bool vec = n % 4 == 0 && al(in, 4 * esz) && (ld_in * esz) % (4 * esz) == 0 && al(out, 16) &&
+                   (ld_out * 4) % 16 == 0 && al(signs, 16);
+  if (in_bf16) {
+    const uint16_t* p = static_cast<const uint16_t*>(in);
+    if (vec)
+      hipLaunchKernelGGL((k_hadamard_rows<uint16_t, true>), dim3(grid), dim3(256), 0, stream, p, ld_in, out, ld_out,
+                         n, nchunk, signs, kb, scale);
+    else
+      hipLaunchKernelGGL((k_hadamard_rows<uint16_t, false>), dim3(grid), dim3(256), 0, stream, p, ld_in, out,
+                         ld_out, n, nchunk, signs, kb, scale);
+  } else {
+    const float* p = static_cast<const float*>(in);
+    if (vec)
+      hipLaunchKernelGGL((k_hadamard_rows<float, true>), dim3(grid), dim3(256), 0, stream, p, ld_in, out, ld_out, n,
+                         nchunk, signs, kb, scale);
+    else
+      hipLaunchKernelGGL((k_hadamard_rows<float, false>), dim3(grid), dim3(256), 0, stream, p, ld_in, out, ld_out,
+                         n, nchunk, signs, kb, scale);
+  }
   return hipGetLastError();
 }
 

@@ -45,7 +45,11 @@ def _gpu_rows(A, d, b, bf16=False, pad=0, inplace=False):
     g = _lib()
     torch, dev = torch_dev()
     rows, n = A.shape
-    if bf16:
+    if bf16 and pad:
+        full = torch.zeros((rows, n + pad), dtype=torch.bfloat16, device=dev)
+        full[:, :n] = bf16_dev(A)
+        src = full[:, :n]
+    elif bf16:
         src = bf16_dev(A)
     elif pad:
         full = torch.zeros((rows, n + pad), dtype=torch.float32, device=dev)
@@ -71,6 +75,8 @@ def _gpu_rows(A, d, b, bf16=False, pad=0, inplace=False):
     (6, 300, 4, False, 0, False),
     (3, 12288, 2048, False, 0, True),
     (1, 5120, 1024, False, 0, False),     # one input vector x^T -> (Q^T x)^T
+    (2, 1002, 2, False, 0, False),        # width not a multiple of 4: element-wise path
+    (3, 4096, 4096, True, 2, False),      # bf16 rows not 8-byte aligned: element-wise path
 ])
 def test_hadamard_rows_parity(rows, n, b, bf16, pad, inplace):
     say(f"hadamard rows rows={rows} n={n} block={b} bf16={bf16} pad={pad} inplace={inplace}")
@@ -78,7 +84,7 @@ def test_hadamard_rows_parity(rows, n, b, bf16, pad, inplace):
                           outliers=max(1, n // 100), outlier_factor=20.0, bf16=bf16).full()
     if bf16:
         A64 = synth.bf16_to_f32(A).astype(np.float64)
-        out = _gpu_rows(A, _signs(n, 1), b, bf16=True)
+        out = _gpu_rows(A, _signs(n, 1), b, bf16=True, pad=pad)
     else:
         A64 = A.astype(np.float64)
         out = _gpu_rows(A, _signs(n, 1), b, pad=pad, inplace=inplace)
