@@ -137,7 +137,8 @@ def gemv_measure(g, torch, packed, scales, zeros, rows, cols, bits, groupsize, d
     fn = g.lib().gptq_dequant_gemv
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     calls = [(ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(s_.data_ptr()), ctypes.c_void_p(z.data_ptr()), rows,
-              cols, bits, groupsize, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()), stream)
+              cols, bits, groupsize, ctypes.c_void_p(x.data_ptr()), g.GPTQ_F32, ctypes.c_void_p(y.data_ptr()),
+              stream)
              for p, s_, z in bufs]
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -144,7 +144,7 @@ int gptq_pack(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits, ui
  *   packed  uint32 [rows, cols*bits/32]   gptq_pack layout, dword aligned
  *   scales  float  [rows, G]              G = ceil(cols / g)
  *   zeros   uint8  [rows, G]
- *   x       float  [cols]
+ *   x       [cols], x_dtype bf16 or fp32 (bf16 widens exactly to fp32)
  *   y       float  [rows]                 written, not accumulated into
  * Accumulation is fp32 in a fixed order (bit-reproducible run to run).
  * bits in {2, 3, 4, 8}; (cols * bits) % 32 == 0; groupsize -1 or a positive
@@ -154,7 +154,7 @@ int gptq_pack(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits, ui
  * launch.  y must not alias the inputs.
  * ------------------------------------------------------------------------- */
 int gptq_dequant_gemv(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
-                      int64_t cols, int32_t bits, int32_t groupsize, const float* x, float* y,
+                      int64_t cols, int32_t bits, int32_t groupsize, const void* x, gptq_dtype x_dtype, float* y,
                       gptq_stream_t stream);
 
 /* ---------------------------------------------------------------------------

@@ -73,7 +73,7 @@ def lib():
     L.gptq_quantize_layer.restype = ctypes.c_int
     L.gptq_pack.argtypes = [vp, i64, i64, i32, vp, vp]
     L.gptq_pack.restype = ctypes.c_int
-    L.gptq_dequant_gemv.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, vp, vp]
+    L.gptq_dequant_gemv.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, vp, vp]
     L.gptq_dequant_gemv.restype = ctypes.c_int
     L.gptq_hadamard_rows.argtypes = [vp, ctypes.c_int, i64, vp, i64, i64, i64, vp, i32, vp]
     L.gptq_hadamard_rows.restype = ctypes.c_int
@@ -194,17 +194,18 @@ def gptq_pack(codes, bits: int, packed, stream=None):
 
 
 def gptq_dequant_gemv(packed, scales, zeros, bits: int, groupsize: int, x, y, stream=None):
-    """y [rows] = W^ x with W^ decoded from packed [rows, cols*bits/32] codes, scales and zeros [rows, G]."""
+    """y [rows] fp32 = W^ x with W^ decoded from packed [rows, cols*bits/32] codes, scales and zeros [rows, G];
+    x [cols] bf16 or fp32."""
     _check_dev(packed, scales, zeros, x, y)
     torch = _torch()
     rows, cols = packed.shape[0], x.shape[0]
-    if (x.dtype != torch.float32 or y.dtype != torch.float32 or scales.dtype != torch.float32
+    if (y.dtype != torch.float32 or scales.dtype != torch.float32
             or zeros.dtype != torch.uint8 or y.shape != (rows,) or x.dim() != 1
             or packed.dim() != 2 or packed.shape[1] * 32 != cols * bits or packed.element_size() != 4
             or scales.shape != zeros.shape or scales.shape[0] != rows):
         raise ValueError("shape or dtype mismatch")
     st = lib().gptq_dequant_gemv(_ptr(packed), _ptr(scales), _ptr(zeros), rows, cols, bits, groupsize, _ptr(x),
-                                 _ptr(y), _stream(stream))
+                                 _dtype_code(x), _ptr(y), _stream(stream))
     if st:
         raise GptqError(st, "gptq_dequant_gemv")
     return y

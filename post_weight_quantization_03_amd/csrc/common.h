@@ -105,7 +105,8 @@ hipError_t pack_launch(const uint8_t* codes, int64_t rows, int64_t cols, int bit
 // Dequantizing GEMV y = W^ x over packed codes (k_gemv.hip).
 bool dequant_gemv_supported(int64_t cols, int32_t bits, int32_t groupsize);
 hipError_t dequant_gemv(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
-                        int64_t cols, int32_t bits, int32_t groupsize, const float* x, float* y, hipStream_t stream);
+                        int64_t cols, int32_t bits, int32_t groupsize, const void* x, bool x_bf16, float* y,
+                        hipStream_t stream);
 
 // Fixed randomised Hadamard rotation (k_hadamard.hip).
 int64_t hadamard_chunks(int64_t n);

@@ -176,18 +176,20 @@ int gptq_pack(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits, ui
 }
 
 int gptq_dequant_gemv(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
-                      int64_t cols, int32_t bits, int32_t groupsize, const float* x, float* y,
+                      int64_t cols, int32_t bits, int32_t groupsize, const void* x, gptq_dtype x_dtype, float* y,
                       gptq_stream_t stream) {
   if (rows < 0 || cols < 0 || rows > MAX_DIM || cols > MAX_DIM) return GPTQ_EINVAL;
   if (!(bits == 2 || bits == 3 || bits == 4 || bits == 8)) return GPTQ_EINVAL;
   if (groupsize == 0 || groupsize < -1) return GPTQ_EINVAL;
+  if (x_dtype != GPTQ_BF16 && x_dtype != GPTQ_F32) return GPTQ_EINVAL;
   if ((cols * bits) % 32 != 0) return GPTQ_EINVAL;
   if (!dequant_gemv_supported(cols, bits, groupsize)) return GPTQ_EUNSUPPORTED;
   if (rows == 0) return GPTQ_OK;
   if (!y || (cols > 0 && (!packed || !scales || !zeros || !x))) return GPTQ_EINVAL;
   auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) != 0; };
   if (misaligned(packed) || misaligned(scales) || misaligned(x) || misaligned(y)) return GPTQ_EINVAL;
-  return dequant_gemv(packed, scales, zeros, rows, cols, bits, groupsize, x, y, (hipStream_t)stream) == hipSuccess
+  return dequant_gemv(packed, scales, zeros, rows, cols, bits, groupsize, x, x_dtype == GPTQ_BF16, y,
+                      (hipStream_t)stream) == hipSuccess
              ? GPTQ_OK
              : GPTQ_EHIP;
 }

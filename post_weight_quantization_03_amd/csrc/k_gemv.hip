@@ -23,6 +23,15 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2), aligned(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// Four consecutive x values as fp32 (bf16 widens exactly).
+__device__ __forceinline__ f32x4 load_x4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 load_x4(const uint16_t* p) {
+  const u16x4 v = *reinterpret_cast<const u16x4*>(p);
+  return f32x4{__uint_as_float((uint32_t)v.x << 16), __uint_as_float((uint32_t)v.y << 16),
+               __uint_as_float((uint32_t)v.z << 16), __uint_as_float((uint32_t)v.w << 16)};
+}
 
 template <int BITS>
 __device__ __forceinline__ void load_run(const uint32_t* p, uint32_t (&w)[BITS]) {
@@ -109,11 +118,11 @@ constexpr int XP = 36;
 
 // Template: R rows per wave, S waves share a row group (column slices).
 // gr = runs per group (any value above the last run when the row is one group).
-template <int BITS, int R, int S>
+template <int BITS, int R, int S, typename XT>
 __global__ __launch_bounds__(256) void k_dequant_gemv(const uint32_t* __restrict__ packed,
                                                       const float* __restrict__ scales,
                                                       const uint8_t* __restrict__ zeros, int64_t rows, int64_t cols,
-                                                      int64_t G, uint32_t gr, const float* __restrict__ x,
+                                                      int64_t G, uint32_t gr, const XT* __restrict__ x,
                                                       float* __restrict__ y) {
   constexpr int RG = 4 / S;              // row groups per workgroup
   constexpr int IT = XCH / (64 * S);     // runs per lane per chunk
@@ -173,7 +182,7 @@ __global__ __launch_bounds__(256) void k_dequant_gemv(const uint32_t* __restrict
       const int e = 4 * (threadIdx.x + 256 * j);  // float index within the chunk
       const int64_t col = 32 * c0 + e;
       // cols is a multiple of 4 (cols b is whole words), so a vector is all in or all out
-      const f32x4 v = col < cols ? *reinterpret_cast<const f32x4*>(x + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      const f32x4 v = col < cols ? load_x4(x + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       *reinterpret_cast<float4*>(xs + (e >> 5) * XP + (e & 31)) = make_float4(v.x, v.y, v.z, v.w);
     }
     __syncthreads();
@@ -233,19 +242,19 @@ __global__ __launch_bounds__(256) void k_dequant_gemv(const uint32_t* __restrict
   }
 }
 
-template <int BITS, int R, int S>
+template <int BITS, int R, int S, typename XT>
 hipError_t launch(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows, int64_t cols,
-                  int64_t G, uint32_t gr, const float* x, float* y, hipStream_t stream) {
+                  int64_t G, uint32_t gr, const XT* x, float* y, hipStream_t stream) {
   constexpr int64_t rows_per_wg = (4 / S) * R;
   const unsigned grid = (unsigned)((rows + rows_per_wg - 1) / rows_per_wg);
-  hipLaunchKernelGGL((k_dequant_gemv<BITS, R, S>), dim3(grid), dim3(256), 0, stream, packed, scales, zeros, rows,
+  hipLaunchKernelGGL((k_dequant_gemv<BITS, R, S, XT>), dim3(grid), dim3(256), 0, stream, packed, scales, zeros, rows,
                      cols, G, gr, x, y);
   return hipGetLastError();
 }
 
-template <int BITS>
+template <int BITS, typename XT>
 hipError_t launch_bits(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows, int64_t cols,
-                       int64_t G, uint32_t gr, const float* x, float* y, hipStream_t stream) {
+                       int64_t G, uint32_t gr, const XT* x, float* y, hipStream_t stream) {
   // Few rows: two rows a wave and the columns split over two waves, for enough
   // workgroups to fill the chip; many rows: four rows a wave, x reused more.
   if (rows < 8192) return launch<BITS, 2, 2>(packed, scales, zeros, rows, cols, G, gr, x, y, stream);
@@ -260,8 +269,9 @@ bool dequant_gemv_supported(int64_t cols, int32_t bits, int32_t groupsize) {
   return groupsize == -1 || (groupsize > 0 && groupsize % 32 == 0);
 }
 
-hipError_t dequant_gemv(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
-                        int64_t cols, int32_t bits, int32_t groupsize, const float* x, float* y, hipStream_t stream) {
+template <typename XT>
+hipError_t dequant_gemv_x(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
+                          int64_t cols, int32_t bits, int32_t groupsize, const XT* x, float* y, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   // cols == 0 still launches: no runs, every y is written as 0
   const int64_t nrun = (cols + 31) / 32;
@@ -273,6 +283,15 @@ hipError_t dequant_gemv(const uint32_t* packed, const float* scales, const uint8
     case 4: return launch_bits<4>(packed, scales, zeros, rows, cols, G, gr, x, y, stream);
     default: return launch_bits<8>(packed, scales, zeros, rows, cols, G, gr, x, y, stream);
   }
+}
+
+hipError_t dequant_gemv(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
+                        int64_t cols, int32_t bits, int32_t groupsize, const void* x, bool x_bf16, float* y,
+                        hipStream_t stream) {
+  if (x_bf16)
+    return dequant_gemv_x(packed, scales, zeros, rows, cols, bits, groupsize, static_cast<const uint16_t*>(x), y,
+                          stream);
+  return dequant_gemv_x(packed, scales, zeros, rows, cols, bits, groupsize, static_cast<const float*>(x), y, stream);
 }
 
 }  // namespace gptq

@@ -90,8 +90,8 @@ def test_pack_argument_errors(bits, cols):
     assert g.lib().gptq_pack(FAKE, 4, cols, bits, FAKE, None) == g.GPTQ_EINVAL
 
 
-def _gemv(rows, cols, bits, groupsize, packed=FAKE, x=FAKE, y=FAKE):
-    return g.lib().gptq_dequant_gemv(packed, FAKE, FAKE, rows, cols, bits, groupsize, x, y, None)
+def _gemv(rows, cols, bits, groupsize, packed=FAKE, x=FAKE, y=FAKE, x_dtype=1):
+    return g.lib().gptq_dequant_gemv(packed, FAKE, FAKE, rows, cols, bits, groupsize, x, x_dtype, y, None)
 
 
 def test_dequant_gemv_argument_errors():
@@ -105,6 +105,7 @@ def test_dequant_gemv_argument_errors():
     assert _gemv(8, 256, 4, 128, packed=None) == g.GPTQ_EINVAL
     assert _gemv(8, 256, 4, 128, y=None) == g.GPTQ_EINVAL
     assert _gemv(8, 256, 4, 128, x=ctypes.c_void_p(0x1002)) == g.GPTQ_EINVAL  # misaligned
+    assert _gemv(8, 256, 4, 128, x_dtype=5) == g.GPTQ_EINVAL  # x dtype
     assert _gemv(0, 256, 4, 128, packed=None) == g.GPTQ_OK     # no rows: no work
 
 

@@ -15,7 +15,8 @@ u = 2^-24.
 import numpy as np
 import pytest
 
-from gpuhelp import say, to_dev, torch_dev
+from gpuhelp import bf16_dev, say, to_dev, torch_dev
+from post_weight_quantization_03_amd import synth
 from oracle import dequant_gemv_ref, pack_ref
 
 pytestmark = pytest.mark.gpu
@@ -52,21 +53,26 @@ def _bound(codes, scales, zeros, x, groupsize):
     return D * U32 * (mag @ np.abs(x.astype(np.float64)))
 
 
-def _gpu(packed, scales, zeros, bits, groupsize, x, rows):
+def _gpu(packed, scales, zeros, bits, groupsize, x, rows, x_bf16=False):
+    """x_bf16: x holds bf16 bit patterns (uint16) and goes to the device as bf16."""
     g = _lib()
     torch, dev = torch_dev()
     y = torch.full((rows,), float("nan"), dtype=torch.float32, device=dev)
     pk = to_dev(packed.view(np.int32)) if packed.size else torch.empty(packed.shape, dtype=torch.int32, device=dev)
-    g.gptq_dequant_gemv(pk, to_dev(scales), to_dev(zeros), bits, groupsize, to_dev(x), y)
+    xd = bf16_dev(x) if x_bf16 else to_dev(x)
+    g.gptq_dequant_gemv(pk, to_dev(scales), to_dev(zeros), bits, groupsize, xd, y)
     torch.cuda.synchronize()
     return y.cpu().numpy()
 
 
-def _check(rows, cols, bits, groupsize, seed):
+def _check(rows, cols, bits, groupsize, seed, x_bf16=False):
     codes, scales, zeros, x = _inputs(rows, cols, bits, groupsize, seed)
     packed = pack_ref(codes, bits)
+    if x_bf16:
+        xb = (x.view(np.uint32) >> 16).astype(np.uint16)  # bf16 activations (truncated recipe)
+        x = synth.bf16_to_f32(xb)
     y0 = dequant_gemv_ref(packed, scales, zeros, bits, groupsize, x, cols)
-    y = _gpu(packed, scales, zeros, bits, groupsize, x, rows)
+    y = _gpu(packed, scales, zeros, bits, groupsize, xb if x_bf16 else x, rows, x_bf16=x_bf16)
     err = np.abs(y.astype(np.float64) - y0)
     bound = _bound(codes, scales, zeros, x, groupsize)
     say(f"   max |err| {err.max(initial=0):.3e}  max err/bound {np.max(err / np.maximum(bound, 1e-300), initial=0):.3f}")
@@ -98,6 +104,14 @@ def _check(rows, cols, bits, groupsize, seed):
 def test_dequant_gemv_parity(rows, cols, bits, groupsize):
     say(f"dequant_gemv rows={rows} cols={cols} bits={bits} groupsize={groupsize}")
     _check(rows, cols, bits, groupsize, seed=rows * 31 + cols + bits)
+
+
+@pytest.mark.parametrize("rows,cols,bits,groupsize", [
+    (37, 4096, 4, 128), (8200, 512, 4, 128), (5, 1000, 4, -1), (9, 2080, 3, 32), (11, 1024, 2, 64), (6, 36, 8, -1),
+])
+def test_dequant_gemv_bf16_activations(rows, cols, bits, groupsize):
+    say(f"dequant_gemv bf16 x rows={rows} cols={cols} bits={bits} groupsize={groupsize}")
+    _check(rows, cols, bits, groupsize, seed=rows + cols, x_bf16=True)
 
 
 def test_dequant_gemv_reproducible():
