@@ -15,6 +15,8 @@ Modules
   pack_ref    LSB-first per-row bitstream packing and unpacking.
   gemv_ref    dequantization of packed codes and the product y = W^ x.
   hadamard_ref  the fixed randomised Hadamard rotation Q and W Q, Q^T H Q.
+  qep_ref     the error-propagation correction of W from full-precision and
+              quantized-model inputs, before GPTQ.
 
 Parity pins: every function here is checked in ``tests/test_oracle_*.py``
 against closed forms, the hand-worked 4x8 example in ``tests/golden``,
@@ -37,4 +39,5 @@ from .gptq_ref import (  # noqa: F401
 )
 from .pack_ref import pack_ref, unpack_ref  # noqa: F401
 from .gemv_ref import dequant_gemv_ref, dequant_ref  # noqa: F401
+from .qep_ref import cross_ref, qep_correct_ref, qep_quantize_ref  # noqa: F401
 from .hadamard_ref import hadamard_matrix, rotate_hessian_ref, rotate_rows_ref, rotation_ref  # noqa: F401
