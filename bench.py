@@ -213,6 +213,52 @@ def hadamard_measure(g, torch, Wd, n, dev, copies=6, rounds=3):
             "hessian_frac": bytes_h / us_h / 1e3 / PEAK_HBM_GBS}
 
 
+def qep_measure(g, torch, Xd, Wd, n, dev):
+    """The error-propagation correction on this layer, outside the timed step: the cross
+    term C = 2 X^T X^ over all tokens (X^ = X + 5 % noise stands in for the quantized
+    model's inputs) and the correction W' = W + alpha W (C - H) H_d^-1, which also leaves
+    H factored for the quantizer.  HIP events around each call."""
+    gen = torch.Generator(dev).manual_seed(3)
+    Xq = torch.empty_like(Xd)
+    for a in range(0, Xd.shape[0], 16384):  # bounded temporaries
+        xs = Xd[a:a + 16384].float()
+        Xq[a:a + 16384] = (xs + 0.05 * xs.std() * torch.randn(xs.shape, device=dev, generator=gen)).to(Xd.dtype)
+    del xs
+    H = torch.zeros((n, n), dtype=torch.float32, device=dev)
+    C = torch.zeros((n, n), dtype=torch.float32, device=dev)
+    ws_h = torch.empty(max(g.gptq_hessian_workspace_bytes(n, Xd.shape[0], g.GPTQ_BF16), 1), dtype=torch.uint8,
+                       device=dev)
+    ws_c = torch.empty(g.gptq_cross_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(g.gptq_qep_workspace_bytes(Wd.shape[0], n), dtype=torch.uint8, device=dev)
+    Wout = torch.empty((Wd.shape[0], n), dtype=torch.float32, device=dev)
+    dst = torch.zeros((1,), dtype=torch.int32, device=dev)
+    times = {"cross": [], "correct": []}
+    for rep in range(3):
+        H.zero_()
+        C.zero_()
+        g.gptq_accumulate_hessian(H, Xq, workspace=ws_h)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        g.gptq_accumulate_cross(C, Xd, Xq, workspace=ws_c)
+        e[1].record()
+        g.gptq_qep_correct(Wd, C, H, 0.5, W_out=Wout, workspace=ws_q, d_status=dst)
+        e[2].record()
+        torch.cuda.synchronize()
+        if rep:
+            times["cross"].append(e[0].elapsed_time(e[1]))
+            times["correct"].append(e[1].elapsed_time(e[2]))
+    if int(dst.item()) != 0:
+        raise SystemExit(f"qep correction status {int(dst.item())}")
+    t_c = float(np.mean(times["cross"])) / 1e3
+    t_q = float(np.mean(times["correct"])) / 1e3
+    N = Xd.shape[0]
+    flop_c = 2.0 * N * n * n
+    return {"kernels": "hipBLASLt bf16 GEMM (cross term); factor + k_gemm_f32 x3 (correction)",
+            "tokens": N, "alpha": 0.5, "cross_ms": t_c * 1e3, "cross_tflops": flop_c / t_c / 1e12,
+            "cross_frac_bf16_peak": flop_c / t_c / 1e12 / PEAK_BF16_TFLOPS,
+            "correct_ms_incl_factor": t_q * 1e3}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -321,6 +367,7 @@ def main():
         "input_generation_s": gen_s,
     }
     rec["hadamard_rotation"] = hadamard_measure(g, torch, Wd, cols, dev)
+    rec["qep_correction"] = qep_measure(g, torch, Xd, Wd, cols, dev)
     rec["dequant_gemv"] = gemv_measure(g, torch, packed, scales, zeros, rows, cols, bits, wl.groupsize, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(W_bits, X_bits, rows, cols, tokens, bits, args)

@@ -14,7 +14,9 @@
  * Conventions for every call
  *   - Tensor pointers are DEVICE pointers owned by the caller.  Row-major.
  *   - Work is queued on `stream` in order; calls return before the GPU is done
- *     unless stated otherwise.  The library never allocates or frees memory.
+ *     unless stated otherwise.  The library allocates and frees no memory,
+ *     except the per-device hipBLASLt handle that gptq_accumulate_cross
+ *     creates on its first call on a device.
  *   - Return 0 (GPTQ_OK) on success, a positive gptq_status otherwise.
  *     Argument errors are detected on the host and return before any launch.
  *   - Calls that share a workspace or an output buffer on one device must not
@@ -183,6 +185,49 @@ int gptq_hadamard_rows(const void* in, gptq_dtype in_dtype, int64_t ld_in, float
  * gptq_accumulate_hessian).  The result is written in full and exactly
  * symmetric (the lower triangle mirrors the upper).  No workspace. */
 int gptq_hadamard_hessian(float* H, int64_t n, const float* signs, int32_t block, gptq_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Error-propagation correction before GPTQ: the QEP idea on the OneComp pages
+ * (the error that quantizing earlier layers leaves in a layer's inputs is
+ * carried into that layer's correction), read as the ridge fit of the
+ * full-precision outputs from the quantized-model inputs.  With X [tokens, n]
+ * the layer's inputs in the full-precision model and Xq those in the partly
+ * quantized one:
+ *   H = 2 Xq^T Xq (gptq_accumulate_hessian on Xq),
+ *   C = 2 X^T Xq  (gptq_accumulate_cross),
+ *   W' = W + alpha W G H_d^-1, G = C - H = 2 (X - Xq)^T Xq, H_d = H damped as
+ *        in gptq_quantize_layer (same lambda, same dead-column rule)
+ *        (gptq_qep_correct),
+ * then gptq_quantize_layer(W', H, flags = GPTQ_H_IS_FACTOR): the correction
+ * leaves H holding the factor.  alpha = 1 minimises
+ *   ||X W^T - Xq W'^T||^2 + (lambda / 2) ||W' - W||^2;  alpha = 0 is plain GPTQ.
+ * ------------------------------------------------------------------------- */
+
+/* Workspace bytes for gptq_accumulate_cross (hipBLASLt's, a fixed 64 MiB). */
+size_t gptq_cross_workspace_bytes(int64_t n);
+
+/* C[n, n] += 2 X^T Xq over one chunk of tokens.  X and Xq: [tokens, n], the same
+ * dtype (bf16 or fp32) and row stride ldx >= n.  C is fp32, not symmetric; the
+ * caller zero-fills it before the first chunk.  One plain GEMM through
+ * hipBLASLt (bf16 products exact, fp32 accumulation).  The first call on a
+ * device creates that device's hipBLASLt handle, which holds its own memory
+ * until the process ends.  tokens == 0 or n == 0: no work. */
+int gptq_accumulate_cross(float* C, int64_t n, const void* X, const void* Xq, gptq_dtype x_dtype, int64_t tokens,
+                          int64_t ldx, void* workspace, size_t workspace_bytes, gptq_stream_t stream);
+
+size_t gptq_qep_workspace_bytes(int64_t rows, int64_t cols);
+
+/* W_out[rows, cols] (fp32) = W + alpha W (C - H) H_d^-1 for W (bf16 or fp32,
+ * row stride cols), C and H as accumulated above (both [cols, cols] fp32).
+ * On return C holds G = C - H and H holds the factor U and the dead flags,
+ * exactly as gptq_quantize_layer leaves them, for a following
+ * gptq_quantize_layer with GPTQ_H_IS_FACTOR.  alpha in [0, 1], damp >= 0.
+ * d_status as in gptq_quantize_layer (GPTQ_ENOTPD when H_d is not positive
+ * definite; W_out then unspecified).  Workspace: gptq_qep_workspace_bytes,
+ * 256-byte aligned.  W_out must not alias W, C, H or the workspace. */
+int gptq_qep_correct(const void* W, gptq_dtype w_dtype, int64_t rows, int64_t cols, float* C, float* H, float damp,
+                     float alpha, float* W_out, void* workspace, size_t workspace_bytes, int32_t* d_status,
+                     gptq_stream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* gptq_status_string(int status);

@@ -79,6 +79,15 @@ def lib():
     L.gptq_hadamard_rows.restype = ctypes.c_int
     L.gptq_hadamard_hessian.argtypes = [vp, i64, vp, i32, vp]
     L.gptq_hadamard_hessian.restype = ctypes.c_int
+    L.gptq_cross_workspace_bytes.argtypes = [i64]
+    L.gptq_cross_workspace_bytes.restype = sz
+    L.gptq_accumulate_cross.argtypes = [vp, i64, vp, vp, ctypes.c_int, i64, i64, vp, sz, vp]
+    L.gptq_accumulate_cross.restype = ctypes.c_int
+    L.gptq_qep_workspace_bytes.argtypes = [i64, i64]
+    L.gptq_qep_workspace_bytes.restype = sz
+    L.gptq_qep_correct.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, ctypes.c_float, ctypes.c_float, vp, vp, sz,
+                                   vp, vp]
+    L.gptq_qep_correct.restype = ctypes.c_int
     L.gptq_status_string.argtypes = [ctypes.c_int]
     L.gptq_status_string.restype = ctypes.c_char_p
     L.gptq_version.argtypes = []
@@ -241,6 +250,51 @@ def gptq_hadamard_hessian(H, signs, block: int, stream=None):
     if st:
         raise GptqError(st, "gptq_hadamard_hessian")
     return H
+
+
+def gptq_cross_workspace_bytes(n: int) -> int:
+    return int(lib().gptq_cross_workspace_bytes(n))
+
+
+def gptq_accumulate_cross(C, X, Xq, workspace=None, stream=None):
+    """C [n, n] fp32 += 2 X^T Xq for X, Xq [tokens, n] (same dtype, unit column stride, same row stride)."""
+    _check_dev(C)
+    n = C.shape[0]
+    torch = _torch()
+    if (C.dtype != torch.float32 or C.shape != (n, n) or X.shape != Xq.shape or X.shape[1] != n
+            or X.dtype != Xq.dtype or X.stride() != Xq.stride() or X.stride(1) != 1 or not X.is_cuda
+            or not Xq.is_cuda):
+        raise ValueError("shape, dtype or stride mismatch")
+    if workspace is None:
+        workspace = _workspace(gptq_cross_workspace_bytes(n), C)
+    st = lib().gptq_accumulate_cross(_ptr(C), n, _ptr(X), _ptr(Xq), _dtype_code(X), X.shape[0], X.stride(0),
+                                     _ptr(workspace), workspace.numel(), _stream(stream))
+    if st:
+        raise GptqError(st, "gptq_accumulate_cross")
+    return C
+
+
+def gptq_qep_workspace_bytes(rows: int, cols: int) -> int:
+    return int(lib().gptq_qep_workspace_bytes(rows, cols))
+
+
+def gptq_qep_correct(W, C, H, alpha: float, damp: float = 0.01, W_out=None, workspace=None, d_status=None,
+                     stream=None):
+    """W_out = W + alpha W (C - H) H_d^-1; afterwards C holds C - H and H the factor (for GPTQ_H_IS_FACTOR)."""
+    _check_dev(W, C, H, W_out, d_status)
+    torch = _torch()
+    rows, cols = W.shape
+    if C.shape != (cols, cols) or H.shape != (cols, cols) or C.dtype != torch.float32 or H.dtype != torch.float32:
+        raise ValueError("shape or dtype mismatch")
+    if W_out is None:
+        W_out = torch.empty((rows, cols), dtype=torch.float32, device=W.device)
+    if workspace is None:
+        workspace = _workspace(gptq_qep_workspace_bytes(rows, cols), W)
+    st = lib().gptq_qep_correct(_ptr(W), _dtype_code(W), rows, cols, _ptr(C), _ptr(H), damp, alpha, _ptr(W_out),
+                                _ptr(workspace), workspace.numel(), _ptr(d_status), _stream(stream))
+    if st:
+        raise GptqError(st, "gptq_qep_correct")
+    return W_out
 
 
 def quantize(W, H, params: Params, stream=None, want_what=True):

@@ -33,7 +33,8 @@ def build_gptq() -> str:
     srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
     out = os.path.join(PKG, "libgptq.so")
     tmp = out + ".tmp"
-    _run([HIPCC, *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp])
+    _run([HIPCC, *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp, "-L/opt/rocm/lib",
+          "-lhipblaslt"])
     os.replace(tmp, out)
     return out
 

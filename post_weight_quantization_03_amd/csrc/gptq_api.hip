@@ -222,4 +222,82 @@ int gptq_hadamard_hessian(float* H, int64_t n, const float* signs, int32_t block
   return hadamard_hessian(H, n, signs, block, (hipStream_t)stream) == hipSuccess ? GPTQ_OK : GPTQ_EHIP;
 }
 
+size_t gptq_cross_workspace_bytes(int64_t n) {
+  if (n <= 0 || n > MAX_DIM) return 0;
+  return cross_workspace(n);
+}
+
+int gptq_accumulate_cross(float* C, int64_t n, const void* X, const void* Xq, gptq_dtype x_dtype, int64_t tokens,
+                          int64_t ldx, void* workspace, size_t workspace_bytes, gptq_stream_t stream) {
+  if (n < 0 || tokens < 0 || n > MAX_DIM || tokens > MAX_DIM) return GPTQ_EINVAL;
+  if (!(x_dtype == GPTQ_BF16 || x_dtype == GPTQ_F32)) return GPTQ_EINVAL;
+  if (n == 0 || tokens == 0) return GPTQ_OK;
+  if (!C || !X || !Xq || ldx < n) return GPTQ_EINVAL;
+  if (workspace_bytes < cross_workspace(n) || !workspace) return GPTQ_EWORKSPACE;
+  return cross_launch(C, n, X, Xq, x_dtype == GPTQ_BF16, tokens, ldx, workspace, workspace_bytes,
+                      (hipStream_t)stream);
+}
+
+namespace {
+struct QepLayout {
+  size_t status, lam, dead, A, Lt, P1, P2, total;
+};
+QepLayout qep_layout(int64_t rows, int64_t cols) {
+  QepLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  L.status = take(4 * sizeof(int));
+  L.lam = take(sizeof(float));
+  L.dead = take((size_t)cols);
+  L.A = take((size_t)cols * cols * sizeof(float));
+  L.Lt = take(factor_scratch_floats(cols) * sizeof(float));
+  L.P1 = take((size_t)rows * cols * sizeof(float));
+  L.P2 = take((size_t)rows * cols * sizeof(float));
+  L.total = off;
+  return L;
+}
+}  // namespace
+
+size_t gptq_qep_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0 || rows > MAX_DIM || cols > MAX_DIM) return 0;
+  return qep_layout(rows, cols).total;
+}
+
+int gptq_qep_correct(const void* W, gptq_dtype w_dtype, int64_t rows, int64_t cols, float* C, float* H, float damp,
+                     float alpha, float* W_out, void* workspace, size_t workspace_bytes, int32_t* d_status,
+                     gptq_stream_t stream_) {
+  hipStream_t stream = (hipStream_t)stream_;
+  if (rows < 0 || cols < 0 || rows > MAX_DIM || cols > MAX_DIM) return GPTQ_EINVAL;
+  if (!(w_dtype == GPTQ_BF16 || w_dtype == GPTQ_F32)) return GPTQ_EINVAL;
+  if (!(damp >= 0.0f) || !(damp < INFINITY) || !(alpha >= 0.0f) || !(alpha <= 1.0f)) return GPTQ_EINVAL;
+  if (rows == 0 || cols == 0) return GPTQ_OK;
+  if (!W || !C || !H || !W_out || !workspace) return GPTQ_EINVAL;
+  if (cols > 65535 * 4 || rows > INT32_MAX || rows * cols > ((int64_t)1 << 40)) return GPTQ_EUNSUPPORTED;
+  const QepLayout L = qep_layout(rows, cols);
+  if (workspace_bytes < L.total) return GPTQ_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return GPTQ_EINVAL;
+  char* ws = static_cast<char*>(workspace);
+  int* status = reinterpret_cast<int*>(ws + L.status);
+  FactorWs f{};
+  f.status = status;
+  f.lam = reinterpret_cast<float*>(ws + L.lam);
+  f.dead = reinterpret_cast<uint8_t*>(ws + L.dead);
+  f.A = reinterpret_cast<float*>(ws + L.A);
+  f.Lt = reinterpret_cast<float*>(ws + L.Lt);
+  if (fill_i32(status, 1, GPTQ_OK, stream) != hipSuccess) return GPTQ_EHIP;
+  if (qep_correct_run(W, w_dtype == GPTQ_BF16, rows, cols, C, H, damp, alpha, W_out, f,
+                      reinterpret_cast<float*>(ws + L.P1), reinterpret_cast<float*>(ws + L.P2), f.A,
+                      stream) != hipSuccess)
+    return GPTQ_EHIP;
+  if (d_status) return copy_status(status, d_status, stream) == hipSuccess ? GPTQ_OK : GPTQ_EHIP;
+  int host = 0;
+  if (hipMemcpyAsync(&host, status, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess) return GPTQ_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return GPTQ_EHIP;
+  return host;
+}
+
 }  // extern "C"

@@ -26,7 +26,8 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == {"gptq_hessian_workspace_bytes", "gptq_accumulate_hessian",
                           "gptq_quantize_workspace_bytes", "gptq_quantize_layer", "gptq_pack",
                           "gptq_dequant_gemv", "gptq_hadamard_rows", "gptq_hadamard_hessian",
-                          "gptq_status_string", "gptq_version"}
+                          "gptq_cross_workspace_bytes", "gptq_accumulate_cross", "gptq_qep_workspace_bytes",
+                          "gptq_qep_correct", "gptq_status_string", "gptq_version"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -124,6 +125,27 @@ def test_hadamard_argument_errors():
     assert L.gptq_hadamard_hessian(FAKE, 100, FAKE, 8, None) == g.GPTQ_EINVAL                        # 8 !| 100
     assert L.gptq_hadamard_hessian(None, 128, FAKE, 8, None) == g.GPTQ_EINVAL
     assert L.gptq_hadamard_hessian(None, 0, None, 1, None) == g.GPTQ_OK
+
+
+def test_qep_argument_errors():
+    L = g.lib()
+    F = g.GPTQ_F32
+    ws = L.gptq_cross_workspace_bytes(256)
+    assert ws > 0
+    assert L.gptq_accumulate_cross(FAKE, 256, FAKE, FAKE, 7, 10, 256, FAKE, ws, None) == g.GPTQ_EINVAL   # dtype
+    assert L.gptq_accumulate_cross(FAKE, 256, FAKE, FAKE, F, 10, 128, FAKE, ws, None) == g.GPTQ_EINVAL   # ldx < n
+    assert L.gptq_accumulate_cross(FAKE, 256, FAKE, None, F, 10, 256, FAKE, ws, None) == g.GPTQ_EINVAL
+    assert L.gptq_accumulate_cross(FAKE, 256, FAKE, FAKE, F, 10, 256, FAKE, 16, None) == g.GPTQ_EWORKSPACE
+    assert L.gptq_accumulate_cross(FAKE, 256, FAKE, FAKE, F, 0, 256, None, 0, None) == g.GPTQ_OK         # no tokens
+    need = L.gptq_qep_workspace_bytes(64, 256)
+    assert need >= 2 * 64 * 256 * 4 + 256 * 256 * 4
+    q = L.gptq_qep_correct
+    assert q(FAKE, F, 64, 256, FAKE, FAKE, 0.01, 1.5, FAKE, FAKE, need, None, None) == g.GPTQ_EINVAL      # alpha > 1
+    assert q(FAKE, F, 64, 256, FAKE, FAKE, -0.1, 0.5, FAKE, FAKE, need, None, None) == g.GPTQ_EINVAL      # damp < 0
+    assert q(FAKE, 9, 64, 256, FAKE, FAKE, 0.01, 0.5, FAKE, FAKE, need, None, None) == g.GPTQ_EINVAL      # dtype
+    assert q(FAKE, F, 64, 256, FAKE, None, 0.01, 0.5, FAKE, FAKE, need, None, None) == g.GPTQ_EINVAL
+    assert q(FAKE, F, 64, 256, FAKE, FAKE, 0.01, 0.5, FAKE, FAKE, need - 1, None, None) == g.GPTQ_EWORKSPACE
+    assert q(None, F, 0, 256, None, None, 0.01, 0.5, None, None, 0, None, None) == g.GPTQ_OK              # no rows
 
 
 def test_product_path_has_no_oracle_import():

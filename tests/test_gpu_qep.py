@@ -1,0 +1,176 @@
+"""GPU parity of the error-propagation correction (cross term, correction, then GPTQ).
+
+Inputs: X from the seeded activation generator (bf16 or fp32), and the
+quantized-model inputs X^ = X + 5 % noise (seeded), rounded to the same dtype.
+
+Gates:
+  cross term C = 2 X^T X^  relative Frobenius error <= 1e-4 (the Hessian's gate;
+                           bf16 products are exact, accumulation is fp32);
+  correction dW = W' - W   relative Frobenius error <= 1e-4 against the oracle's,
+                           which solves with H_d in fp64 while the GPU applies the
+                           fp32 factor twice after an fp32 product with G (each
+                           within ~1e-5; measured up to 2e-5 at 1024 columns);
+  the factor left in H     relative Frobenius error <= 1e-4 (the factor gate);
+  the quantized layer      every quantize gate, against the oracle's GPTQ of the
+                           oracle's own corrected W.
+"""
+
+import numpy as np
+import pytest
+
+from gpuhelp import bf16_dev, check_quantize, say, to_dev, torch_dev
+from oracle import cross_ref, damp_ref, factor_ref, hessian_ref, qep_correct_ref
+from post_weight_quantization_03_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import post_weight_quantization_03_amd as g
+    g.lib()
+    return g
+
+
+def _inputs(n, tokens, bf16, seed=11):
+    X = synth.Activations(seed=seed, tensor=synth.T_X, n=n, tokens=tokens, dist=synth.STUDENT_T4,
+                          outliers=max(1, n // 100), outlier_factor=20.0, bf16=bf16).full()
+    Xf = synth.bf16_to_f32(X) if bf16 else X
+    rng = np.random.default_rng(seed + 1)
+    sig = np.sqrt(np.mean(Xf.astype(np.float64) ** 2, axis=0))
+    Xq = (Xf + 0.05 * sig * rng.standard_normal(Xf.shape)).astype(np.float32)
+    if bf16:
+        Xq_bits = (Xq.view(np.uint32) >> 16).astype(np.uint16)  # truncated to bf16: an input recipe
+        return X, Xq_bits, Xf.astype(np.float64), synth.bf16_to_f32(Xq_bits).astype(np.float64)
+    return X, Xq, Xf.astype(np.float64), Xq.astype(np.float64)
+
+
+def _dev(a, bf16):
+    return bf16_dev(a) if bf16 else to_dev(a)
+
+
+def _gpu_hc(X, Xq, n, bf16, chunks=1):
+    g = _lib()
+    torch, dev = torch_dev()
+    H = torch.zeros((n, n), dtype=torch.float32, device=dev)
+    C = torch.zeros((n, n), dtype=torch.float32, device=dev)
+    Xd, Xqd = _dev(X, bf16), _dev(Xq, bf16)
+    bounds = np.linspace(0, X.shape[0], chunks + 1).astype(int)
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        g.gptq_accumulate_hessian(H, Xqd[a:b])
+        g.gptq_accumulate_cross(C, Xd[a:b], Xqd[a:b])
+    torch.cuda.synchronize()
+    return H, C
+
+
+def _rel(a, b):
+    return np.linalg.norm(a - b) / np.linalg.norm(b)
+
+
+@pytest.mark.parametrize("n,tokens,bf16,chunks", [(256, 1000, True, 1), (300, 777, False, 2), (1024, 4096, True, 3)])
+def test_cross_parity(n, tokens, bf16, chunks):
+    say(f"cross term n={n} tokens={tokens} bf16={bf16} chunks={chunks}")
+    X, Xq, X64, Xq64 = _inputs(n, tokens, bf16)
+    _, C = _gpu_hc(X, Xq, n, bf16, chunks)
+    ref = cross_ref([(X64, Xq64)], n)
+    rel = _rel(C.cpu().numpy().astype(np.float64), ref)
+    say(f"   rel Frobenius {rel:.3e}")
+    assert rel <= 1e-4
+
+
+def test_cross_q_proj_full_width_sampled():
+    """n = 4096 over 65536 bf16 tokens, sampled entries against fp64 column dot products."""
+    n, tokens = 4096, 65536
+    say(f"cross term n={n} tokens={tokens} bf16, sampled entries")
+    X, Xq, X64, Xq64 = _inputs(n, tokens, True, seed=21)
+    _, C = _gpu_hc(X, Xq, n, True)
+    Cn = C.cpu().numpy()
+    rng = np.random.default_rng(4)
+    idx = np.r_[0, n - 1, 127, 128, rng.integers(0, n, size=60)]
+    for i in idx[:32]:
+        for j in idx[32:]:
+            ref = 2.0 * X64[:, i] @ Xq64[:, j]
+            scale = 2.0 * np.sqrt((X64[:, i] @ X64[:, i]) * (Xq64[:, j] @ Xq64[:, j]))
+            assert abs(Cn[i, j] - ref) <= 2e-5 * scale, (i, j)
+
+
+@pytest.mark.parametrize("rows,n,alpha,wbf16", [(64, 256, 1.0, False), (37, 300, 0.5, True), (128, 1024, 0.7, True)])
+def test_qep_correct_parity(rows, n, alpha, wbf16):
+    say(f"qep correct rows={rows} n={n} alpha={alpha} wbf16={wbf16}")
+    g = _lib()
+    torch, dev = torch_dev()
+    X, Xq, X64, Xq64 = _inputs(n, 4 * n, True, seed=n)
+    H, C = _gpu_hc(X, Xq, n, True)
+    rng = np.random.default_rng(rows)
+    W = (0.02 * rng.standard_normal((rows, n))).astype(np.float32)
+    if wbf16:
+        Wb = (W.view(np.uint32) >> 16).astype(np.uint16)
+        W64 = synth.bf16_to_f32(Wb).astype(np.float64)
+        Wd = bf16_dev(Wb)
+    else:
+        W64 = W.astype(np.float64)
+        Wd = to_dev(W)
+    Wout = g.gptq_qep_correct(Wd, C, H, alpha)
+    torch.cuda.synchronize()
+    H_ref = hessian_ref([Xq64], n)
+    C_ref = cross_ref([(X64, Xq64)], n)
+    ref = qep_correct_ref(W64, H_ref, C_ref, alpha)
+    dW = Wout.cpu().numpy().astype(np.float64) - W64
+    rel = _rel(dW, ref - W64)
+    say(f"   correction rel Frobenius {rel:.3e}  (|dW| / |W| = {np.linalg.norm(ref - W64) / np.linalg.norm(W64):.3e})")
+    assert rel <= 1e-4
+    # H now holds the factor of the damped H^
+    U = factor_ref(damp_ref(H_ref, W64, 0.01)[0])
+    relu = _rel(np.triu(H.cpu().numpy().astype(np.float64)), U)
+    say(f"   factor rel Frobenius {relu:.3e}")
+    assert relu <= 1e-4
+
+
+def test_qep_zero_strength_is_identity():
+    say("qep correct alpha = 0")
+    g = _lib()
+    torch, dev = torch_dev()
+    X, Xq, _, _ = _inputs(256, 1000, True)
+    H, C = _gpu_hc(X, Xq, 256, True)
+    W = (0.02 * np.random.default_rng(1).standard_normal((16, 256))).astype(np.float32)
+    Wout = g.gptq_qep_correct(to_dev(W), C, H, 0.0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(Wout.cpu().numpy(), W)
+
+
+def test_qep_then_gptq_end_to_end():
+    """Correct and quantize on the GPU (the factor reused) against the oracle's GPTQ of its own
+    corrected W: 256 x 512, 4-bit g128, alpha 0.5."""
+    say("qep + gptq 256x512 4-bit g128 alpha=0.5")
+    g = _lib()
+    torch, dev = torch_dev()
+    rows, n = 256, 512
+    X, Xq, X64, Xq64 = _inputs(n, 2048, True, seed=5)
+    H, C = _gpu_hc(X, Xq, n, True)
+    W = (0.02 * np.random.default_rng(2).standard_normal((rows, n))).astype(np.float32)
+    Wout = g.gptq_qep_correct(to_dev(W), C, H, 0.5)
+    out = g.quantize(Wout, H, g.Params(bits=4, groupsize=128, flags=g.GPTQ_H_IS_FACTOR))
+    torch.cuda.synchronize()
+    o = {k: v.cpu().numpy() for k, v in out.items() if v is not None}
+    H_ref = hessian_ref([Xq64], n)
+    Wc = qep_correct_ref(W.astype(np.float64), H_ref, cross_ref([(X64, Xq64)], n), 0.5)
+    check_quantize(Wc, H_ref.astype(np.float32), 4, 128, o)
+
+
+def test_qep_correct_q_proj_full_size():
+    """The q_proj shape (4096 x 4096, bf16 W), in the launch configuration the benchmark
+    times; H and C from 16384 tokens (the correction's launches do not depend on tokens)."""
+    say("qep correct q_proj 4096x4096 alpha=0.5")
+    g = _lib()
+    torch, dev = torch_dev()
+    n = 4096
+    X, Xq, X64, Xq64 = _inputs(n, 16384, True, seed=31)
+    H, C = _gpu_hc(X, Xq, n, True)
+    wl = synth.workload("q_proj_4096", tokens=64)
+    W_bits = wl.linears[0].weight()
+    W64 = synth.bf16_to_f32(W_bits).astype(np.float64)
+    Wout = g.gptq_qep_correct(bf16_dev(W_bits), C, H, 0.5)
+    torch.cuda.synchronize()
+    ref = qep_correct_ref(W64, hessian_ref([Xq64], n), cross_ref([(X64, Xq64)], n), 0.5)
+    rel = _rel(Wout.cpu().numpy().astype(np.float64) - W64, ref - W64)
+    say(f"   correction rel Frobenius {rel:.3e}")
+    assert rel <= 1e-4
