@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens in the oracle's Hessian sample")
     ap.add_argument("--cpu-rows", type=int, default=512, help="rows in the oracle's quantize sample")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the measurements outside the timed step (GEMV, rotation, error-propagation correction)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -366,9 +368,10 @@ def main():
                      "algorithmic_bytes": alg["x_bytes"] + 4.0 * cols * cols},
         "input_generation_s": gen_s,
     }
-    rec["hadamard_rotation"] = hadamard_measure(g, torch, Wd, cols, dev)
-    rec["qep_correction"] = qep_measure(g, torch, Xd, Wd, cols, dev)
-    rec["dequant_gemv"] = gemv_measure(g, torch, packed, scales, zeros, rows, cols, bits, wl.groupsize, dev)
+    if not args.no_extras:
+        rec["hadamard_rotation"] = hadamard_measure(g, torch, Wd, cols, dev)
+        rec["qep_correction"] = qep_measure(g, torch, Xd, Wd, cols, dev)
+        rec["dequant_gemv"] = gemv_measure(g, torch, packed, scales, zeros, rows, cols, bits, wl.groupsize, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(W_bits, X_bits, rows, cols, tokens, bits, args)
     print(json.dumps(rec), flush=True)
