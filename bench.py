@@ -369,9 +369,21 @@ def main():
         "input_generation_s": gen_s,
     }
     if not args.no_extras:
-        rec["hadamard_rotation"] = hadamard_measure(g, torch, Wd, cols, dev)
-        rec["qep_correction"] = qep_measure(g, torch, Xd, Wd, cols, dev)
-        rec["dequant_gemv"] = gemv_measure(g, torch, packed, scales, zeros, rows, cols, bits, wl.groupsize, dev)
+        # measurements outside the timed step; a failure is reported in its field and
+        # does not take the step's line with it
+        extras = {
+            "hadamard_rotation": lambda: hadamard_measure(g, torch, Wd, cols, dev),
+            "qep_correction": lambda: qep_measure(g, torch, Xd, Wd, cols, dev),
+            "dequant_gemv": lambda: gemv_measure(g, torch, packed, scales, zeros, rows, cols, bits, wl.groupsize,
+                                                 dev),
+        }
+        for name, fn in extras.items():
+            try:
+                rec[name] = fn()
+            except Exception as ex:  # noqa: BLE001
+                rec[name] = {"error": f"{type(ex).__name__}: {ex}"}
+                print(f"bench.py: {name} failed: {ex}", file=sys.stderr)
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(W_bits, X_bits, rows, cols, tokens, bits, args)
     print(json.dumps(rec), flush=True)
