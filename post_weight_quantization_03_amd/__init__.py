@@ -232,7 +232,10 @@ def gptq_hadamard_rows(inp, signs, block: int, out=None, stream=None):
             or signs.dtype != torch.float32 or signs.shape != (n,)):
         raise ValueError("shape or dtype mismatch")
     _check_dev(signs)
-    st = lib().gptq_hadamard_rows(_ptr(inp), _dtype_code(inp), inp.stride(0), _ptr(out), out.stride(0), rows, n,
+    # a one-row tensor may carry any stride on its first axis (NumPy gives 0 for x[None, :])
+    ld_in = inp.stride(0) if rows > 1 else n
+    ld_out = out.stride(0) if rows > 1 else n
+    st = lib().gptq_hadamard_rows(_ptr(inp), _dtype_code(inp), ld_in, _ptr(out), ld_out, rows, n,
                                   _ptr(signs), block, _stream(stream))
     if st:
         raise GptqError(st, "gptq_hadamard_rows")
