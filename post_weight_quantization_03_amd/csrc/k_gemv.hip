@@ -116,15 +116,16 @@ __device__ __forceinline__ float run_dot(const uint32_t (&w)[BITS], const float 
 constexpr int XCH = 128;
 constexpr int XP = 36;
 
-// Template: R rows per wave, S waves share a row group (column slices).
-// gr = runs per group (any value above the last run when the row is one group).
-template <int BITS, int R, int S, typename XT>
-__global__ __launch_bounds__(256) void k_dequant_gemv(const uint32_t* __restrict__ packed,
+// Template: NW waves per workgroup, R rows per wave, S waves share a row group
+// (column slices).  gr = runs per group (any value above the last run when the
+// row is one group).
+template <int BITS, int R, int S, int NW, typename XT>
+__global__ __launch_bounds__(64 * NW) void k_dequant_gemv(const uint32_t* __restrict__ packed,
                                                       const float* __restrict__ scales,
                                                       const uint8_t* __restrict__ zeros, int64_t rows, int64_t cols,
                                                       int64_t G, uint32_t gr, const XT* __restrict__ x,
                                                       float* __restrict__ y) {
-  constexpr int RG = 4 / S;              // row groups per workgroup
+  constexpr int RG = NW / S;             // row groups per workgroup
   constexpr int IT = XCH / (64 * S);     // runs per lane per chunk
   static_assert(IT >= 1 && IT * 64 * S == XCH, "chunk must be whole lane sweeps");
   __shared__ __align__(16) float xs[XCH * XP];
@@ -178,8 +179,8 @@ __global__ __launch_bounds__(256) void k_dequant_gemv(const uint32_t* __restrict
   for (int64_t c0 = 0; c0 < nrun; c0 += XCH) {
     __syncthreads();  // the previous chunk's reads of xs are done
 #pragma unroll
-    for (int j = 0; j < XCH * 32 / 1024; ++j) {
-      const int e = 4 * (threadIdx.x + 256 * j);  // float index within the chunk
+    for (int j = 0; j < XCH * 32 / (256 * NW); ++j) {
+      const int e = 4 * (threadIdx.x + 64 * NW * j);  // float index within the chunk
       const int64_t col = 32 * c0 + e;
       // cols is a multiple of 4 (cols b is whole words), so a vector is all in or all out
       const f32x4 v = col < cols ? load_x4(x + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -242,13 +243,13 @@ __global__ __launch_bounds__(256) void k_dequant_gemv(const uint32_t* __restrict
   }
 }
 
-template <int BITS, int R, int S, typename XT>
+template <int BITS, int R, int S, int NW, typename XT>
 hipError_t launch(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows, int64_t cols,
                   int64_t G, uint32_t gr, const XT* x, float* y, hipStream_t stream) {
-  constexpr int64_t rows_per_wg = (4 / S) * R;
+  constexpr int64_t rows_per_wg = (NW / S) * R;
   const unsigned grid = (unsigned)((rows + rows_per_wg - 1) / rows_per_wg);
-  hipLaunchKernelGGL((k_dequant_gemv<BITS, R, S, XT>), dim3(grid), dim3(256), 0, stream, packed, scales, zeros, rows,
-                     cols, G, gr, x, y);
+  hipLaunchKernelGGL((k_dequant_gemv<BITS, R, S, NW, XT>), dim3(grid), dim3(64 * NW), 0, stream, packed, scales,
+                     zeros, rows, cols, G, gr, x, y);
   return hipGetLastError();
 }
 
@@ -256,9 +257,10 @@ template <int BITS, typename XT>
 hipError_t launch_bits(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows, int64_t cols,
                        int64_t G, uint32_t gr, const XT* x, float* y, hipStream_t stream) {
   // Few rows: two rows a wave and the columns split over two waves, for enough
-  // workgroups to fill the chip; many rows: four rows a wave, x reused more.
-  if (rows < 8192) return launch<BITS, 2, 2>(packed, scales, zeros, rows, cols, G, gr, x, y, stream);
-  return launch<BITS, 4, 1>(packed, scales, zeros, rows, cols, G, gr, x, y, stream);
+  // waves to fill the chip, eight waves a workgroup so one staging of x serves
+  // eight rows; many rows: four rows a wave, x reused more.
+  if (rows < 8192) return launch<BITS, 2, 2, 8>(packed, scales, zeros, rows, cols, G, gr, x, y, stream);
+  return launch<BITS, 4, 1, 4>(packed, scales, zeros, rows, cols, G, gr, x, y, stream);
 }
 
 }  // namespace
