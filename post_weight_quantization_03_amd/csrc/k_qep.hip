@@ -12,7 +12,8 @@
 // with the quantizer's own factor (H_d^-1 = U^T U, H then holds U exactly as
 // the quantizer leaves it, so the layer is quantized next with the factor
 // reused), and applies H_d^-1 as two triangular products with the library's
-// fp32 MFMA GEMM: W' = W + alpha ((W G) U^T) U.
+// fp32 MFMA GEMM: W' = W + alpha ((W G) U^T) U (the U^T product skips the
+// zero half of its K range).
 #include <hipblaslt/hipblaslt.h>
 
 #include <mutex>
@@ -144,12 +145,15 @@ hipError_t qep_correct_run(const void* W, bool w_bf16, int64_t rows, int64_t n, 
   g.alpha = 1.0f;
   g.beta = 0;
   if ((e = gemm_f32(g, stream)) != hipSuccess) return e;
-  // P2 = P1 U^T: B(k, j) = U[j][k] = T[j][k], n-major
+  // P2 = P1 U^T: B(k, j) = U[j][k] = T[j][k], n-major; U[j][k] = 0 for k < j, so a
+  // tile of columns from n0 on needs only k >= n0
   g.A = P1;
   g.B = T;
   g.b_kmajor = 0;
   g.C = P2;
+  g.klo_n = 1;
   if ((e = gemm_f32(g, stream)) != hipSuccess) return e;
+  g.klo_n = 0;
   // W_out += alpha P2 U: B(k, j) = U[k][j] = T[k][j], k-major
   g.A = P2;
   g.B = T;
