@@ -69,8 +69,8 @@ def parse():
 
 
 def algorithmic(rows, cols, tokens, bits):
-    """Algorithmic work of one step (SURVEY conventions: symmetric Hessian N n(n+1), factor 2n^3/3,
-    quantize rows*cols^2 of which trailing rows*cols*(cols-128))."""
+    """Algorithmic work of one step: the symmetric Hessian N n(n+1) flops, the factor 2n^3/3,
+    the quantize loop rows*cols^2 of which the trailing update rows*cols*(cols-128)."""
     hess = tokens * cols * (cols + 1)
     factor = 2.0 * cols ** 3 / 3.0
     quant = float(rows) * cols * cols
