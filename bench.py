@@ -155,9 +155,32 @@ def gemv_measure(g, torch, packed, scales, zeros, rows, cols, bits, groupsize, d
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (rounds * copies)
     gbs = alg_bytes / (us * 1e-6) / 1e9
+    # the same weights against a batch of 8 vectors (gptq_dequant_gemm)
+    B = 8
+    Xb = torch.randn(B, cols, dtype=torch.float32, device=dev, generator=torch.Generator(dev).manual_seed(2))
+    Yb = torch.empty(B, rows, dtype=torch.float32, device=dev)
+    fb = g.lib().gptq_dequant_gemm
+    bcalls = [(ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(s_.data_ptr()), ctypes.c_void_p(z.data_ptr()), rows,
+               cols, bits, groupsize, ctypes.c_void_p(Xb.data_ptr()), g.GPTQ_F32, cols, B,
+               ctypes.c_void_p(Yb.data_ptr()), rows, stream) for p, s_, z in bufs]
+    for a in bcalls:
+        if fb(*a):
+            raise RuntimeError("gptq_dequant_gemm failed")
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)
+    e0.record()
+    for _ in range(rounds):
+        for a in bcalls:
+            fb(*a)
+    e1.record()
+    torch.cuda.synchronize()
+    us_b = e0.elapsed_time(e1) * 1e3 / (rounds * copies)
+    bytes_b = alg_bytes + (B - 1) * (cols + rows) * 4
     return {"kernel": "k_dequant_gemv", "shape": [rows, cols], "bits": bits, "groupsize": groupsize,
             "us_per_launch": us, "algorithmic_bytes": alg_bytes, "achieved_GBs": gbs, "peak_GBs": PEAK_HBM_GBS,
-            "frac": gbs / PEAK_HBM_GBS, "weight_copies": copies}
+            "frac": gbs / PEAK_HBM_GBS, "weight_copies": copies,
+            "batch8": {"kernel": "k_dequant_gemm", "us_per_launch": us_b, "algorithmic_bytes": bytes_b,
+                       "achieved_GBs": bytes_b / (us_b * 1e-6) / 1e9, "us_per_vector": us_b / B}}
 
 
 def hadamard_measure(g, torch, Wd, n, dev, copies=6, rounds=3):

@@ -159,6 +159,16 @@ int gptq_dequant_gemv(const uint32_t* packed, const float* scales, const uint8_t
                       int64_t cols, int32_t bits, int32_t groupsize, const void* x, gptq_dtype x_dtype, float* y,
                       gptq_stream_t stream);
 
+/* The same product for a small batch: Y[t, :] = W^ X[t, :] for t < batch, with
+ * X [batch, cols] (row stride ldx >= cols, bf16 or fp32; for bf16 ldx even)
+ * and Y [batch, rows] fp32 (row stride ldy >= rows).  The codes are read once
+ * per group of up to 8 vectors.  Accumulation as in gptq_dequant_gemv; a batch
+ * of one gives exactly gptq_dequant_gemv's result.  batch == 0 or rows == 0:
+ * no work.  Y must not alias the inputs. */
+int gptq_dequant_gemm(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
+                      int64_t cols, int32_t bits, int32_t groupsize, const void* X, gptq_dtype x_dtype, int64_t ldx,
+                      int64_t batch, float* Y, int64_t ldy, gptq_stream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Fixed randomised Hadamard rotation, the untrained form of the rotation
  * preprocessing on the OneComp hub article (rotations absorbed into the

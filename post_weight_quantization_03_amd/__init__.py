@@ -75,6 +75,8 @@ def lib():
     L.gptq_pack.restype = ctypes.c_int
     L.gptq_dequant_gemv.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, vp, vp]
     L.gptq_dequant_gemv.restype = ctypes.c_int
+    L.gptq_dequant_gemm.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, i64, i64, vp, i64, vp]
+    L.gptq_dequant_gemm.restype = ctypes.c_int
     L.gptq_hadamard_rows.argtypes = [vp, ctypes.c_int, i64, vp, i64, i64, i64, vp, i32, vp]
     L.gptq_hadamard_rows.restype = ctypes.c_int
     L.gptq_hadamard_hessian.argtypes = [vp, i64, vp, i32, vp]
@@ -218,6 +220,27 @@ def gptq_dequant_gemv(packed, scales, zeros, bits: int, groupsize: int, x, y, st
     if st:
         raise GptqError(st, "gptq_dequant_gemv")
     return y
+
+
+def gptq_dequant_gemm(packed, scales, zeros, bits: int, groupsize: int, X, Y, stream=None):
+    """Y [batch, rows] fp32 = (W^ X^T)^T for X [batch, cols] bf16 or fp32 (unit column stride)."""
+    _check_dev(packed, scales, zeros, Y)
+    torch = _torch()
+    rows = packed.shape[0]
+    if X.dim() != 2 or not X.is_cuda or X.stride(1) != 1:
+        raise ValueError("X must be a 2-D device tensor with unit column stride")
+    batch, cols = X.shape
+    if (Y.dtype != torch.float32 or Y.shape != (batch, rows) or scales.dtype != torch.float32
+            or zeros.dtype != torch.uint8 or packed.dim() != 2 or packed.shape[1] * 32 != cols * bits
+            or packed.element_size() != 4 or scales.shape != zeros.shape or scales.shape[0] != rows):
+        raise ValueError("shape or dtype mismatch")
+    ldx = X.stride(0) if batch > 1 else cols
+    st = lib().gptq_dequant_gemm(_ptr(packed), _ptr(scales), _ptr(zeros), rows, cols, bits, groupsize, _ptr(X),
+                                 _dtype_code(X), ldx, batch, _ptr(Y), Y.stride(0) if batch > 1 else rows,
+                                 _stream(stream))
+    if st:
+        raise GptqError(st, "gptq_dequant_gemm")
+    return Y
 
 
 def gptq_hadamard_rows(inp, signs, block: int, out=None, stream=None):

@@ -107,6 +107,9 @@ bool dequant_gemv_supported(int64_t cols, int32_t bits, int32_t groupsize);
 hipError_t dequant_gemv(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
                         int64_t cols, int32_t bits, int32_t groupsize, const void* x, bool x_bf16, float* y,
                         hipStream_t stream);
+hipError_t dequant_gemm(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
+                        int64_t cols, int32_t bits, int32_t groupsize, const void* X, bool x_bf16, int64_t ldx,
+                        int64_t batch, float* Y, int64_t ldy, hipStream_t stream);
 
 // Fixed randomised Hadamard rotation (k_hadamard.hip).
 int64_t hadamard_chunks(int64_t n);

@@ -194,6 +194,27 @@ int gptq_dequant_gemv(const uint32_t* packed, const float* scales, const uint8_t
              : GPTQ_EHIP;
 }
 
+int gptq_dequant_gemm(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
+                      int64_t cols, int32_t bits, int32_t groupsize, const void* X, gptq_dtype x_dtype, int64_t ldx,
+                      int64_t batch, float* Y, int64_t ldy, gptq_stream_t stream) {
+  if (rows < 0 || cols < 0 || batch < 0 || rows > MAX_DIM || cols > MAX_DIM || batch > MAX_DIM) return GPTQ_EINVAL;
+  if (!(bits == 2 || bits == 3 || bits == 4 || bits == 8)) return GPTQ_EINVAL;
+  if (groupsize == 0 || groupsize < -1) return GPTQ_EINVAL;
+  if (x_dtype != GPTQ_BF16 && x_dtype != GPTQ_F32) return GPTQ_EINVAL;
+  if ((cols * bits) % 32 != 0) return GPTQ_EINVAL;
+  if (!dequant_gemv_supported(cols, bits, groupsize)) return GPTQ_EUNSUPPORTED;
+  if (rows == 0 || batch == 0) return GPTQ_OK;
+  if (ldx < cols || ldy < rows) return GPTQ_EINVAL;
+  if (!Y || (cols > 0 && (!packed || !scales || !zeros || !X))) return GPTQ_EINVAL;
+  auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) != 0; };
+  if (misaligned(packed) || misaligned(scales) || misaligned(X) || misaligned(Y)) return GPTQ_EINVAL;
+  if (x_dtype == GPTQ_BF16 && (ldx & 1)) return GPTQ_EINVAL;  // every row of X dword aligned
+  return dequant_gemm(packed, scales, zeros, rows, cols, bits, groupsize, X, x_dtype == GPTQ_BF16, ldx, batch, Y,
+                      ldy, (hipStream_t)stream) == hipSuccess
+             ? GPTQ_OK
+             : GPTQ_EHIP;
+}
+
 static bool hadamard_block_ok(int64_t n, int32_t block) {
   return block >= 1 && block <= 4096 && (block & (block - 1)) == 0 && n % block == 0;
 }

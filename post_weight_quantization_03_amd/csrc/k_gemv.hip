@@ -110,6 +110,46 @@ __device__ __forceinline__ float run_dot(const uint32_t (&w)[BITS], const float 
   return acc;
 }
 
+// A run's 32 codes as floats, in code order, scaled as run_dot scales them
+// (1 / code_unit() for 2 and 4 bits, exact otherwise).
+template <int BITS>
+__device__ __forceinline__ void run_codes(const uint32_t (&w)[BITS], float (&q)[32]) {
+  if constexpr (BITS == 8) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) q[4 * j + b] = byte_f(w[j], b);
+  } else if constexpr (BITS == 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = w[j] & 0x0f0f0f0fu, hi = (w[j] >> 4) & 0x0f0f0f0fu;
+      const auto l01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+      const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+      const auto l23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+      const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+      q[8 * j + 0] = l01[0]; q[8 * j + 1] = h01[0]; q[8 * j + 2] = l01[1]; q[8 * j + 3] = h01[1];
+      q[8 * j + 4] = l23[0]; q[8 * j + 5] = h23[0]; q[8 * j + 6] = l23[1]; q[8 * j + 7] = h23[1];
+    }
+  } else if constexpr (BITS == 2) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t c = (w[j] >> (2 * s)) & 0x03030303u;
+        const auto c01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);
+        const auto c23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, true);
+        q[16 * j + s] = c01[0]; q[16 * j + 4 + s] = c01[1]; q[16 * j + 8 + s] = c23[0]; q[16 * j + 12 + s] = c23[1];
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int bit = 3 * i, wi = bit >> 5, sh = bit & 31;
+      const uint32_t v = sh + 3 > 32 ? __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) : w[wi] >> sh;
+      q[i] = (float)(v & 7u);
+    }
+  }
+}
+
 // x goes through LDS in chunks of XCH runs, each run's 32 values in a row of XP
 // floats: the padding puts the rows of eight consecutive runs on different
 // banks, so the lanes' 16-byte reads of their runs do not collide.
@@ -263,6 +303,120 @@ hipError_t launch_bits(const uint32_t* packed, const float* scales, const uint8_
   return launch<BITS, 4, 1, 4>(packed, scales, zeros, rows, cols, G, gr, x, y, stream);
 }
 
+// Y[t, :] = W^ X[t, :] for a small batch of T activation vectors.  Same
+// layout as the single-vector kernel with R = 2, S = 1 and chunks of 64 runs:
+// a lane converts its run's codes to floats once and applies them to all T
+// vectors, staged together in LDS.
+constexpr int BCH = 64;
+
+template <int BITS, int T, typename XT>
+__global__ __launch_bounds__(256) void k_dequant_gemm(const uint32_t* __restrict__ packed,
+                                                      const float* __restrict__ scales,
+                                                      const uint8_t* __restrict__ zeros, int64_t rows, int64_t cols,
+                                                      int64_t G, uint32_t gr, const XT* __restrict__ X, int64_t ldx,
+                                                      float* __restrict__ Y, int64_t ldy) {
+  constexpr int R = 2;
+  __shared__ __align__(16) float xs[T][BCH * XP];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * R;
+  const int64_t wpr = cols * BITS / 32;
+  const int64_t nfull = cols / 32, nrun = (cols + 31) / 32;
+  const float unit = (BITS == 2 || BITS == 4) ? code_unit() : 1.0f;
+  const uint32_t* prow[R];
+  const float* srow[R];
+  const uint8_t* zrow[R];
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    const int64_t r = r0 + q < rows ? r0 + q : rows - 1;  // rows past the end repeat the last, unwritten
+    prow[q] = packed + r * wpr;
+    srow[q] = scales + r * G;
+    zrow[q] = zeros + r * G;
+  }
+  float yacc[T][R] = {};
+  for (int64_t c0 = 0; c0 < nrun; c0 += BCH) {
+    __syncthreads();  // the previous chunk's reads of xs are done
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int j = 0; j < BCH * 32 / 1024; ++j) {
+        const int e = 4 * (threadIdx.x + 256 * j);
+        const int64_t col = 32 * c0 + e;
+        // cols is a multiple of 4 (cols b is whole words), so a vector is all in or all out
+        const f32x4 v = col < cols ? load_x4(X + t * ldx + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        *reinterpret_cast<float4*>(&xs[t][(e >> 5) * XP + (e & 31)]) = make_float4(v.x, v.y, v.z, v.w);
+      }
+    __syncthreads();
+    const int64_t k = c0 + lane;
+    if (k < nrun) {
+      uint32_t w[R][BITS];
+      if (k < nfull) {
+#pragma unroll
+        for (int q = 0; q < R; ++q) load_run<BITS>(prow[q] + BITS * k, w[q]);
+      } else {
+        const int nw = (int)(cols - 32 * k) * BITS / 32;  // the partial last run's whole words
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+#pragma unroll
+          for (int j = 0; j < BITS; ++j) w[q][j] = j < nw ? prow[q][BITS * k + j] : 0u;
+      }
+      const uint32_t gk = (uint32_t)k / gr;
+      float sv[R], zv[R], qv[R][32];
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        sv[q] = srow[q][gk];
+        zv[q] = (float)zrow[q][gk];
+        run_codes<BITS>(w[q], qv[q]);
+      }
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        float xv[32];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float4 v = *reinterpret_cast<const float4*>(&xs[t][lane * XP + 4 * i]);
+          xv[4 * i] = v.x; xv[4 * i + 1] = v.y; xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
+        }
+        float sx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) sx += xv[i];
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+          float dot = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) dot = fmaf(qv[q][i], xv[i], dot);
+          yacc[t][q] = fmaf(sv[q], fmaf(dot, unit, -zv[q] * sx), yacc[t][q]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      float v = yacc[t][q];
+#pragma unroll
+      for (int m = 32; m > 0; m >>= 1) v += __shfl_xor(v, m, 64);
+      if (lane == 0 && r0 + q < rows) Y[t * ldy + r0 + q] = v;
+    }
+}
+
+template <int BITS, int T, typename XT>
+hipError_t launch_gemm(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows, int64_t cols,
+                       int64_t G, uint32_t gr, const XT* X, int64_t ldx, float* Y, int64_t ldy, hipStream_t stream) {
+  const unsigned grid = (unsigned)((rows + 7) / 8);
+  hipLaunchKernelGGL((k_dequant_gemm<BITS, T, XT>), dim3(grid), dim3(256), 0, stream, packed, scales, zeros, rows,
+                     cols, G, gr, X, ldx, Y, ldy);
+  return hipGetLastError();
+}
+
+template <int BITS, typename XT>
+hipError_t gemm_bits(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows, int64_t cols,
+                     int64_t G, uint32_t gr, const XT* X, int64_t ldx, int t, float* Y, int64_t ldy,
+                     hipStream_t stream) {
+  if (t >= 8) return launch_gemm<BITS, 8>(packed, scales, zeros, rows, cols, G, gr, X, ldx, Y, ldy, stream);
+  if (t >= 4) return launch_gemm<BITS, 4>(packed, scales, zeros, rows, cols, G, gr, X, ldx, Y, ldy, stream);
+  return launch_gemm<BITS, 2>(packed, scales, zeros, rows, cols, G, gr, X, ldx, Y, ldy, stream);
+}
+
 }  // namespace
 
 bool dequant_gemv_supported(int64_t cols, int32_t bits, int32_t groupsize) {
@@ -294,6 +448,48 @@ hipError_t dequant_gemv(const uint32_t* packed, const float* scales, const uint8
     return dequant_gemv_x(packed, scales, zeros, rows, cols, bits, groupsize, static_cast<const uint16_t*>(x), y,
                           stream);
   return dequant_gemv_x(packed, scales, zeros, rows, cols, bits, groupsize, static_cast<const float*>(x), y, stream);
+}
+
+template <typename XT>
+hipError_t dequant_gemm_x(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
+                          int64_t cols, int32_t bits, int32_t groupsize, const XT* X, int64_t ldx, int64_t batch,
+                          float* Y, int64_t ldy, hipStream_t stream) {
+  const int64_t nrun = (cols + 31) / 32;
+  const int64_t G = groupsize == -1 ? 1 : (cols + groupsize - 1) / groupsize;
+  const uint32_t gr = groupsize == -1 ? (uint32_t)(nrun > 0 ? nrun : 1) : (uint32_t)(groupsize / 32);
+  for (int64_t b0 = 0; b0 < batch;) {
+    const int64_t left = batch - b0;
+    const XT* xb = X + b0 * ldx;
+    float* yb = Y + b0 * ldy;
+    hipError_t e;
+    int took;
+    if (left == 1) {
+      e = dequant_gemv_x(packed, scales, zeros, rows, cols, bits, groupsize, xb, yb, stream);
+      took = 1;
+    } else {
+      took = left >= 8 ? 8 : (left >= 4 ? 4 : 2);
+      switch (bits) {
+        case 2: e = gemm_bits<2>(packed, scales, zeros, rows, cols, G, gr, xb, ldx, took, yb, ldy, stream); break;
+        case 3: e = gemm_bits<3>(packed, scales, zeros, rows, cols, G, gr, xb, ldx, took, yb, ldy, stream); break;
+        case 4: e = gemm_bits<4>(packed, scales, zeros, rows, cols, G, gr, xb, ldx, took, yb, ldy, stream); break;
+        default: e = gemm_bits<8>(packed, scales, zeros, rows, cols, G, gr, xb, ldx, took, yb, ldy, stream); break;
+      }
+    }
+    if (e != hipSuccess) return e;
+    b0 += took;
+  }
+  return hipSuccess;
+}
+
+hipError_t dequant_gemm(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
+                        int64_t cols, int32_t bits, int32_t groupsize, const void* X, bool x_bf16, int64_t ldx,
+                        int64_t batch, float* Y, int64_t ldy, hipStream_t stream) {
+  if (rows <= 0 || batch <= 0) return hipSuccess;
+  if (x_bf16)
+    return dequant_gemm_x(packed, scales, zeros, rows, cols, bits, groupsize, static_cast<const uint16_t*>(X), ldx,
+                          batch, Y, ldy, stream);
+  return dequant_gemm_x(packed, scales, zeros, rows, cols, bits, groupsize, static_cast<const float*>(X), ldx, batch,
+                        Y, ldy, stream);
 }
 
 }  // namespace gptq

@@ -25,7 +25,7 @@ def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"gptq_hessian_workspace_bytes", "gptq_accumulate_hessian",
                           "gptq_quantize_workspace_bytes", "gptq_quantize_layer", "gptq_pack",
-                          "gptq_dequant_gemv", "gptq_hadamard_rows", "gptq_hadamard_hessian",
+                          "gptq_dequant_gemv", "gptq_dequant_gemm", "gptq_hadamard_rows", "gptq_hadamard_hessian",
                           "gptq_cross_workspace_bytes", "gptq_accumulate_cross", "gptq_qep_workspace_bytes",
                           "gptq_qep_correct", "gptq_status_string", "gptq_version"}
     for n in names:
@@ -108,6 +108,18 @@ def test_dequant_gemv_argument_errors():
     assert _gemv(8, 256, 4, 128, x=ctypes.c_void_p(0x1002)) == g.GPTQ_EINVAL  # misaligned
     assert _gemv(8, 256, 4, 128, x_dtype=5) == g.GPTQ_EINVAL  # x dtype
     assert _gemv(0, 256, 4, 128, packed=None) == g.GPTQ_OK     # no rows: no work
+
+
+def test_dequant_gemm_argument_errors():
+    L = g.lib()
+    q = L.gptq_dequant_gemm
+    assert q(FAKE, FAKE, FAKE, 8, 256, 4, 128, FAKE, 1, 128, 4, FAKE, 8, None) == g.GPTQ_EINVAL      # ldx < cols
+    assert q(FAKE, FAKE, FAKE, 8, 256, 4, 128, FAKE, 1, 256, 4, FAKE, 4, None) == g.GPTQ_EINVAL      # ldy < rows
+    assert q(FAKE, FAKE, FAKE, 8, 256, 4, 128, FAKE, 0, 257, 4, FAKE, 8, None) == g.GPTQ_EINVAL      # odd bf16 ldx
+    assert q(FAKE, FAKE, FAKE, 8, 256, 5, 128, FAKE, 1, 256, 4, FAKE, 8, None) == g.GPTQ_EINVAL      # bits
+    assert q(FAKE, FAKE, FAKE, 8, 256, 4, 48, FAKE, 1, 256, 4, FAKE, 8, None) == g.GPTQ_EUNSUPPORTED # group
+    assert q(FAKE, FAKE, FAKE, 8, 256, 4, 128, FAKE, 1, 256, -1, FAKE, 8, None) == g.GPTQ_EINVAL     # batch
+    assert q(None, None, None, 8, 256, 4, 128, None, 1, 256, 0, None, 8, None) == g.GPTQ_OK         # no vectors
 
 
 def test_hadamard_argument_errors():

@@ -183,3 +183,50 @@ def test_dequant_gemv_q_proj_full_size():
     """The 4096 x 4096 q_proj shape at 4 bits, groups of 128: every output checked."""
     say("dequant_gemv q_proj rows=4096 cols=4096 bits=4 groupsize=128")
     _check(4096, 4096, 4, 128, seed=11)
+
+
+def _check_batch(rows, cols, bits, groupsize, batch, seed, x_bf16=False):
+    g = _lib()
+    torch, dev = torch_dev()
+    codes, scales, zeros, _ = _inputs(rows, cols, bits, groupsize, seed)
+    X = np.random.default_rng(seed + 99).standard_normal((batch, cols)).astype(np.float32)
+    if x_bf16:
+        Xb = (X.view(np.uint32) >> 16).astype(np.uint16)
+        X = synth.bf16_to_f32(Xb)
+    packed = pack_ref(codes, bits)
+    Y0 = dequant_gemv_ref(packed, scales, zeros, bits, groupsize, X.T.astype(np.float64), cols).T
+    Y = torch.full((batch, rows), float("nan"), dtype=torch.float32, device=dev)
+    Xd = bf16_dev(Xb) if x_bf16 else to_dev(X)
+    g.gptq_dequant_gemm(to_dev(packed.view(np.int32)), to_dev(scales), to_dev(zeros), bits, groupsize, Xd, Y)
+    torch.cuda.synchronize()
+    Yg = Y.cpu().numpy()
+    assert np.all(np.isfinite(Yg))
+    worst = 0.0
+    for t in range(batch):
+        err = np.abs(Yg[t].astype(np.float64) - Y0[t])
+        bound = _bound(codes, scales, zeros, X[t], groupsize)
+        worst = max(worst, float(np.max(err / bound)))
+        assert np.all(err <= bound), t
+    say(f"   max err/bound {worst:.3f}")
+    return packed, scales, zeros, X, Yg
+
+
+@pytest.mark.parametrize("rows,cols,bits,groupsize,batch,x_bf16", [
+    (37, 4096, 4, 128, 8, False),
+    (9, 1000, 4, -1, 5, False),       # 4 + 1: a group of four, then the single-vector kernel
+    (16, 2080, 3, 32, 3, False),      # 2 + 1
+    (130, 1536, 2, 64, 13, False),    # 8 + 4 + 1
+    (8200, 256, 8, -1, 2, False),
+    (33, 512, 4, 128, 6, True),       # bf16 activations: 4 + 2
+    (4096, 4096, 4, 128, 8, False),   # the q_proj shape at a batch of eight
+])
+def test_dequant_gemm_parity(rows, cols, bits, groupsize, batch, x_bf16):
+    say(f"dequant_gemm rows={rows} cols={cols} bits={bits} groupsize={groupsize} batch={batch} bf16={x_bf16}")
+    _check_batch(rows, cols, bits, groupsize, batch, seed=rows + cols + batch, x_bf16=x_bf16)
+
+
+def test_dequant_gemm_batch_of_one_is_the_gemv():
+    say("dequant_gemm batch 1 vs dequant_gemv")
+    packed, scales, zeros, X, Yg = _check_batch(64, 2048, 4, 128, 1, seed=5)
+    y = _gpu(packed, scales, zeros, 4, 128, X[0], 64)
+    assert np.array_equal(Yg[0], y)
