@@ -308,9 +308,10 @@ hipError_t launch_bits(const uint32_t* packed, const float* scales, const uint8_
 // a lane converts its run's codes to floats once and applies them to all T
 // vectors, staged together in LDS.
 constexpr int BCH = 64;
+constexpr int GEMM_NW = 8;  // waves per workgroup (one staging of x serves 16 rows)
 
-template <int BITS, int T, typename XT>
-__global__ __launch_bounds__(256) void k_dequant_gemm(const uint32_t* __restrict__ packed,
+template <int BITS, int T, int NW, typename XT>
+__global__ __launch_bounds__(64 * NW) void k_dequant_gemm(const uint32_t* __restrict__ packed,
                                                       const float* __restrict__ scales,
                                                       const uint8_t* __restrict__ zeros, int64_t rows, int64_t cols,
                                                       int64_t G, uint32_t gr, const XT* __restrict__ X, int64_t ldx,
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(256) void k_dequant_gemm(const uint32_t* __restrict
   constexpr int R = 2;
   __shared__ __align__(16) float xs[T][BCH * XP];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * R;
+  const int64_t r0 = ((int64_t)blockIdx.x * NW + wave) * R;
   const int64_t wpr = cols * BITS / 32;
   const int64_t nfull = cols / 32, nrun = (cols + 31) / 32;
   const float unit = (BITS == 2 || BITS == 4) ? code_unit() : 1.0f;
@@ -338,8 +339,9 @@ __global__ __launch_bounds__(256) void k_dequant_gemm(const uint32_t* __restrict
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
-      for (int j = 0; j < BCH * 32 / 1024; ++j) {
-        const int e = 4 * (threadIdx.x + 256 * j);
+      for (int j = 0; j < (BCH * 32 + 256 * NW - 1) / (256 * NW); ++j) {
+        const int e = 4 * (threadIdx.x + 64 * NW * j);
+        if (e >= BCH * 32) break;
         const int64_t col = 32 * c0 + e;
         // cols is a multiple of 4 (cols b is whole words), so a vector is all in or all out
         const f32x4 v = col < cols ? load_x4(X + t * ldx + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -402,9 +404,10 @@ __global__ __launch_bounds__(256) void k_dequant_gemm(const uint32_t* __restrict
 template <int BITS, int T, typename XT>
 hipError_t launch_gemm(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows, int64_t cols,
                        int64_t G, uint32_t gr, const XT* X, int64_t ldx, float* Y, int64_t ldy, hipStream_t stream) {
-  const unsigned grid = (unsigned)((rows + 7) / 8);
-  hipLaunchKernelGGL((k_dequant_gemm<BITS, T, XT>), dim3(grid), dim3(256), 0, stream, packed, scales, zeros, rows,
-                     cols, G, gr, X, ldx, Y, ldy);
+  constexpr int NW = GEMM_NW;
+  const unsigned grid = (unsigned)((rows + 2 * NW - 1) / (2 * NW));
+  hipLaunchKernelGGL((k_dequant_gemm<BITS, T, NW, XT>), dim3(grid), dim3(64 * NW), 0, stream, packed, scales, zeros,
+                     rows, cols, G, gr, X, ldx, Y, ldy);
   return hipGetLastError();
 }
 
