@@ -12,7 +12,9 @@
 // them to its R rows:
 //   y_r += s_g (sum_i q_i x_i - z_g sum_i x_i).
 // Lanes meet in a butterfly over the wave, slices in LDS.  Accumulation is
-// fp32 in a fixed order, so results are reproducible.
+// fp32 in a fixed order, so results are reproducible.  A small-batch variant
+// (k_dequant_gemm, below) converts each run's codes to floats once and applies
+// them to up to 8 vectors staged together.
 #include "common.h"
 
 namespace gptq {
