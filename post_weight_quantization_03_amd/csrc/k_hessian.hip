@@ -122,6 +122,54 @@ __device__ __forceinline__ void decode_offdiag_first(int t, int nbt, int& I, int
   J = i + 1 + (t - base);
 }
 
+// One token split (many tiles): the items of a round go to the 8 XCDs in turn,
+// so an XCD's 32 concurrent tiles are every eighth item.  Tiles are therefore
+// numbered by supertiles of 4 block rows x 8 block columns, the supertiles that
+// lie wholly above the diagonal first (32 tiles each, row-major), the rest
+// after them, and item i of a full round of 256 takes tile 32 (8 (m / 32) + x) +
+// m % 32 with x = i % 8 and m = i / 8: each XCD runs one whole supertile at a
+// time, whose 32 tiles read 12 column blocks of X between them instead of about
+// 33 in row-major order, so its L2 streams X far fewer times.  Items of the
+// last, partial round keep their own numbers.  A bijection onto the tiles.
+__device__ __forceinline__ bool full_supertile(int a, int b, int nbt) {
+  return 4 * a + 4 <= nbt && 8 * b + 8 <= nbt && 8 * b >= 4 * a + 3;
+}
+
+__device__ __forceinline__ void decode_supertiles(int i, int nbt, int T, int& I, int& J) {
+  const int R = T / 256;
+  int t = i;
+  if (i < R * 256) {
+    const int x = i & 7, m = i >> 3;
+    t = 32 * (8 * (m >> 5) + x) + (m & 31);
+  }
+  int base = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int a = 0; 4 * a < nbt; ++a) {
+      const int i0 = 4 * a, i1 = min(i0 + 4, nbt);
+      for (int b = i0 / 8; 8 * b < nbt; ++b) {
+        if ((pass == 0) != full_supertile(a, b, nbt)) continue;
+        const int j0 = 8 * b, j1 = min(j0 + 8, nbt);
+        int cnt = 0;
+        for (int r = i0; r < i1; ++r) cnt += max(0, j1 - max(j0, r));
+        if (t < base + cnt) {
+          int k = t - base;
+          for (int r = i0; r < i1; ++r) {
+            const int w = max(0, j1 - max(j0, r));
+            if (k < w) {
+              I = r;
+              J = max(j0, r) + k;
+              return;
+            }
+            k -= w;
+          }
+        }
+        base += cnt;
+      }
+    }
+  }
+  I = J = 0;  // not reached for i < T
+}
+
 __device__ __forceinline__ void decode_upper(int t, int nbt, int& I, int& J) {
   // row-major enumeration of upper tiles: row I holds nbt - I tiles
   int i = 0, base = 0;
@@ -442,7 +490,10 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
 
   const Item it = decode_item(a, blockIdx.x);
   int I, J;
-  decode_offdiag_first(it.tile, a.nbt, I, J);
+  if (a.S == 1)
+    decode_supertiles(blockIdx.x, a.nbt, a.T, I, J);
+  else
+    decode_offdiag_first(it.tile, a.nbt, I, J);
   const bool diag = (I == J);
   const int t0 = it.t0, t1 = it.t1;
   const int nst = t1 > t0 ? (t1 - t0 + KB - 1) / KB : 0;
