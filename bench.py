@@ -37,9 +37,9 @@ PEAK_HBM_GBS = 8000.0
 # of a plain 1 GiB copy; the summary with the commands is
 # profiles/hbm_counters_q_proj_4096x4096_262144tok.md.  Valid only for the kernel source they
 # were taken on: a different k_hessian.hip reports traffic as null.
-SYRK_TRAFFIC = {"k_hessian_sha256": "f33214ee2f7a0fcaa4f3c5367aa86162d706f7974f5f2f1fe3dc9b6ca33f64a6",
+SYRK_TRAFFIC = {"k_hessian_sha256": "ad5690e19bdd38695b7538e2e12ec82c1fec6b918d275b72c06b7738a3ebed1c",
                 "workload": "q_proj_4096", "tokens": 262144,
-                "fetch_bytes": 9211036048.0, "write_bytes": 492678805.0}
+                "fetch_bytes": 9210818884.9, "write_bytes": 492769221.3}
 
 
 def syrk_traffic(workload, tokens):
