@@ -58,6 +58,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="q_proj_4096")
     ap.add_argument("--tokens", type=int, default=None, help="override the calibration token count")
+    ap.add_argument("--layer", type=int, default=0, help="which linear layer of the workload (default the first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens in the oracle's Hessian sample")
     ap.add_argument("--cpu-rows", type=int, default=512, help="rows in the oracle's quantize sample")
@@ -298,7 +299,7 @@ def main():
     from post_weight_quantization_03_amd import synth
 
     wl = synth.workload(args.workload, tokens=args.tokens)
-    lin = wl.linears[0]
+    lin = wl.linears[args.layer]
     acts = wl.hessians[lin.hessian]
     rows, cols, tokens, bits = lin.rows, lin.cols, acts.tokens, lin.bits
     dev = torch.device("cuda:0")
@@ -377,7 +378,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.description, "rows": rows, "cols": cols, "tokens": tokens, "bits": bits,
+        "config": {"workload": wl.description, "layer": lin.name, "rows": rows, "cols": cols, "tokens": tokens, "bits": bits,
                    "groupsize": wl.groupsize, "blocksize": wl.blocksize, "damp": wl.damp},
         "tflops": alg["total_flop"] / step_s / 1e12,
         "stages_ms": {"hessian": t_h * 1e3, "factor_and_quantize": t_q * 1e3, "pack": t_p * 1e3},
