@@ -7,9 +7,14 @@
  * quantizer table; item 3, the LPCD example GPTQ(wbits=3, groupsize=128)),
  * run layer by layer (same article, "limitations", point 3), with a Quantizer
  * interface exposing quantize() and save() (same article, "code
- * architecture").  The three entry points below are that layer pass:
+ * architecture").  The first three entry points below are that layer pass:
  * calibration statistics (gptq_accumulate_hessian), quantize()
  * (gptq_quantize_layer) and the packed artefact behind save() (gptq_pack).
+ * After them: the dequantizing product that serves the packed layer
+ * (gptq_dequant_gemv, gptq_dequant_gemm), a fixed Hadamard rotation applied
+ * before quantizing (gptq_hadamard_rows, gptq_hadamard_hessian), and an
+ * error-propagation correction of W before quantizing (gptq_accumulate_cross,
+ * gptq_qep_correct).
  *
  * Conventions for every call
  *   - Tensor pointers are DEVICE pointers owned by the caller.  Row-major.
