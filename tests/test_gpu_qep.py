@@ -174,3 +174,24 @@ def test_qep_correct_q_proj_full_size():
     rel = _rel(Wout.cpu().numpy().astype(np.float64) - W64, ref - W64)
     say(f"   correction rel Frobenius {rel:.3e}")
     assert rel <= 1e-4
+
+
+def test_qep_not_positive_definite():
+    """H = -I: damping cannot make it positive definite; the correction reports GPTQ_ENOTPD,
+    synchronously (raised) and through a device status."""
+    say("qep correct with an indefinite H")
+    g = _lib()
+    torch, dev = torch_dev()
+    n = 256
+    W = to_dev((0.02 * np.random.default_rng(3).standard_normal((16, n))).astype(np.float32))
+    H = -torch.eye(n, dtype=torch.float32, device=dev)
+    C = torch.zeros((n, n), dtype=torch.float32, device=dev)
+    with pytest.raises(g.GptqError) as ei:
+        g.gptq_qep_correct(W, C, H, 0.5)
+    assert ei.value.status == g.GPTQ_ENOTPD
+    H = -torch.eye(n, dtype=torch.float32, device=dev)
+    C.zero_()
+    dst = torch.zeros(1, dtype=torch.int32, device=dev)
+    g.gptq_qep_correct(W, C, H, 0.5, d_status=dst)
+    torch.cuda.synchronize()
+    assert int(dst.item()) == g.GPTQ_ENOTPD
