@@ -202,6 +202,60 @@ __global__ __launch_bounds__(256) void k_tile_pairs(float* H, int64_t n, int mod
   }
 }
 
+// The same, with whole 16-byte vectors in global memory (n % 4 == 0, H 16-byte
+// aligned): a tile row is 16 float4, each staged into or out of LDS element by
+// element, so the transposed LDS reads stay on the padded column layout.
+__global__ __launch_bounds__(256) void k_tile_pairs4(float* H, int64_t n, int mode) {
+  const int bi = blockIdx.y, bj = blockIdx.x;
+  if (bi > bj) return;
+  __shared__ float ta[64][65], tb[64][65];
+  const int64_t r0 = (int64_t)bi * 64, c0 = (int64_t)bj * 64;
+  const bool two = mode == 0 && bi != bj;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = threadIdx.x + 256 * it, r = idx >> 4, c4 = 4 * (idx & 15);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r0 + r < n && c0 + c4 < n) v = *reinterpret_cast<const float4*>(H + (r0 + r) * n + c0 + c4);
+    ta[r][c4] = v.x; ta[r][c4 + 1] = v.y; ta[r][c4 + 2] = v.z; ta[r][c4 + 3] = v.w;
+    if (two) {
+      float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c0 + r < n && r0 + c4 < n) w = *reinterpret_cast<const float4*>(H + (c0 + r) * n + r0 + c4);
+      tb[r][c4] = w.x; tb[r][c4 + 1] = w.y; tb[r][c4 + 2] = w.z; tb[r][c4 + 3] = w.w;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = threadIdx.x + 256 * it, rr = idx >> 4, c4 = 4 * (idx & 15);
+    if (mode == 0) {
+      if (bi == bj) {
+        if (r0 + rr < n && r0 + c4 < n)
+          *reinterpret_cast<float4*>(H + (r0 + rr) * n + r0 + c4) =
+              make_float4(ta[c4][rr], ta[c4 + 1][rr], ta[c4 + 2][rr], ta[c4 + 3][rr]);
+      } else {
+        if (r0 + rr < n && c0 + c4 < n)
+          *reinterpret_cast<float4*>(H + (r0 + rr) * n + c0 + c4) =
+              make_float4(tb[c4][rr], tb[c4 + 1][rr], tb[c4 + 2][rr], tb[c4 + 3][rr]);
+        if (c0 + rr < n && r0 + c4 < n)
+          *reinterpret_cast<float4*>(H + (c0 + rr) * n + r0 + c4) =
+              make_float4(ta[c4][rr], ta[c4 + 1][rr], ta[c4 + 2][rr], ta[c4 + 3][rr]);
+      }
+    } else {
+      // lower-tile element (c0 + rr, r0 + c4 + e) = upper element (r0 + c4 + e, c0 + rr)
+      const int64_t gr = c0 + rr, gc = r0 + c4;
+      if (gr >= n || gc >= n) continue;
+      if (bi != bj) {
+        *reinterpret_cast<float4*>(H + gr * n + gc) =
+            make_float4(ta[c4][rr], ta[c4 + 1][rr], ta[c4 + 2][rr], ta[c4 + 3][rr]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (gr > gc + e) H[gr * n + gc + e] = ta[c4 + e][rr];
+      }
+    }
+  }
+}
+
 int log2_exact(int b) {
   int k = 0;
   while ((1 << k) < b) ++k;
@@ -249,11 +303,18 @@ hipError_t hadamard_hessian(float* H, int64_t n, const float* signs, int block, 
   const unsigned nb = (unsigned)((n + 63) / 64);
   hipError_t e = hadamard_rows(H, false, n, H, n, n, n, signs, block, stream);  // H Q
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_tile_pairs, dim3(nb, nb), dim3(256), 0, stream, H, n, 0);  // Q^T H
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const bool vec = n % 4 == 0 && (reinterpret_cast<uintptr_t>(H) & 15) == 0;
+  auto pairs = [&](int mode) {
+    if (vec)
+      hipLaunchKernelGGL(k_tile_pairs4, dim3(nb, nb), dim3(256), 0, stream, H, n, mode);
+    else
+      hipLaunchKernelGGL(k_tile_pairs, dim3(nb, nb), dim3(256), 0, stream, H, n, mode);
+    return hipGetLastError();
+  };
+  if ((e = pairs(0)) != hipSuccess) return e;  // Q^T H
   e = hadamard_rows(H, false, n, H, n, n, n, signs, block, stream);  // Q^T H Q
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_tile_pairs, dim3(nb, nb), dim3(256), 0, stream, H, n, 1);  // exact symmetry
+  if ((e = pairs(1)) != hipSuccess) return e;  // exact symmetry
   return hipGetLastError();
 }
 
