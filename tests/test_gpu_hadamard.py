@@ -134,7 +134,8 @@ def _gpu_hessian_rot(H32, d, b):
     return Hd.cpu().numpy()
 
 
-@pytest.mark.parametrize("n,b,tokens", [(256, 256, 600), (300, 4, 700), (200, 8, 100), (4096, 4096, 8192)])
+@pytest.mark.parametrize("n,b,tokens", [(256, 256, 600), (300, 4, 700), (200, 8, 100), (4096, 4096, 8192),
+                                          (302, 2, 500)])  # width not a multiple of 4: element-wise tile pairs
 def test_hadamard_hessian_parity(n, b, tokens):
     say(f"hadamard hessian n={n} block={b}")
     X = synth.Activations(seed=5, tensor=synth.T_X, n=n, tokens=tokens, dist=synth.STUDENT_T4,
