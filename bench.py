@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=512, help="rows in the oracle's quantize sample")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the measurements outside the timed step (GEMV, rotation, error-propagation correction)")
+    ap.add_argument("--whole", action="store_true",
+                    help="one step = every Hessian and every linear layer of the workload, in order, "
+                         "with all inputs resident (layers that share a Hessian reuse its factor)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -285,6 +288,146 @@ def qep_measure(g, torch, Xd, Wd, n, dev):
             "correct_ms_incl_factor": t_q * 1e3}
 
 
+def whole_workload(args, g, torch, wl, dev):
+    """Time one pass over every layer of a workload: per Hessian, H = 0 and H += 2 X^T X;
+    per linear, damping, factor and quantize loop (the first layer on a Hessian factors it,
+    the others reuse the factor through GPTQ_H_IS_FACTOR) and packing.  Every Hessian's
+    activations and every layer's weights are a tensor of their own, resident in HBM before
+    the timed region; codes go to one scratch buffer per shape, scales, zeros and packed
+    codes to buffers of their own per layer."""
+    t0 = time.perf_counter()
+    # one generated tensor per shape; every Hessian and every layer then gets a copy of its
+    # own, rolled by a distinct offset along the tokens (activations) or rows (weights), so
+    # no two calls read the same memory and the values keep the generator's law
+    base_x, X = {}, {}
+    for i, (name, acts) in enumerate(wl.hessians.items()):
+        key = (acts.n, acts.tokens)
+        if key not in base_x:
+            Xd = torch.empty((acts.tokens, acts.n), dtype=torch.bfloat16, device=dev)
+            for t, blk in zip(range(0, acts.tokens, acts.chunk), acts.chunks()):
+                Xd[t:t + blk.shape[0]].copy_(torch.from_numpy(blk.view(np.int16)).view(torch.bfloat16))
+            base_x[key] = Xd
+            print(f"bench.py: activations {acts.tokens}x{acts.n} generated ({time.perf_counter() - t0:.0f} s)",
+                  file=sys.stderr, flush=True)
+        X[name] = torch.roll(base_x[key], shifts=(97 * i) % acts.tokens, dims=0)
+    del base_x
+    base_w, Ws = {}, []
+    for i, lin in enumerate(wl.linears):
+        key = (lin.rows, lin.cols)
+        if key not in base_w:
+            base_w[key] = torch.from_numpy(lin.weight().view(np.int16)).to(dev).view(torch.bfloat16)
+        Ws.append(torch.roll(base_w[key], shifts=(13 * i) % lin.rows, dims=0))
+    del base_w
+    torch.cuda.synchronize()
+    print(f"bench.py: {len(X)} activation and {len(Ws)} weight tensors resident ({time.perf_counter() - t0:.0f} s)",
+          file=sys.stderr, flush=True)
+    gen_s = time.perf_counter() - t0
+
+    Hbuf = {n: torch.zeros((n, n), dtype=torch.float32, device=dev) for n in {a.n for a in wl.hessians.values()}}
+    codes = {(l.rows, l.cols): torch.empty((l.rows, l.cols), dtype=torch.uint8, device=dev) for l in wl.linears}
+    params, outs = [], []
+    ws_q_bytes = ws_h_bytes = 1
+    for lin in wl.linears:
+        p = g.Params(bits=lin.bits, groupsize=wl.groupsize, blocksize=wl.blocksize, damp=wl.damp)
+        params.append(p)
+        G = -(-lin.cols // wl.groupsize)
+        outs.append((torch.empty((lin.rows, G), dtype=torch.float32, device=dev),
+                     torch.empty((lin.rows, G), dtype=torch.uint8, device=dev),
+                     torch.empty((lin.rows,), dtype=torch.float32, device=dev),
+                     torch.empty((lin.rows, lin.cols * lin.bits // 32), dtype=torch.int32, device=dev)))
+        ws_q_bytes = max(ws_q_bytes, g.gptq_quantize_workspace_bytes(lin.rows, lin.cols, p))
+    for a in wl.hessians.values():
+        ws_h_bytes = max(ws_h_bytes, g.gptq_hessian_workspace_bytes(a.n, a.tokens, g.GPTQ_BF16))
+    ws_h = torch.empty(ws_h_bytes, dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(ws_q_bytes, dtype=torch.uint8, device=dev)
+    dstat = torch.zeros((1,), dtype=torch.int32, device=dev)
+    kinds = {"hessian": [], "factor_and_quantize": [], "pack": []}
+
+    def step(record):
+        marks = []
+
+        def mark(kind):
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                marks.append((kind, e))
+
+        current = None
+        for lin, W, p, (scales, zeros, loss, packed) in zip(wl.linears, Ws, params, outs):
+            H = Hbuf[lin.cols]
+            shared = lin.hessian == current
+            if not shared:
+                H.zero_()
+                mark(None)
+                g.gptq_accumulate_hessian(H, X[lin.hessian], workspace=ws_h)
+                mark("hessian")
+                current = lin.hessian
+            q = p if not shared else g.Params(p.bits, p.groupsize, p.blocksize, p.damp, g.GPTQ_H_IS_FACTOR)
+            c = codes[(lin.rows, lin.cols)]
+            mark(None)
+            g.gptq_quantize_layer(W, H, q, c, scales, zeros, None, loss, workspace=ws_q, d_status=dstat)
+            mark("factor_and_quantize")
+            g.gptq_pack(c, lin.bits, packed)
+            mark("pack")
+        return marks
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    all_marks = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        all_marks.append(step(True))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if int(dstat.item()) != 0:
+        raise SystemExit(f"quantizer status {int(dstat.item())}: {g.gptq_status_string(int(dstat.item()))}")
+    for marks in all_marks:
+        for (_, a), (k, b) in zip(marks, marks[1:]):
+            if k is not None:
+                kinds[k].append(a.elapsed_time(b) / 1e3)
+    step_s = wall / args.steps
+    stage_s = {k: sum(v) / args.steps for k, v in kinds.items()}
+    hess_flop = sum(a.tokens * a.n * (a.n + 1.0) for a in wl.hessians.values())
+    fq_flop = 0.0
+    current = None
+    for lin in wl.linears:
+        if lin.hessian != current:
+            fq_flop += 2.0 * lin.cols ** 3 / 3.0
+            current = lin.hessian
+        fq_flop += float(lin.rows) * lin.cols * lin.cols
+    hess_tflops = hess_flop / stage_s["hessian"] / 1e12
+    nl = len(wl.linears)
+    bits_mix = {str(b): sum(1 for l in wl.linears if l.bits == b) for b in sorted({l.bits for l in wl.linears})}
+    tokens = sorted({a.tokens for a in wl.hessians.values()})
+    return {
+        "metric": METRIC,
+        "value": nl / step_s,
+        "unit": "layers/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.description, "whole": True, "layers": nl, "hessians": len(wl.hessians),
+                   "tokens": tokens[0] if len(tokens) == 1 else tokens, "bits": bits_mix,
+                   "groupsize": wl.groupsize, "blocksize": wl.blocksize, "damp": wl.damp,
+                   "inputs": "one generated tensor per shape; each Hessian and layer reads its own copy, "
+                             "rolled by a distinct offset"},
+        "stages_ms": {k: v * 1e3 for k, v in stage_s.items()},
+        "stage_tflops": {"hessian_bf16_mfma": hess_tflops,
+                         "factor_and_quantize_f32": fq_flop / stage_s["factor_and_quantize"] / 1e12},
+        "roofline": {"bound": "mfma", "kernel": "k_syrk_bf16 + k_syrk_reduce (every Hessian call of the pass)",
+                     "achieved": hess_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": hess_tflops / PEAK_BF16_TFLOPS, "traffic": None},
+        "input_generation_s": gen_s,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -299,6 +442,9 @@ def main():
     from post_weight_quantization_03_amd import synth
 
     wl = synth.workload(args.workload, tokens=args.tokens)
+    if args.whole:
+        print(json.dumps(whole_workload(args, g, torch, wl, torch.device("cuda:0"))), flush=True)
+        return
     lin = wl.linears[args.layer]
     acts = wl.hessians[lin.hessian]
     rows, cols, tokens, bits = lin.rows, lin.cols, acts.tokens, lin.bits
