@@ -85,7 +85,7 @@ def algorithmic(rows, cols, tokens, bits):
             "total_flop": float(hess) + factor + quant}
 
 
-def cpu_baseline(W, X_bits, rows, cols, tokens, bits, args):
+def cpu_baseline(W, X_bits, rows, cols, tokens, bits, args, x_bf16=True, w_bf16=True):
     """The oracle on the host cores, on a bounded sample, scaled to one full layer."""
     from oracle import gptq_quantize, hessian_ref
     from post_weight_quantization_03_amd import synth
@@ -96,13 +96,13 @@ def cpu_baseline(W, X_bits, rows, cols, tokens, bits, args):
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     nt = min(args.cpu_tokens, tokens)
-    Xs = synth.bf16_to_f32(X_bits[:nt])
+    Xs = synth.bf16_to_f32(X_bits[:nt]) if x_bf16 else X_bits[:nt].astype(np.float32)
     t0 = time.perf_counter()
     H = hessian_ref([Xs], cols)
     t_h = time.perf_counter() - t0
     H = H * (tokens / nt)  # a same-law stand-in for the full-token Hessian
     nr = min(args.cpu_rows, rows)
-    Ws = synth.bf16_to_f32(W[:nr]).astype(np.float64)
+    Ws = (synth.bf16_to_f32(W[:nr]) if w_bf16 else W[:nr]).astype(np.float64)
     t0 = time.perf_counter()
     out = gptq_quantize(Ws, H, bits, 128, 0.01, blocksize=128)
     t_fq = time.perf_counter() - t0
@@ -288,6 +288,11 @@ def qep_measure(g, torch, Xd, Wd, n, dev):
             "correct_ms_incl_factor": t_q * 1e3}
 
 
+def host_tensor(torch, a, bf16):
+    """A generated host array as a torch tensor: bf16 bit patterns (uint16) or fp32."""
+    return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if bf16 else torch.from_numpy(a)
+
+
 def whole_workload(args, g, torch, wl, dev):
     """Time one pass over every layer of a workload: per Hessian, H = 0 and H += 2 X^T X;
     per linear, damping, factor and quantize loop (the first layer on a Hessian factors it,
@@ -303,9 +308,10 @@ def whole_workload(args, g, torch, wl, dev):
     for i, (name, acts) in enumerate(wl.hessians.items()):
         key = (acts.n, acts.tokens)
         if key not in base_x:
-            Xd = torch.empty((acts.tokens, acts.n), dtype=torch.bfloat16, device=dev)
+            Xd = torch.empty((acts.tokens, acts.n), dtype=torch.bfloat16 if acts.bf16 else torch.float32,
+                             device=dev)
             for t, blk in zip(range(0, acts.tokens, acts.chunk), acts.chunks()):
-                Xd[t:t + blk.shape[0]].copy_(torch.from_numpy(blk.view(np.int16)).view(torch.bfloat16))
+                Xd[t:t + blk.shape[0]].copy_(host_tensor(torch, blk, acts.bf16))
             base_x[key] = Xd
             print(f"bench.py: activations {acts.tokens}x{acts.n} generated ({time.perf_counter() - t0:.0f} s)",
                   file=sys.stderr, flush=True)
@@ -315,7 +321,7 @@ def whole_workload(args, g, torch, wl, dev):
     for i, lin in enumerate(wl.linears):
         key = (lin.rows, lin.cols)
         if key not in base_w:
-            base_w[key] = torch.from_numpy(lin.weight().view(np.int16)).to(dev).view(torch.bfloat16)
+            base_w[key] = host_tensor(torch, lin.weight(), lin.bf16).to(dev)
         Ws.append(torch.roll(base_w[key], shifts=(13 * i) % lin.rows, dims=0))
     del base_w
     torch.cuda.synchronize()
@@ -337,7 +343,8 @@ def whole_workload(args, g, torch, wl, dev):
                      torch.empty((lin.rows, lin.cols * lin.bits // 32), dtype=torch.int32, device=dev)))
         ws_q_bytes = max(ws_q_bytes, g.gptq_quantize_workspace_bytes(lin.rows, lin.cols, p))
     for a in wl.hessians.values():
-        ws_h_bytes = max(ws_h_bytes, g.gptq_hessian_workspace_bytes(a.n, a.tokens, g.GPTQ_BF16))
+        ws_h_bytes = max(ws_h_bytes, g.gptq_hessian_workspace_bytes(a.n, a.tokens,
+                                                                     g.GPTQ_BF16 if a.bf16 else g.GPTQ_F32))
     ws_h = torch.empty(ws_h_bytes, dtype=torch.uint8, device=dev)
     ws_q = torch.empty(ws_q_bytes, dtype=torch.uint8, device=dev)
     dstat = torch.zeros((1,), dtype=torch.int32, device=dev)
@@ -397,6 +404,8 @@ def whole_workload(args, g, torch, wl, dev):
             current = lin.hessian
         fq_flop += float(lin.rows) * lin.cols * lin.cols
     hess_tflops = hess_flop / stage_s["hessian"] / 1e12
+    x_bf16 = all(a.bf16 for a in wl.hessians.values())
+    hess_peak = PEAK_BF16_TFLOPS if x_bf16 else PEAK_F32_TFLOPS
     nl = len(wl.linears)
     bits_mix = {str(b): sum(1 for l in wl.linears if l.bits == b) for b in sorted({l.bits for l in wl.linears})}
     tokens = sorted({a.tokens for a in wl.hessians.values()})
@@ -411,7 +420,7 @@ def whole_workload(args, g, torch, wl, dev):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if x_bf16 else "f32",
         "data": "synthetic",
         "config": {"workload": wl.description, "whole": True, "layers": nl, "hessians": len(wl.hessians),
                    "tokens": tokens[0] if len(tokens) == 1 else tokens, "bits": bits_mix,
@@ -419,11 +428,13 @@ def whole_workload(args, g, torch, wl, dev):
                    "inputs": "one generated tensor per shape; each Hessian and layer reads its own copy, "
                              "rolled by a distinct offset"},
         "stages_ms": {k: v * 1e3 for k, v in stage_s.items()},
-        "stage_tflops": {"hessian_bf16_mfma": hess_tflops,
+        "stage_tflops": {"hessian_bf16_mfma" if x_bf16 else "hessian_f32_mfma": hess_tflops,
                          "factor_and_quantize_f32": fq_flop / stage_s["factor_and_quantize"] / 1e12},
-        "roofline": {"bound": "mfma", "kernel": "k_syrk_bf16 + k_syrk_reduce (every Hessian call of the pass)",
-                     "achieved": hess_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": hess_tflops / PEAK_BF16_TFLOPS, "traffic": None},
+        "roofline": {"bound": "mfma",
+                     "kernel": ("k_syrk_bf16" if x_bf16 else "k_syrk_f32")
+                               + " + k_syrk_reduce (every Hessian call of the pass)",
+                     "achieved": hess_tflops, "peak": hess_peak, "unit": "TFLOP/s",
+                     "frac": hess_tflops / hess_peak, "traffic": None},
         "input_generation_s": gen_s,
     }
 
@@ -453,8 +464,9 @@ def main():
     X_bits = acts.full()
     W_bits = lin.weight()
     gen_s = time.perf_counter() - t0
-    Xd = torch.from_numpy(X_bits.view(np.int16)).to(dev).view(torch.bfloat16)
-    Wd = torch.from_numpy(W_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    x_bf16 = acts.bf16
+    Xd = host_tensor(torch, X_bits, x_bf16).to(dev)
+    Wd = host_tensor(torch, W_bits, lin.bf16).to(dev)
     params = g.Params(bits=bits, groupsize=wl.groupsize, blocksize=wl.blocksize, damp=wl.damp)
     G = -(-cols // wl.groupsize)
     H = torch.zeros((cols, cols), dtype=torch.float32, device=dev)
@@ -464,8 +476,8 @@ def main():
     loss = torch.empty((rows,), dtype=torch.float32, device=dev)
     packed = torch.empty((rows, cols * bits // 32), dtype=torch.int32, device=dev)
     dstat = torch.zeros((1,), dtype=torch.int32, device=dev)
-    ws_h = torch.empty(max(g.gptq_hessian_workspace_bytes(cols, tokens, g.GPTQ_BF16), 1), dtype=torch.uint8,
-                       device=dev)
+    ws_h = torch.empty(max(g.gptq_hessian_workspace_bytes(cols, tokens, g.GPTQ_BF16 if x_bf16 else g.GPTQ_F32), 1),
+                       dtype=torch.uint8, device=dev)
     ws_q = torch.empty(g.gptq_quantize_workspace_bytes(rows, cols, params), dtype=torch.uint8, device=dev)
 
     if args.calib_copy:
@@ -510,6 +522,9 @@ def main():
     t_p = float(np.mean([a.elapsed_time(b) for a, b in zip(ev["q1"], ev["p1"])])) / 1e3
     step_s = wall / args.steps
     alg = algorithmic(rows, cols, tokens, bits)
+    if not x_bf16:
+        alg["x_bytes"] *= 2
+    hess_peak = PEAK_BF16_TFLOPS if x_bf16 else PEAK_F32_TFLOPS
     hess_tflops = alg["hessian_flop"] / t_h / 1e12
     rec = {
         "metric": METRIC,
@@ -522,23 +537,26 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if x_bf16 else "f32",
         "data": "synthetic",
         "config": {"workload": wl.description, "layer": lin.name, "rows": rows, "cols": cols, "tokens": tokens, "bits": bits,
                    "groupsize": wl.groupsize, "blocksize": wl.blocksize, "damp": wl.damp},
         "tflops": alg["total_flop"] / step_s / 1e12,
         "stages_ms": {"hessian": t_h * 1e3, "factor_and_quantize": t_q * 1e3, "pack": t_p * 1e3},
-        "stage_tflops": {"hessian_bf16_mfma": hess_tflops,
+        "stage_tflops": {"hessian_bf16_mfma" if x_bf16 else "hessian_f32_mfma": hess_tflops,
                          "factor_and_quantize_f32": (alg["factor_flop"] + alg["quantize_flop"]) / t_q / 1e12},
         "quantize_only_layers_per_s": 1.0 / (t_q + t_p),
-        "roofline": {"bound": "mfma", "kernel": "k_syrk_bf16 + k_syrk_reduce (one Hessian call)",
+        "roofline": {"bound": "mfma",
+                     "kernel": ("k_syrk_bf16" if x_bf16 else "k_syrk_f32") + " + k_syrk_reduce (one Hessian call)",
                      "achieved": hess_tflops,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": hess_tflops / PEAK_BF16_TFLOPS,
+                     "peak": hess_peak, "unit": "TFLOP/s", "frac": hess_tflops / hess_peak,
                      "traffic": syrk_traffic(args.workload, tokens),
                      "algorithmic_bytes": alg["x_bytes"] + 4.0 * cols * cols},
         "input_generation_s": gen_s,
     }
-    if not args.no_extras:
+    if not args.no_extras and not (x_bf16 and lin.bf16):
+        rec["extras"] = "skipped: the rotation, correction and GEMV measurements take bf16 weights and activations"
+    elif not args.no_extras:
         # measurements outside the timed step; a failure is reported in its field and
         # does not take the step's line with it
         extras = {
@@ -555,7 +573,7 @@ def main():
                 print(f"bench.py: {name} failed: {ex}", file=sys.stderr)
             torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(W_bits, X_bits, rows, cols, tokens, bits, args)
+        rec["cpu_baseline"] = cpu_baseline(W_bits, X_bits, rows, cols, tokens, bits, args, x_bf16, lin.bf16)
     print(json.dumps(rec), flush=True)
 
 
