@@ -56,7 +56,13 @@ enum {
      call with the same cols (shared Hessian: q/k/v, gate/up).  Damping and the
      factor are skipped; the dead-column mask is read back from H's strictly
      lower triangle (see gptq_quantize_layer).  Needs cols >= 3. */
-  GPTQ_H_IS_FACTOR = 1
+  GPTQ_H_IS_FACTOR = 1,
+  /* Damping and the factor in fp64 (the factor's precision option): lambda,
+     H_d and every step of the factor are fp64, and U is rounded to fp32 once,
+     when it is written into H.  The workspace holds an fp64 work matrix
+     (gptq_quantize_workspace_bytes grows by 4 * cols^2 bytes).  Ignored with
+     GPTQ_H_IS_FACTOR. */
+  GPTQ_FACTOR_F64 = 2
 };
 
 /* Quantizer knobs: wbits and groupsize as in GPTQ(wbits, groupsize) on the
@@ -66,7 +72,7 @@ typedef struct {
   int32_t groupsize; /* -1 (one group per row), 32, 64, or a multiple of 128 */
   int32_t blocksize; /* lazy-batch width; 128 is the one supported value */
   float damp;        /* lambda = damp * mean(diag H); typically 0.01; >= 0 and finite */
-  int32_t flags;     /* GPTQ_H_IS_FACTOR or 0 */
+  int32_t flags;     /* GPTQ_H_IS_FACTOR, GPTQ_FACTOR_F64, both, or 0 */
 } gptq_params;
 
 /* ---------------------------------------------------------------------------

@@ -28,6 +28,7 @@ from .gptq_ref import (  # noqa: F401
     damp_ref,
     factor_ref,
     factor_ref_reverse,
+    factor_ref_large,
     gptq_from_factor,
     gptq_quantize,
     grid_params,

@@ -114,6 +114,28 @@ def factor_ref_reverse(Hd) -> np.ndarray:
     return np.ascontiguousarray(np.linalg.inv(R))
 
 
+def factor_ref_large(Hd) -> np.ndarray:
+    """The reverse route of factor_ref_reverse on PyTorch's CPU LAPACK, in fp64.
+
+    For the wide layers (n in the tens of thousands) where NumPy's general
+    inverse takes minutes: the lower Cholesky factor of the index-reversed
+    H_d flipped back gives the upper R with H_d = R R^T, and U = R^{-1} comes
+    from one upper-triangular solve against the identity.  Same U as
+    factor_ref up to rounding.
+    """
+    import torch
+    H = torch.from_numpy(np.ascontiguousarray(Hd, dtype=np.float64))
+    Lr, info = torch.linalg.cholesky_ex(H.flip(0, 1).contiguous())
+    if int(info) != 0:
+        raise NotPositiveDefinite(f"leading minor {int(info)} is not positive definite")
+    R = Lr.flip(0, 1).contiguous()
+    del Lr
+    n = R.shape[0]
+    eye = torch.eye(n, dtype=torch.float64)
+    U = torch.linalg.solve_triangular(R, eye, upper=True)
+    return U.numpy()
+
+
 # ---------------------------------------------------------------------------
 # Grid
 # ---------------------------------------------------------------------------

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libgptq.so")
 GPTQ_OK, GPTQ_EINVAL, GPTQ_ENOTPD, GPTQ_EWORKSPACE, GPTQ_EUNSUPPORTED, GPTQ_EHIP = range(6)
 GPTQ_BF16, GPTQ_F32 = 0, 1
 GPTQ_H_IS_FACTOR = 1
+GPTQ_FACTOR_F64 = 2
 
 
 class GptqError(RuntimeError):
@@ -130,9 +131,16 @@ def _check_dev(*ts):
             raise ValueError("tensors must be contiguous device tensors")
 
 
-def _workspace(nbytes, like):
+def _workspace(nbytes, like, stream=None):
+    """A temporary workspace, freed when the caller drops it.  PyTorch's caching allocator ties a
+    block to the stream current at allocation; when the library's work runs on another stream,
+    the block is recorded on that stream too, so it is not handed out again before that work is
+    done."""
     torch = _torch()
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=like.device)
+    ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=like.device)
+    if stream is not None:
+        ws.record_stream(stream)
+    return ws
 
 
 # --------------------------------------------------------------------------- entry points
@@ -160,7 +168,7 @@ def gptq_accumulate_hessian(H, X, workspace=None, stream=None):
     dt = _dtype_code(X)
     need = gptq_hessian_workspace_bytes(n, X.shape[0], dt)
     if workspace is None:
-        workspace = _workspace(need, H)
+        workspace = _workspace(need, H, stream)
     st = lib().gptq_accumulate_hessian(_ptr(H), n, _ptr(X), dt, X.shape[0], X.stride(0), _ptr(workspace),
                                        workspace.numel(), _stream(stream))
     if st:
@@ -185,7 +193,7 @@ def gptq_quantize_layer(W, H, params: Params, codes, scales, zeros, w_hat=None, 
     p = params.c()
     need = int(lib().gptq_quantize_workspace_bytes(rows, cols, ctypes.byref(p)))
     if workspace is None:
-        workspace = _workspace(need, W)
+        workspace = _workspace(need, W, stream)
     st = lib().gptq_quantize_layer(_ptr(W), _dtype_code(W), rows, cols, _ptr(H), ctypes.byref(p), _ptr(codes),
                                    _ptr(scales), _ptr(zeros), _ptr(w_hat), _ptr(row_loss), _ptr(workspace),
                                    workspace.numel(), _ptr(d_status), _stream(stream))
@@ -292,7 +300,7 @@ def gptq_accumulate_cross(C, X, Xq, workspace=None, stream=None):
             or not Xq.is_cuda):
         raise ValueError("shape, dtype or stride mismatch")
     if workspace is None:
-        workspace = _workspace(gptq_cross_workspace_bytes(n), C)
+        workspace = _workspace(gptq_cross_workspace_bytes(n), C, stream)
     st = lib().gptq_accumulate_cross(_ptr(C), n, _ptr(X), _ptr(Xq), _dtype_code(X), X.shape[0], X.stride(0),
                                      _ptr(workspace), workspace.numel(), _stream(stream))
     if st:
@@ -315,7 +323,7 @@ def gptq_qep_correct(W, C, H, alpha: float, damp: float = 0.01, W_out=None, work
     if W_out is None:
         W_out = torch.empty((rows, cols), dtype=torch.float32, device=W.device)
     if workspace is None:
-        workspace = _workspace(gptq_qep_workspace_bytes(rows, cols), W)
+        workspace = _workspace(gptq_qep_workspace_bytes(rows, cols), W, stream)
     st = lib().gptq_qep_correct(_ptr(W), _dtype_code(W), rows, cols, _ptr(C), _ptr(H), damp, alpha, _ptr(W_out),
                                 _ptr(workspace), workspace.numel(), _ptr(d_status), _stream(stream))
     if st:

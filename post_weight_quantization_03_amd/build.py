@@ -30,10 +30,25 @@ def _run(cmd):
 
 
 def build_gptq() -> str:
+    """Compiles each kernel file to an object (in parallel), then links the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+
     srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+    obj_dir = os.path.join(ROOT, "_build", "gptq")
+    os.makedirs(obj_dir, exist_ok=True)
+    cflags = [f for f in HIP_FLAGS if f != "-shared"]
+
+    def compile_one(src):
+        obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+        _run([HIPCC, *cflags, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj])
+        return obj
+
+    jobs = max(1, min(len(srcs), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(compile_one, srcs))
     out = os.path.join(PKG, "libgptq.so")
     tmp = out + ".tmp"
-    _run([HIPCC, *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp, "-L/opt/rocm/lib",
+    _run([HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp, "-L/opt/rocm/lib",
           "-lhipblaslt"])
     os.replace(tmp, out)
     return out

@@ -71,6 +71,16 @@ size_t factor_scratch_floats(int64_t n);  // floats of FactorWs::Lt
 // H (fp32 [n, n]) -> damped, factored; U written back to H's upper triangle, dead flags to the
 // strictly lower slots.  Status (ENOTPD) is raised on the device.
 hipError_t factor_run(float* H, int64_t n, float damp, const FactorWs& ws, hipStream_t stream);
+// The same factor computed in fp64 (k_factor64.hip); U is rounded to fp32 when written to H.
+struct Factor64Ws {
+  int* status;
+  double* lam;      // device: lambda (double)
+  uint8_t* dead;    // device [n]
+  double* A;        // [n, n] fp64 work matrix
+  double* Lt;       // [ceil(n / 128), 128, 128] fp64 L_kk^T of each diagonal block
+};
+size_t factor64_scratch_doubles(int64_t n);  // doubles of Factor64Ws::Lt
+hipError_t factor64_run(float* H, int64_t n, float damp, const Factor64Ws& ws, hipStream_t stream);
 // H holds a factor from an earlier call: read the dead flags back from it.
 hipError_t dead_from_factor(const float* H, int64_t n, uint8_t* dead, hipStream_t stream);
 

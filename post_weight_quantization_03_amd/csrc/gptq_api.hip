@@ -18,7 +18,7 @@ bool params_ok(const gptq_params* p, int64_t cols, int* why) {
   if (!p) return (*why = GPTQ_EINVAL), false;
   if (!(p->bits == 2 || p->bits == 3 || p->bits == 4 || p->bits == 8)) return (*why = GPTQ_EINVAL), false;
   if (!(p->damp >= 0.0f) || !(p->damp < INFINITY)) return (*why = GPTQ_EINVAL), false;
-  if (p->flags & ~GPTQ_H_IS_FACTOR) return (*why = GPTQ_EINVAL), false;
+  if (p->flags & ~(GPTQ_H_IS_FACTOR | GPTQ_FACTOR_F64)) return (*why = GPTQ_EINVAL), false;
   if (p->groupsize == 0 || p->groupsize < -1) return (*why = GPTQ_EINVAL), false;
   if (p->blocksize != 128) return (*why = GPTQ_EUNSUPPORTED), false;
   const int64_t g = p->groupsize;
@@ -36,7 +36,7 @@ QuantLayout layout(int64_t rows, int64_t cols, const gptq_params* p) {
     return at;
   };
   L.status = take(4 * sizeof(int));
-  L.lam = take(sizeof(float));
+  L.lam = take(sizeof(double));
   L.dead = take((size_t)cols);
   L.loss = take((size_t)rows * sizeof(float));
   L.Wf = take((size_t)rows * cols * sizeof(float));
@@ -46,8 +46,13 @@ QuantLayout layout(int64_t rows, int64_t cols, const gptq_params* p) {
     L.Us = ub ? take(ub) : 0;
   }
   if (!(p->flags & GPTQ_H_IS_FACTOR)) {
-    L.A = take((size_t)cols * cols * sizeof(float));
-    L.Lt = take(factor_scratch_floats(cols) * sizeof(float));
+    if (p->flags & GPTQ_FACTOR_F64) {
+      L.A = take((size_t)cols * cols * sizeof(double));
+      L.Lt = take(factor64_scratch_doubles(cols) * sizeof(double));
+    } else {
+      L.A = take((size_t)cols * cols * sizeof(float));
+      L.Lt = take(factor_scratch_floats(cols) * sizeof(float));
+    }
   }
   L.total = off;
   return L;
@@ -123,6 +128,14 @@ int gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t rows, int64_t
   if (e != hipSuccess) return GPTQ_EHIP;
   if (p->flags & GPTQ_H_IS_FACTOR) {
     e = dead_from_factor(H, cols, dead, stream);
+  } else if (p->flags & GPTQ_FACTOR_F64) {
+    Factor64Ws f{};
+    f.status = status;
+    f.lam = reinterpret_cast<double*>(ws + L.lam);
+    f.dead = dead;
+    f.A = reinterpret_cast<double*>(ws + L.A);
+    f.Lt = reinterpret_cast<double*>(ws + L.Lt);
+    e = factor64_run(H, cols, p->damp, f, stream);
   } else {
     FactorWs f{};
     f.status = status;

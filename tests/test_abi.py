@@ -54,6 +54,7 @@ def test_quantize_argument_errors():
     assert _q(8, 256, P(4, 128, 128, -1.0, 0)) == g.GPTQ_EINVAL            # damp
     assert _q(8, 256, P(4, 128, 128, float("nan"), 0)) == g.GPTQ_EINVAL
     assert _q(8, 256, P(4, 128, 128, 0.01, 8)) == g.GPTQ_EINVAL            # unknown flag
+    assert _q(8, 256, P(4, 128, 128, 0.01, 4)) == g.GPTQ_EINVAL
     assert _q(8, 2, P(4, 128, 128, 0.01, 1)) == g.GPTQ_EINVAL              # shared factor needs cols >= 3
     assert _q(-1, 256, P(4, 128, 128, 0.01, 0)) == g.GPTQ_EINVAL
     assert _q(8, 256, P(4, 128, 128, 0.01, 0), W=None) == g.GPTQ_EINVAL
@@ -72,6 +73,12 @@ def test_quantize_workspace_sizes():
     assert b < a and b >= 4096 * 4096 * 4
     assert g.gptq_quantize_workspace_bytes(4096, 4096, g.Params(bits=5)) == 0
     assert g.gptq_quantize_workspace_bytes(0, 4096, p) == 0
+    # the fp64 factor option: the work matrix and the diagonal-block buffers in fp64
+    c = g.gptq_quantize_workspace_bytes(4096, 4096, g.Params(bits=4, groupsize=128, flags=g.GPTQ_FACTOR_F64))
+    assert c - a == 4096 * 4096 * 4 + 32 * 128 * 128 * 4
+    d = g.gptq_quantize_workspace_bytes(4096, 4096, g.Params(bits=4, groupsize=128,
+                                                             flags=g.GPTQ_FACTOR_F64 | g.GPTQ_H_IS_FACTOR))
+    assert d == b
 
 
 def test_hessian_argument_errors_and_workspace():

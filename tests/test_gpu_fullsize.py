@@ -15,12 +15,15 @@ outputs it can compute one by one:
             oracle from fewer tokens of the workload's activations (the
             quantizer's launch configuration depends on rows and cols only),
             and both sides take the same fp32 H.
-  The Qwen3-32B down_proj layer (25600 columns) is quantized against a
-  block-diagonal H (10 blocks of 2560 = 20 groups): the inverse of a
-  block-diagonal matrix and its Cholesky factor are block-diagonal, so the error
-  feedback never leaves a block and, groups tiling the blocks, each block is an
-  independent GPTQ problem with the damping lambda of the whole diagonal.  The
-  GPU still runs its full blocked factor over the 25600^2 matrix.
+  The Qwen3-32B down_proj layer (25600 columns) is quantized against a dense
+  25600^2 H from 16384 tokens of its activation law.  The oracle factors it in
+  fp64 (the LAPACK route) and replays every column of 1024 sampled rows; the
+  layer output error is compared over those rows.  A second case quantizes
+  the same layer against a block-diagonal H (10 blocks of 2560 = 20 groups):
+  the inverse of a block-diagonal matrix and its Cholesky factor are
+  block-diagonal, so the error feedback never leaves a block and, groups
+  tiling the blocks, each block is an independent GPTQ problem with the
+  damping lambda of the whole diagonal; there every row is checked.
 """
 
 from __future__ import annotations
@@ -215,3 +218,85 @@ def test_quantize_full_size_down_proj_32b_block_diagonal():
         g0, g1 = c0 // 128, c1 // 128
         _compare(Wr[:, c0:c1], U, lin.bits, codes[:, c0:c1], scales[:, g0:g1], zeros[:, g0:g1], what[:, c0:c1],
                  blocks[b])
+
+
+_DENSE_32B = {}
+
+
+def _dense_32b_case():
+    """Inputs and oracle products of the dense 25600^2 case, built once per session.
+
+    H = 2 X^T X over the first 16384 tokens of the layer's activation law (t4, 128 outlier
+    channels x30), summed in fp64 and rounded to fp32; both sides take that fp32 H.  With
+    fewer tokens than columns H has rank 16384, so 9216 eigenvalues of H_d are lambda alone:
+    a worse-conditioned factor than the full 131072-token Hessian's.
+    """
+    if _DENSE_32B:
+        return _DENSE_32B
+    import torch
+
+    from oracle import damp_ref, factor_ref_large
+    w = synth.workload("down_proj_32b")
+    lin = w.linears[0]
+    n, ntok = lin.cols, 16384
+    say(f"-- down_proj_32b dense: W {lin.rows}x{n}, H from {ntok} tokens ({torch.get_num_threads()} threads)")
+    t0 = time.perf_counter()
+    Xt = torch.from_numpy(synth.bf16_to_f32(w.hessians["x"].block(0, ntok))).double()
+    H64 = (2.0 * (Xt.T @ Xt)).numpy()
+    del Xt
+    H32 = H64.astype(np.float32)
+    H64[...] = H32
+    say(f"   H took {time.perf_counter() - t0:.1f}s")
+    t0 = time.perf_counter()
+    Hd, _, dead, _ = damp_ref(H64, np.zeros((1, n)), 0.01)
+    assert not dead.any()
+    U = factor_ref_large(Hd)
+    del Hd
+    say(f"   oracle factor (fp64, {n}^2) took {time.perf_counter() - t0:.1f}s")
+    rng = np.random.default_rng(25600)
+    sel = np.unique(np.concatenate([[0, 1, 2, lin.rows // 2, lin.rows - 2, lin.rows - 1],
+                                    rng.choice(lin.rows, size=1018, replace=False)]))
+    W_bits = lin.weight()
+    _DENSE_32B.update(lin=lin, H64=H64, H32=H32, U=U, sel=sel, W_bits=W_bits,
+                      Wr=synth.bf16_to_f32(W_bits[sel]).astype(np.float64))
+    return _DENSE_32B
+
+
+@pytest.mark.parametrize("flags", [0, 2], ids=["factor_f32", "factor_f64"])
+def test_quantize_full_size_down_proj_32b_dense(flags):
+    """The whole 5120 x 25600 layer against a dense 25600^2 H: 200 block steps of the factor (fp32,
+    or the fp64 option) with every off-diagonal update live, then the column loop; every column of
+    1024 sampled rows is replayed against the oracle's fp64 factor."""
+    import torch
+
+    from oracle import gptq_from_factor, layer_error, replay_compare
+    c = _dense_32b_case()
+    lin, sel = c["lin"], c["sel"]
+    say(f"   GPU layer, flags={flags}")
+    out, Hd = _gpu_layer(c["W_bits"], c["H32"], lin.bits, flags=flags)
+    # the factor itself against the oracle's on the sampled rows' diagonal and a band of rows
+    rows_u = torch.as_tensor([0, 1, 12799, 25598, 25599], device=Hd.device)
+    Ug = Hd[rows_u].cpu().numpy().astype(np.float64)
+    Uo = c["U"][[0, 1, 12799, 25598, 25599]]
+    for i, r in enumerate([0, 1, 12799, 25598, 25599]):
+        Ug[i, :r] = 0.0
+    say(f"   U rows rel error {np.linalg.norm(Ug - Uo) / np.linalg.norm(Uo):.3e}")
+    del Hd
+    codes = out["codes"].cpu().numpy()[sel].astype(np.int64)
+    scales = out["scales"].cpu().numpy()[sel]
+    zeros = out["zeros"].cpu().numpy()[sel]
+    what = out["w_hat"].cpu().numpy()[sel].astype(np.float64)
+    del out
+    t0 = time.perf_counter()
+    st = replay_compare(c["Wr"], c["U"], lin.bits, 128, codes, scales, zeros, TAU, blocksize=128)
+    st.pop("what")
+    say(f"   replay over {len(sel)} rows took {time.perf_counter() - t0:.1f}s")
+    say("   replay:", {k: (round(v, 8) if isinstance(v, float) else v) for k, v in st.items()})
+    assert st["hard_flips"] == 0 and st["zero_hard"] == 0, st
+    assert st["identical_frac"] >= IDENT_MIN, st
+    assert st["max_scale_rel"] <= SCALE_RTOL, st
+    ref = gptq_from_factor(c["Wr"], c["U"], lin.bits, 128, blocksize=128, decision=np.float32)
+    e_or = layer_error(c["Wr"], ref["what"], c["H64"])
+    e_gpu = layer_error(c["Wr"], what, c["H64"])
+    say(f"   layer error (sampled rows) gpu {e_gpu:.6e} oracle {e_or:.6e} ratio-1 {e_gpu / e_or - 1:.2e}")
+    assert abs(e_gpu / e_or - 1.0) <= LERR_RTOL

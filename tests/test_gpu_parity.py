@@ -91,6 +91,33 @@ def test_hessian_empty_and_accumulating():
     assert torch.equal(H.cpu(), torch.full((64, 64), 3.0) + 2 * torch.eye(64))
 
 
+def test_hessian_on_side_stream_temporary_workspace():
+    """The binding's temporary workspace, used on a stream that is not the current one, is not
+    handed to a new allocation while that stream's kernels still write it: allocating and
+    filling memory on the current stream right after the call leaves H unchanged."""
+    g = _lib_loaded()
+    torch, dev = torch_dev()
+    n, tokens = 1024, 65536
+    say(f"hessian on a side stream, n={n} tokens={tokens}")
+    assert g.gptq_hessian_workspace_bytes(n, tokens, g.GPTQ_BF16) > 0
+    a = synth.Activations(seed=13, tensor=synth.T_X, n=n, tokens=tokens, dist=synth.STUDENT_T4,
+                          outliers=10, outlier_factor=20.0, bf16=True)
+    Xd = bf16_dev(a.full())
+    ref = torch.zeros((n, n), dtype=torch.float32, device=dev)
+    g.gptq_accumulate_hessian(ref, Xd)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for _ in range(3):
+        H = torch.zeros((n, n), dtype=torch.float32, device=dev)
+        side.wait_stream(torch.cuda.current_stream())
+        g.gptq_accumulate_hessian(H, Xd, stream=side)
+        junk = torch.full((g.gptq_hessian_workspace_bytes(n, tokens, g.GPTQ_BF16) // 4,), 7.0, device=dev)
+        side.synchronize()
+        torch.cuda.synchronize()
+        assert torch.equal(H, ref)
+        del junk
+
+
 # --------------------------------------------------------------------------- quantize
 
 def test_worked_example_gpu():

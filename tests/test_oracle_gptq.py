@@ -11,7 +11,8 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import (NotPositiveDefinite, damp_ref, factor_ref, factor_ref_reverse, gptq_from_factor,
+from oracle import (NotPositiveDefinite, damp_ref, factor_ref, factor_ref_large, factor_ref_reverse,
+                    gptq_from_factor,
                     gptq_quantize, grid_params, hessian_ref, layer_error, replay_compare, rtn_ref)
 from oracle.gptq_exact import gptq_exact, rint_half_even
 
@@ -284,6 +285,7 @@ def test_factor_2x2_closed_form():
     expect = np.array([[u00, u01], [0.0, u11]])
     np.testing.assert_allclose(factor_ref(Hd), expect, rtol=1e-14)
     np.testing.assert_allclose(factor_ref_reverse(Hd), expect, rtol=1e-14)
+    np.testing.assert_allclose(factor_ref_large(Hd), expect, rtol=1e-14)
     assert u11 == pytest.approx(1 / np.sqrt(c), rel=1e-14)  # last pivot is 1/sqrt(H_nn)
 
 
@@ -295,6 +297,25 @@ def test_factor_properties_and_routes():
     assert np.allclose(np.tril(U1, -1), 0) and (np.diag(U1) > 0).all()
     np.testing.assert_allclose(U1.T @ U1 @ Hd, np.eye(64), atol=1e-9)
     np.testing.assert_allclose(U2, U1, rtol=1e-8, atol=1e-12 * np.abs(U1).max())
+
+
+@pytest.mark.parametrize("n", [64, 300, 1030])
+def test_factor_large_route_matches_inverse_route(n):
+    """The LAPACK reverse route (used for the widest layers) gives factor_ref's U: upper, positive
+    diagonal, U^T U H_d = I, and the same entries up to rounding, at ragged sizes too."""
+    rng = np.random.default_rng(n)
+    X = rng.standard_t(4, size=(max(2 * n, 256), n)) * np.where(rng.random(n) < 0.02, 20.0, 1.0)
+    Hd, _, _, _ = damp_ref(2.0 * X.T @ X, np.zeros((1, n)), 0.01)
+    U1 = factor_ref(Hd)
+    U3 = factor_ref_large(Hd)
+    assert np.array_equal(np.tril(U3, -1), np.zeros((n, n))) and (np.diag(U3) > 0).all()
+    np.testing.assert_allclose(U3.T @ U3 @ Hd, np.eye(n), atol=1e-8)
+    np.testing.assert_allclose(U3, U1, rtol=0, atol=1e-9 * np.abs(U1).max())
+
+
+def test_factor_large_route_not_positive_definite():
+    with pytest.raises(NotPositiveDefinite):
+        factor_ref_large(np.diag([1.0, 2.0, -1.0, 3.0]))
 
 
 def test_not_positive_definite():
