@@ -95,6 +95,33 @@ int gptq_accumulate_hessian(float* H, int64_t n, const void* X, gptq_dtype x_dty
                             int64_t tokens, int64_t ldx, void* workspace,
                             size_t workspace_bytes, gptq_stream_t stream);
 
+/* gptq_accumulate_hessian for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving or calibration loops, harnesses that
+ * forbid hipMalloc.  No workspace argument: the split-K partial tiles go to a
+ * fixed device array inside the library, GPTQ_HESSIAN_STATIC_BYTES per device,
+ * which a device holds from the library's first use on it until the process
+ * ends.  The call allocates and frees nothing.
+ *
+ * Same arguments (less the workspace), work split, kernels and result (bit for
+ * bit) as gptq_accumulate_hessian.  A call whose
+ * gptq_hessian_workspace_bytes(n, tokens, x_dtype) exceeds
+ * GPTQ_HESSIAN_STATIC_BYTES returns GPTQ_EWORKSPACE before any work.  For bf16
+ * X that admits every n <= 1792 at any token count, every n >= 9729 (those
+ * need no partials) and, in between, calls of fewer than 1024 tokens; a
+ * 4096-wide layer must therefore be fed in chunks of at most 1023 tokens.
+ * `stream` must belong to the current device (GPTQ_EINVAL otherwise); the
+ * array used is that device's.
+ *
+ * Every call on a device shares that device's array, and a call leaves its
+ * partials there.  Nothing needs clearing between calls (every partial slot a
+ * call reads is written by that call first), but calls that overlap in time on
+ * one device -- on different streams, or from different host threads without
+ * ordering -- race on the array and leave H undefined. */
+#define GPTQ_HESSIAN_STATIC_BYTES ((size_t)64 << 20)
+
+int gptq_accumulate_hessian_static(float* H, int64_t n, const void* X, gptq_dtype x_dtype,
+                                   int64_t tokens, int64_t ldx, gptq_stream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Quantize one linear layer W[rows, cols] (dtype w_dtype, row stride cols)
  * against its Hessian H[cols, cols] (fp32, full symmetric as written by

@@ -67,6 +67,8 @@ def lib():
     L.gptq_hessian_workspace_bytes.restype = sz
     L.gptq_accumulate_hessian.argtypes = [vp, i64, vp, ctypes.c_int, i64, i64, vp, sz, vp]
     L.gptq_accumulate_hessian.restype = ctypes.c_int
+    L.gptq_accumulate_hessian_static.argtypes = [vp, i64, vp, ctypes.c_int, i64, i64, vp]
+    L.gptq_accumulate_hessian_static.restype = ctypes.c_int
     L.gptq_quantize_workspace_bytes.argtypes = [i64, i64, ctypes.POINTER(gptq_params)]
     L.gptq_quantize_workspace_bytes.restype = sz
     L.gptq_quantize_layer.argtypes = [vp, ctypes.c_int, i64, i64, vp, ctypes.POINTER(gptq_params), vp, vp, vp,
@@ -173,6 +175,25 @@ def gptq_accumulate_hessian(H, X, workspace=None, stream=None):
                                        workspace.numel(), _stream(stream))
     if st:
         raise GptqError(st, "gptq_accumulate_hessian")
+    return H
+
+
+GPTQ_HESSIAN_STATIC_BYTES = 64 << 20
+
+
+def gptq_accumulate_hessian_static(H, X, stream=None):
+    """gptq_accumulate_hessian with the partial tiles in the library's fixed device array: no
+    workspace and no allocation, for calls whose workspace need fits GPTQ_HESSIAN_STATIC_BYTES."""
+    _check_dev(H)
+    if not X.is_cuda or X.stride(1) != 1:
+        raise ValueError("X must be a device tensor with unit column stride")
+    n = H.shape[0]
+    if H.dtype != _torch().float32 or H.shape != (n, n) or X.shape[1] != n:
+        raise ValueError("shape or dtype mismatch")
+    st = lib().gptq_accumulate_hessian_static(_ptr(H), n, _ptr(X), _dtype_code(X), X.shape[0], X.stride(0),
+                                              _stream(stream))
+    if st:
+        raise GptqError(st, "gptq_accumulate_hessian_static")
     return H
 
 

@@ -1,6 +1,8 @@
 // C ABI of libgptq.so: argument checks on the host, workspace carving and the
 // launch sequence of each entry point.  Every declaration is documented in
 // include/gptq.h.
+#include <mutex>
+
 #include "common.h"
 
 namespace {
@@ -91,6 +93,61 @@ int gptq_accumulate_hessian(float* H, int64_t n, const void* X, gptq_dtype x_dty
   const size_t need = hessian_workspace(n, tokens, x_dtype);
   if (workspace_bytes < need || (need > 0 && !workspace)) return GPTQ_EWORKSPACE;
   return hessian_launch(H, n, X, x_dtype, tokens, ldx, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Hessian accumulation without allocation: the split-K partial tiles go to this
+// fixed array instead of a caller workspace.  The name is a host-side stand-in
+// for the device symbol: host code uses only the per-device address that
+// hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[GPTQ_HESSIAN_STATIC_BYTES];
+
+namespace {
+
+constexpr int MAX_DEVICES = 256;
+std::mutex scratch_mu;
+void* scratch_addr[MAX_DEVICES] = {};
+
+// The current device's address of `scratch`, taken once per device with that
+// device current.
+int scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return GPTQ_EHIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return GPTQ_EHIP;
+    scratch_addr[dev] = p;
+  }
+  *out = scratch_addr[dev];
+  return GPTQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gptq_accumulate_hessian_static(float* H, int64_t n, const void* X, gptq_dtype x_dtype, int64_t tokens,
+                                   int64_t ldx, gptq_stream_t stream) {
+  if (n < 0 || tokens < 0 || n > MAX_DIM || tokens > MAX_DIM) return GPTQ_EINVAL;
+  if (!(x_dtype == GPTQ_BF16 || x_dtype == GPTQ_F32)) return GPTQ_EINVAL;
+  if (n == 0 || tokens == 0) return GPTQ_OK;
+  if (!H || !X || ldx < n) return GPTQ_EINVAL;
+  if (n * n > ((int64_t)1 << 31) * 2) return GPTQ_EUNSUPPORTED;
+  const size_t need = hessian_workspace(n, tokens, x_dtype);
+  if (need > GPTQ_HESSIAN_STATIC_BYTES) return GPTQ_EWORKSPACE;
+  if (stream) {
+    int cur = -1, sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess)
+      return GPTQ_EHIP;
+    if (cur != sdev) return GPTQ_EINVAL;
+  }
+  void* ws = nullptr;
+  const int st = scratch_ptr(&ws);
+  if (st != GPTQ_OK) return st;
+  return hessian_launch(H, n, X, x_dtype, tokens, ldx, ws, GPTQ_HESSIAN_STATIC_BYTES, (hipStream_t)stream);
 }
 
 size_t gptq_quantize_workspace_bytes(int64_t rows, int64_t cols, const gptq_params* p) {

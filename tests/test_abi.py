@@ -23,7 +23,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported():
     lib = g.lib()
     names = declared_functions()
-    assert set(names) == {"gptq_hessian_workspace_bytes", "gptq_accumulate_hessian",
+    assert set(names) == {"gptq_hessian_workspace_bytes", "gptq_accumulate_hessian", "gptq_accumulate_hessian_static",
                           "gptq_quantize_workspace_bytes", "gptq_quantize_layer", "gptq_pack",
                           "gptq_dequant_gemv", "gptq_dequant_gemm", "gptq_hadamard_rows", "gptq_hadamard_hessian",
                           "gptq_cross_workspace_bytes", "gptq_accumulate_cross", "gptq_qep_workspace_bytes",
@@ -91,6 +91,27 @@ def test_hessian_argument_errors_and_workspace():
     assert need > 0
     assert L.gptq_accumulate_hessian(FAKE, 4096, FAKE, 0, 262144, 4096, FAKE, need - 1, None) == g.GPTQ_EWORKSPACE
     assert g.gptq_hessian_workspace_bytes(11008, 131072, g.GPTQ_BF16) == 0  # enough tiles: no split
+
+
+def test_hessian_static_argument_errors_and_limit():
+    """The entry point without allocation checks its arguments and its fixed array's limit on the
+    host, before any device work."""
+    L = g.lib()
+    f = L.gptq_accumulate_hessian_static
+    assert f(FAKE, 64, FAKE, 7, 10, 64, None) == g.GPTQ_EINVAL       # dtype
+    assert f(FAKE, 64, FAKE, 0, 10, 32, None) == g.GPTQ_EINVAL       # ldx < n
+    assert f(None, 64, FAKE, 0, 10, 64, None) == g.GPTQ_EINVAL
+    assert f(FAKE, -1, FAKE, 0, 10, 64, None) == g.GPTQ_EINVAL
+    assert f(FAKE, 64, FAKE, 0, 0, 64, None) == g.GPTQ_OK            # no tokens: no work
+    # partials beyond the fixed array: rejected
+    assert g.gptq_hessian_workspace_bytes(4096, 4096, g.GPTQ_BF16) > g.GPTQ_HESSIAN_STATIC_BYTES
+    assert f(FAKE, 4096, FAKE, 0, 4096, 4096, None) == g.GPTQ_EWORKSPACE
+    assert g.gptq_hessian_workspace_bytes(2048, 8192, g.GPTQ_BF16) > g.GPTQ_HESSIAN_STATIC_BYTES
+    assert f(FAKE, 2048, FAKE, 0, 8192, 2048, None) == g.GPTQ_EWORKSPACE
+    # the limit stated in the header is the one the binding uses
+    text = open(HEADER).read()
+    assert re.search(r"#define GPTQ_HESSIAN_STATIC_BYTES \(\(size_t\)64 << 20\)", text)
+    assert g.GPTQ_HESSIAN_STATIC_BYTES == 64 << 20
 
 
 @pytest.mark.parametrize("bits,cols", [(3, 40), (4, 12), (5, 64), (2, 8)])
