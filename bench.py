@@ -32,11 +32,10 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes per Hessian accumulation call on this workload (k_syrk_bf16 and k_syrk_reduce
-# together), from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by the reading
-# of a plain 1 GiB copy; the summary with the commands is
-# profiles/hbm_counters_q_proj_4096x4096_262144tok.md.  Valid only for the kernel source they
-# were taken on: a different k_hessian.hip reports traffic as null.
+# HBM bytes per Hessian accumulation call (k_syrk_bf16 and k_syrk_reduce together), from two
+# rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by the reading of a plain 1 GiB copy;
+# the summary with the commands is profiles/hbm_counters_q_proj_4096x4096_262144tok.md.  Valid
+# only for the kernel source they were taken on: a different k_hessian.hip reports null.
 SYRK_TRAFFIC = {"k_hessian_sha256": "ad5690e19bdd38695b7538e2e12ec82c1fec6b918d275b72c06b7738a3ebed1c",
                 "workload": "q_proj_4096", "tokens": 262144,
                 "fetch_bytes": 9210818884.9, "write_bytes": 492769221.3}
@@ -69,6 +68,10 @@ def parse():
                          "with all inputs resident (layers that share a Hessian reuse its factor)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the oracle over the whole layer (every token, every row) instead of a sample")
+    ap.add_argument("--no-second", action="store_true",
+                    help="skip the metric's second shape (11008x4096, 4-bit g128) on the default workload")
     return ap.parse_args()
 
 
@@ -85,41 +88,69 @@ def algorithmic(rows, cols, tokens, bits):
             "total_flop": float(hess) + factor + quant}
 
 
-def cpu_baseline(W, X_bits, rows, cols, tokens, bits, args, x_bf16=True, w_bf16=True):
-    """The oracle on the host cores, on a bounded sample, scaled to one full layer."""
-    from oracle import gptq_quantize, hessian_ref
-    from post_weight_quantization_03_amd import synth
+def cpu_info():
+    """The host the oracle runs on: core counts, CPU model and the BLAS libraries in use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), model)
+    except OSError:  # pragma: no cover
+        pass
+    blas = []
     try:
         from threadpoolctl import threadpool_info
-        threads = max((d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"),
-                      default=1)
+        blas = [{k: d.get(k) for k in ("internal_api", "version", "num_threads", "architecture")}
+                for d in threadpool_info() if d.get("user_api") == "blas"]
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    nt = min(args.cpu_tokens, tokens)
-    Xs = synth.bf16_to_f32(X_bits[:nt]) if x_bf16 else X_bits[:nt].astype(np.float32)
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count()
+    return {"cpu_count": os.cpu_count(), "affinity": affinity, "cpu_model": model, "blas": blas}
+
+
+def cpu_baseline(W, acts, rows, cols, tokens, bits, args, x_bf16=True, w_bf16=True):
+    """The oracle on the host cores: the Hessian over a token sample (or every token), the damped
+    factor of the full layer, and the lazy-batch GPTQ loop over a row sample (or every row), each
+    timed on its own and scaled to one full layer."""
+    from oracle import damp_ref, factor_ref, gptq_from_factor, hessian_ref
+    from post_weight_quantization_03_amd import synth
+    info = cpu_info()
+    threads = max([b["num_threads"] or 1 for b in info["blas"]] or [os.cpu_count() or 1])
+    nt = tokens if args.cpu_full else min(args.cpu_tokens, tokens)
+    nr = rows if args.cpu_full else min(args.cpu_rows, rows)
+
+    def chunks():
+        for t0 in range(0, nt, 16384):
+            blk = acts.block(t0, min(16384, nt - t0))
+            yield synth.bf16_to_f32(blk) if x_bf16 else blk
+
     t0 = time.perf_counter()
-    H = hessian_ref([Xs], cols)
+    H = hessian_ref(chunks(), cols)
     t_h = time.perf_counter() - t0
-    H = H * (tokens / nt)  # a same-law stand-in for the full-token Hessian
-    nr = min(args.cpu_rows, rows)
+    H *= tokens / nt  # a same-law stand-in for the full-token Hessian when sampled
     Ws = (synth.bf16_to_f32(W[:nr]) if w_bf16 else W[:nr]).astype(np.float64)
     t0 = time.perf_counter()
-    out = gptq_quantize(Ws, H, bits, 128, 0.01, blocksize=128)
-    t_fq = time.perf_counter() - t0
-    # split factor from loop: time the factor alone
-    from oracle import damp_ref, factor_ref
-    t0 = time.perf_counter()
-    Hd, _, _, _ = damp_ref(H, Ws[:1], 0.01)
-    factor_ref(Hd)
+    Hd, Ws, _, _ = damp_ref(H, Ws, 0.01)
+    U = factor_ref(Hd)
     t_f = time.perf_counter() - t0
-    t_q = max(t_fq - t_f, 0.0)
+    del H, Hd
+    t0 = time.perf_counter()
+    gptq_from_factor(Ws, U, bits, 128, blocksize=128)
+    t_q = time.perf_counter() - t0
     est = t_h * (tokens / nt) + t_f + t_q * (rows / nr)
-    del out
-    return {"value": 1.0 / est, "unit": "layers/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"fp64 NumPy oracle: Hessian over {nt} of {tokens} tokens (x{tokens / nt:g}), "
-                       f"full {cols}x{cols} factor, lazy-batch GPTQ loop over {nr} of {rows} rows "
-                       f"(x{rows / nr:g}); measured {t_h:.2f}s + {t_f:.2f}s + {t_q:.2f}s"),
-            "seconds_full_layer_est": est}
+    if args.cpu_full:
+        sample = (f"fp64 NumPy oracle over the whole layer: Hessian over all {tokens} tokens, {cols}x{cols} "
+                  f"factor, lazy-batch GPTQ loop over all {rows} rows; measured {t_h:.2f}s + {t_f:.2f}s + "
+                  f"{t_q:.2f}s")
+    else:
+        sample = (f"fp64 NumPy oracle: Hessian over {nt} of {tokens} tokens (x{tokens / nt:g}), "
+                  f"full {cols}x{cols} factor, lazy-batch GPTQ loop over {nr} of {rows} rows "
+                  f"(x{rows / nr:g}); measured {t_h:.2f}s + {t_f:.2f}s + {t_q:.2f}s")
+    return {"value": 1.0 / est, "unit": "layers/s", "cores": int(threads), "kind": "oracle", "sample": sample,
+            "seconds_full_layer": est, "measured_in_full": bool(args.cpu_full),
+            "stage_seconds": {"hessian": t_h, "factor": t_f, "quantize_loop": t_q}, "host": info}
 
 
 def gemv_measure(g, torch, packed, scales, zeros, rows, cols, bits, groupsize, dev, rounds=4):
@@ -257,7 +288,8 @@ def qep_measure(g, torch, Xd, Wd, n, dev):
     C = torch.zeros((n, n), dtype=torch.float32, device=dev)
     ws_h = torch.empty(max(g.gptq_hessian_workspace_bytes(n, Xd.shape[0], g.GPTQ_BF16), 1), dtype=torch.uint8,
                        device=dev)
-    ws_c = torch.empty(g.gptq_cross_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(max(g.gptq_cross_workspace_bytes(n, Xd.shape[0], g.GPTQ_BF16), 1), dtype=torch.uint8,
+                       device=dev)
     ws_q = torch.empty(g.gptq_qep_workspace_bytes(Wd.shape[0], n), dtype=torch.uint8, device=dev)
     Wout = torch.empty((Wd.shape[0], n), dtype=torch.float32, device=dev)
     dst = torch.zeros((1,), dtype=torch.int32, device=dev)
@@ -282,7 +314,7 @@ def qep_measure(g, torch, Xd, Wd, n, dev):
     t_q = float(np.mean(times["correct"])) / 1e3
     N = Xd.shape[0]
     flop_c = 2.0 * N * n * n
-    return {"kernels": "hipBLASLt bf16 GEMM (cross term); factor + k_gemm_f32 x3 (correction)",
+    return {"kernels": "k_syrk_bf16 cross mode + k_syrk_reduce (cross term); factor + k_gemm_f32 x3 (correction)",
             "tokens": N, "alpha": 0.5, "cross_ms": t_c * 1e3, "cross_tflops": flop_c / t_c / 1e12,
             "cross_frac_bf16_peak": flop_c / t_c / 1e12 / PEAK_BF16_TFLOPS,
             "correct_ms_incl_factor": t_q * 1e3}
@@ -439,33 +471,18 @@ def whole_workload(args, g, torch, wl, dev):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the Hessian would shard by tokens with one reduction, rows and layers are independent; "
-              "see the design notes)", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
-    import post_weight_quantization_03_amd as g
-    from post_weight_quantization_03_amd import synth
-
-    wl = synth.workload(args.workload, tokens=args.tokens)
-    if args.whole:
-        print(json.dumps(whole_workload(args, g, torch, wl, torch.device("cuda:0"))), flush=True)
-        return
-    lin = wl.linears[args.layer]
-    acts = wl.hessians[lin.hessian]
-    rows, cols, tokens, bits = lin.rows, lin.cols, acts.tokens, lin.bits
-    dev = torch.device("cuda:0")
+def time_layer(args, g, torch, wl, lin, acts, bits, dev, workload_name, description=None):
+    """Times args.steps passes over one layer (H = 0, Hessian, factor and quantize loop, pack)
+    after args.warmup untimed ones, with the inputs resident in HBM.  Returns the record and the
+    device tensors the measurements outside the step reuse."""
+    rows, cols, tokens = lin.rows, lin.cols, acts.tokens
     t0 = time.perf_counter()
     X_bits = acts.full()
     W_bits = lin.weight()
     gen_s = time.perf_counter() - t0
     x_bf16 = acts.bf16
     Xd = host_tensor(torch, X_bits, x_bf16).to(dev)
+    del X_bits
     Wd = host_tensor(torch, W_bits, lin.bf16).to(dev)
     params = g.Params(bits=bits, groupsize=wl.groupsize, blocksize=wl.blocksize, damp=wl.damp)
     G = -(-cols // wl.groupsize)
@@ -539,8 +556,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if x_bf16 else "f32",
         "data": "synthetic",
-        "config": {"workload": wl.description, "layer": lin.name, "rows": rows, "cols": cols, "tokens": tokens, "bits": bits,
-                   "groupsize": wl.groupsize, "blocksize": wl.blocksize, "damp": wl.damp},
+        "config": {"workload": description or wl.description, "layer": lin.name, "rows": rows, "cols": cols,
+                   "tokens": tokens, "bits": bits, "groupsize": wl.groupsize, "blocksize": wl.blocksize,
+                   "damp": wl.damp},
         "tflops": alg["total_flop"] / step_s / 1e12,
         "stages_ms": {"hessian": t_h * 1e3, "factor_and_quantize": t_q * 1e3, "pack": t_p * 1e3},
         "stage_tflops": {"hessian_bf16_mfma" if x_bf16 else "hessian_f32_mfma": hess_tflops,
@@ -550,20 +568,47 @@ def main():
                      "kernel": ("k_syrk_bf16" if x_bf16 else "k_syrk_f32") + " + k_syrk_reduce (one Hessian call)",
                      "achieved": hess_tflops,
                      "peak": hess_peak, "unit": "TFLOP/s", "frac": hess_tflops / hess_peak,
-                     "traffic": syrk_traffic(args.workload, tokens),
+                     "traffic": syrk_traffic(workload_name, tokens),
                      "algorithmic_bytes": alg["x_bytes"] + 4.0 * cols * cols},
         "input_generation_s": gen_s,
     }
-    if not args.no_extras and not (x_bf16 and lin.bf16):
+    state = {"W_bits": W_bits, "Xd": Xd, "Wd": Wd, "packed": packed, "scales": scales, "zeros": zeros,
+             "x_bf16": x_bf16, "w_bf16": lin.bf16}
+    return rec, state
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the Hessian would shard by tokens with one reduction, rows and layers are independent; "
+              "see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import post_weight_quantization_03_amd as g
+    from post_weight_quantization_03_amd import synth
+
+    wl = synth.workload(args.workload, tokens=args.tokens)
+    dev = torch.device("cuda:0")
+    if args.whole:
+        print(json.dumps(whole_workload(args, g, torch, wl, dev)), flush=True)
+        return
+    lin = wl.linears[args.layer]
+    acts = wl.hessians[lin.hessian]
+    rows, cols, tokens, bits = lin.rows, lin.cols, acts.tokens, lin.bits
+    rec, st = time_layer(args, g, torch, wl, lin, acts, bits, dev, args.workload)
+    if not args.no_extras and not (st["x_bf16"] and st["w_bf16"]):
         rec["extras"] = "skipped: the rotation, correction and GEMV measurements take bf16 weights and activations"
     elif not args.no_extras:
         # measurements outside the timed step; a failure is reported in its field and
         # does not take the step's line with it
         extras = {
-            "hadamard_rotation": lambda: hadamard_measure(g, torch, Wd, cols, dev),
-            "qep_correction": lambda: qep_measure(g, torch, Xd, Wd, cols, dev),
-            "dequant_gemv": lambda: gemv_measure(g, torch, packed, scales, zeros, rows, cols, bits, wl.groupsize,
-                                                 dev),
+            "hadamard_rotation": lambda: hadamard_measure(g, torch, st["Wd"], cols, dev),
+            "qep_correction": lambda: qep_measure(g, torch, st["Xd"], st["Wd"], cols, dev),
+            "dequant_gemv": lambda: gemv_measure(g, torch, st["packed"], st["scales"], st["zeros"], rows, cols,
+                                                 bits, wl.groupsize, dev),
         }
         for name, fn in extras.items():
             try:
@@ -572,8 +617,27 @@ def main():
                 rec[name] = {"error": f"{type(ex).__name__}: {ex}"}
                 print(f"bench.py: {name} failed: {ex}", file=sys.stderr)
             torch.cuda.empty_cache()
+    W_bits = st["W_bits"]
+    x_bf16, w_bf16 = st["x_bf16"], st["w_bf16"]
+    del st
+    torch.cuda.empty_cache()
+    if args.workload == "q_proj_4096" and args.layer == 0 and args.tokens is None and not args.no_second:
+        # the metric's second shape: a Llama-2-7B gate_proj-shaped layer (11008 x 4096) at 4-bit
+        # g128, on its own 131072-token Hessian of the MLP input law
+        wl2 = synth.workload("mlp_7b")
+        lin2 = wl2.linears[0]
+        desc = ("Llama-2-7B gate_proj 11008x4096 bf16 ~N(0,0.02^2), X 131072x4096 bf16 t4 with 41 outlier "
+                "channels x20, 4-bit g128")
+        rec2, st2 = time_layer(args, g, torch, wl2, lin2, wl2.hessians[lin2.hessian], 4, dev, "gate_proj_4bit",
+                               desc)
+        del st2
+        torch.cuda.empty_cache()
+        rec["shape_11008x4096"] = {k: rec2[k] for k in ("value", "unit", "ms_per_step", "config", "tflops",
+                                                        "stages_ms", "stage_tflops", "quantize_only_layers_per_s",
+                                                        "roofline")}
+        rec["both_shapes_layers_per_s"] = 2.0 / (rec["ms_per_step"] / 1e3 + rec2["ms_per_step"] / 1e3)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(W_bits, X_bits, rows, cols, tokens, bits, args, x_bf16, lin.bf16)
+        rec["cpu_baseline"] = cpu_baseline(W_bits, acts, rows, cols, tokens, bits, args, x_bf16, w_bf16)
     print(json.dumps(rec), flush=True)
 
 

@@ -19,9 +19,9 @@
  * Conventions for every call
  *   - Tensor pointers are DEVICE pointers owned by the caller.  Row-major.
  *   - Work is queued on `stream` in order; calls return before the GPU is done
- *     unless stated otherwise.  The library allocates and frees no memory,
- *     except the per-device hipBLASLt handle that gptq_accumulate_cross
- *     creates on its first call on a device.
+ *     unless stated otherwise.  The library allocates and frees no memory:
+ *     scratch memory is the caller's workspace argument (or, for
+ *     gptq_accumulate_hessian_static, a fixed device array of the library).
  *   - Return 0 (GPTQ_OK) on success, a positive gptq_status otherwise.
  *     Argument errors are detected on the host and return before any launch.
  *   - Calls that share a workspace or an output buffer on one device must not
@@ -251,15 +251,18 @@ int gptq_hadamard_hessian(float* H, int64_t n, const float* signs, int32_t block
  *   ||X W^T - Xq W'^T||^2 + (lambda / 2) ||W' - W||^2;  alpha = 0 is plain GPTQ.
  * ------------------------------------------------------------------------- */
 
-/* Workspace bytes for gptq_accumulate_cross (hipBLASLt's, a fixed 64 MiB). */
-size_t gptq_cross_workspace_bytes(int64_t n);
+/* Workspace bytes for gptq_accumulate_cross over `tokens` tokens: the split-K
+ * partial tiles, as for the Hessian (0 when the tokens are not split). */
+size_t gptq_cross_workspace_bytes(int64_t n, int64_t tokens, gptq_dtype x_dtype);
 
 /* C[n, n] += 2 X^T Xq over one chunk of tokens.  X and Xq: [tokens, n], the same
- * dtype (bf16 or fp32) and row stride ldx >= n.  C is fp32, not symmetric; the
- * caller zero-fills it before the first chunk.  One plain GEMM through
- * hipBLASLt (bf16 products exact, fp32 accumulation).  The first call on a
- * device creates that device's hipBLASLt handle, which holds its own memory
- * until the process ends.  tokens == 0 or n == 0: no work. */
+ * dtype (bf16 or fp32) and row stride ldx >= n.  C is fp32, not symmetric
+ * (C[i][j] pairs column i of X with column j of Xq); the caller zero-fills it
+ * before the first chunk.  The Hessian's MFMA kernels in their cross mode:
+ * every tile of the square grid, bf16 products exact in fp32, fp32
+ * accumulation in a fixed order (bit-reproducible run to run).  workspace:
+ * gptq_cross_workspace_bytes(n, tokens, x_dtype) bytes, 256-byte aligned (may be
+ * 0 bytes, then NULL is accepted).  tokens == 0 or n == 0: no work. */
 int gptq_accumulate_cross(float* C, int64_t n, const void* X, const void* Xq, gptq_dtype x_dtype, int64_t tokens,
                           int64_t ldx, void* workspace, size_t workspace_bytes, gptq_stream_t stream);
 

@@ -84,7 +84,7 @@ def lib():
     L.gptq_hadamard_rows.restype = ctypes.c_int
     L.gptq_hadamard_hessian.argtypes = [vp, i64, vp, i32, vp]
     L.gptq_hadamard_hessian.restype = ctypes.c_int
-    L.gptq_cross_workspace_bytes.argtypes = [i64]
+    L.gptq_cross_workspace_bytes.argtypes = [i64, i64, ctypes.c_int]
     L.gptq_cross_workspace_bytes.restype = sz
     L.gptq_accumulate_cross.argtypes = [vp, i64, vp, vp, ctypes.c_int, i64, i64, vp, sz, vp]
     L.gptq_accumulate_cross.restype = ctypes.c_int
@@ -307,8 +307,8 @@ def gptq_hadamard_hessian(H, signs, block: int, stream=None):
     return H
 
 
-def gptq_cross_workspace_bytes(n: int) -> int:
-    return int(lib().gptq_cross_workspace_bytes(n))
+def gptq_cross_workspace_bytes(n: int, tokens: int, x_dtype: int) -> int:
+    return int(lib().gptq_cross_workspace_bytes(n, tokens, x_dtype))
 
 
 def gptq_accumulate_cross(C, X, Xq, workspace=None, stream=None):
@@ -321,7 +321,7 @@ def gptq_accumulate_cross(C, X, Xq, workspace=None, stream=None):
             or not Xq.is_cuda):
         raise ValueError("shape, dtype or stride mismatch")
     if workspace is None:
-        workspace = _workspace(gptq_cross_workspace_bytes(n), C, stream)
+        workspace = _workspace(gptq_cross_workspace_bytes(n, X.shape[0], _dtype_code(X)), C, stream)
     st = lib().gptq_accumulate_cross(_ptr(C), n, _ptr(X), _ptr(Xq), _dtype_code(X), X.shape[0], X.stride(0),
                                      _ptr(workspace), workspace.numel(), _stream(stream))
     if st:

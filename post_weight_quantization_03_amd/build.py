@@ -48,8 +48,7 @@ def build_gptq() -> str:
         objs = list(ex.map(compile_one, srcs))
     out = os.path.join(PKG, "libgptq.so")
     tmp = out + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp, "-L/opt/rocm/lib",
-          "-lhipblaslt"])
+    _run([HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp])
     os.replace(tmp, out)
     return out
 

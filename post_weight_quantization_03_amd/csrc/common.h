@@ -128,8 +128,9 @@ hipError_t hadamard_rows(const void* in, bool in_bf16, int64_t ld_in, float* out
 hipError_t hadamard_hessian(float* H, int64_t n, const float* signs, int block, hipStream_t stream);
 
 // Error-propagation correction (k_qep.hip).
-size_t cross_workspace(int64_t n);
-int cross_launch(float* C, int64_t n, const void* X, const void* Xq, bool bf16, int64_t tokens, int64_t ldx,
+// Cross term C += 2 X^T Xq: the Hessian kernels in their cross mode (k_hessian.hip).
+size_t cross_workspace(int64_t n, int64_t tokens, gptq_dtype dt);
+int cross_launch(float* C, int64_t n, const void* X, const void* Xq, gptq_dtype dt, int64_t tokens, int64_t ldx,
                  void* ws, size_t ws_bytes, hipStream_t stream);
 hipError_t qep_correct_run(const void* W, bool w_bf16, int64_t rows, int64_t n, float* C, float* H, float damp,
                            float alpha, float* W_out, const FactorWs& f, float* P1, float* P2, float* T,

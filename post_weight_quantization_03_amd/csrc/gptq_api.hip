@@ -313,9 +313,10 @@ int gptq_hadamard_hessian(float* H, int64_t n, const float* signs, int32_t block
   return hadamard_hessian(H, n, signs, block, (hipStream_t)stream) == hipSuccess ? GPTQ_OK : GPTQ_EHIP;
 }
 
-size_t gptq_cross_workspace_bytes(int64_t n) {
-  if (n <= 0 || n > MAX_DIM) return 0;
-  return cross_workspace(n);
+size_t gptq_cross_workspace_bytes(int64_t n, int64_t tokens, gptq_dtype x_dtype) {
+  if (n <= 0 || tokens <= 0 || n > MAX_DIM || tokens > MAX_DIM) return 0;
+  if (!(x_dtype == GPTQ_BF16 || x_dtype == GPTQ_F32)) return 0;
+  return cross_workspace(n, tokens, x_dtype);
 }
 
 int gptq_accumulate_cross(float* C, int64_t n, const void* X, const void* Xq, gptq_dtype x_dtype, int64_t tokens,
@@ -324,9 +325,10 @@ int gptq_accumulate_cross(float* C, int64_t n, const void* X, const void* Xq, gp
   if (!(x_dtype == GPTQ_BF16 || x_dtype == GPTQ_F32)) return GPTQ_EINVAL;
   if (n == 0 || tokens == 0) return GPTQ_OK;
   if (!C || !X || !Xq || ldx < n) return GPTQ_EINVAL;
-  if (workspace_bytes < cross_workspace(n) || !workspace) return GPTQ_EWORKSPACE;
-  return cross_launch(C, n, X, Xq, x_dtype == GPTQ_BF16, tokens, ldx, workspace, workspace_bytes,
-                      (hipStream_t)stream);
+  if (n * n > ((int64_t)1 << 31) * 2) return GPTQ_EUNSUPPORTED;
+  const size_t need = cross_workspace(n, tokens, x_dtype);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return GPTQ_EWORKSPACE;
+  return cross_launch(C, n, X, Xq, x_dtype, tokens, ldx, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 namespace {

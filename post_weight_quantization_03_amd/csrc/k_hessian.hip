@@ -36,6 +36,11 @@
 // does not depend on scheduling.  Tiles that would make up a last, mostly
 // empty round of an XCD run as shorter token pieces instead, so that round
 // keeps every CU busy.
+//
+// Cross term (CROSS = true): the same kernels compute C += 2 X^T Xq for two
+// activation matrices of one shape, the B operand streamed from Xq.  C is not
+// symmetric, so every tile of the square grid is computed and written once,
+// with no mirror and no diagonal specialisation.
 #include <algorithm>
 #include <type_traits>
 
@@ -46,12 +51,13 @@ namespace {
 
 struct SyrkArgs {
   const void* X;
+  const void* X2;  // source of the B operand: X for the Hessian, Xq for the cross term
   float* H;
   float* part;     // partial tiles, [slots][tile * tile] (S > 1)
   int64_t ldx;
   int n, tokens;
   int nbt;         // tiles per dimension
-  int T;           // upper tiles
+  int T;           // upper tiles (Hessian) or all tiles (cross term)
   int S;           // token splits
   int tps;         // tokens per split
   int full;        // tiles computed whole per split; tiles full .. T-1 run in pieces
@@ -181,6 +187,38 @@ __device__ __forceinline__ void decode_upper(int t, int nbt, int& I, int& J) {
   J = i + (t - base);
 }
 
+// Cross term with one token split: the square tile grid in supertiles of 4
+// block rows x 8 block columns (the whole ones first, row-major), then the
+// tiles outside them row-major; rounds of 256 items are spread over the XCDs
+// as in decode_supertiles, so each XCD runs one supertile at a time.  A
+// bijection onto the nbt^2 tiles.
+__device__ __forceinline__ void decode_square_supertiles(int i, int nbt, int T, int& I, int& J) {
+  const int R = T / 256;
+  int t = i;
+  if (i < R * 256) {
+    const int x = i & 7, m = i >> 3;
+    t = 32 * (8 * (m >> 5) + x) + (m & 31);
+  }
+  const int SR = nbt / 4, SC = nbt / 8;
+  const int F = SR * SC * 32;
+  if (t < F) {
+    const int sup = t >> 5, w = t & 31;
+    I = 4 * (sup / SC) + (w >> 3);
+    J = 8 * (sup % SC) + (w & 7);
+    return;
+  }
+  int k = t - F;
+  const int wA = nbt - 8 * SC;  // columns right of the whole supertiles, rows inside them
+  if (k < 4 * SR * wA) {
+    I = k / wA;
+    J = 8 * SC + k % wA;
+    return;
+  }
+  k -= 4 * SR * wA;
+  I = 4 * SR + k / nbt;
+  J = k % nbt;
+}
+
 // acc[i][j] is the 32x32 block (i, j) of this wave's (32 WB) x (32 WB) quarter.
 // H += 2 acc on the upper triangle, mirrored into the lower one.  The 16 H
 // values a lane adds to in one block are loaded together, one block ahead of
@@ -188,7 +226,7 @@ __device__ __forceinline__ void decode_upper(int t, int nbt, int& I, int& J) {
 // full memory round trip before its store (the compiler cannot move a load
 // above a store that might alias it), which under the streaming load of the
 // other workgroups costs hundreds of microseconds per tile.
-template <int TILE, int WB>
+template <int TILE, int WB, bool CROSS>
 __device__ __forceinline__ void load_block(const SyrkArgs& a, int I, int J, int b, int lane, int wm, int wn,
                                            float (&h)[16]) {
   const int n = a.n;
@@ -197,21 +235,21 @@ __device__ __forceinline__ void load_block(const SyrkArgs& a, int I, int J, int 
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int gr = I * TILE + wm * 32 * WB + 32 * i + acc_row(r, lane);
-    h[r] = (gr < n && gc < n && gr <= gc) ? a.H[(int64_t)gr * n + gc] : 0.f;
+    h[r] = (gr < n && gc < n && (CROSS || gr <= gc)) ? a.H[(int64_t)gr * n + gc] : 0.f;
   }
 }
 
-template <int TILE, int WB>
+template <int TILE, int WB, bool CROSS>
 __device__ __forceinline__ void write_tile(const SyrkArgs& a, int I, int J, f32x16 (&acc)[WB][WB], int lane,
                                            int wm, int wn) {
   const int n = a.n;
   const bool vec_mirror = a.h_vec != 0;
   float hc[16], hn[16];
-  load_block<TILE, WB>(a, I, J, 0, lane, wm, wn, hc);
+  load_block<TILE, WB, CROSS>(a, I, J, 0, lane, wm, wn, hc);
 #pragma unroll
   for (int b = 0; b < WB * WB; ++b) {
     const int i = b / WB, j = b % WB;
-    if (b + 1 < WB * WB) load_block<TILE, WB>(a, I, J, b + 1, lane, wm, wn, hn);
+    if (b + 1 < WB * WB) load_block<TILE, WB, CROSS>(a, I, J, b + 1, lane, wm, wn, hn);
     const int gc = J * TILE + wn * 32 * WB + 32 * j + acc_col(lane);
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -221,10 +259,10 @@ __device__ __forceinline__ void write_tile(const SyrkArgs& a, int I, int J, f32x
       for (int e = 0; e < 4; ++e) {
         const int gr = gr0 + e;
         v[e] = hc[4 * r4 + e] + 2.0f * acc[i][j][4 * r4 + e];
-        if (gr < n && gc < n && gr <= gc) a.H[(int64_t)gr * n + gc] = v[e];
+        if (gr < n && gc < n && (CROSS || gr <= gc)) a.H[(int64_t)gr * n + gc] = v[e];
       }
       // mirror: rows gr0..gr0+3 of column gc become four consecutive floats of row gc
-      if (gc < n) {
+      if (!CROSS && gc < n) {
         float* m = a.H + (int64_t)gc * n + gr0;
         if (vec_mirror && gr0 + 3 < gc && gr0 + 3 < n) {
           *reinterpret_cast<float4*>(m) = make_float4(v[0], v[1], v[2], v[3]);
@@ -260,17 +298,21 @@ __device__ __forceinline__ void store_partial(const SyrkArgs& a, int slot, f32x1
 // coordinates of the four values, as write_tile does.  Each thread has eight
 // partial loads in flight at a time; the whole chip runs the reduction, so it
 // is bound by HBM bandwidth rather than by one workgroup's memory latency.
-template <int TILE, int WB>
+template <int TILE, int WB, bool CROSS>
 __global__ __launch_bounds__(256) void k_syrk_reduce(SyrkArgs a) {
   constexpr int PARTIAL4 = TILE * TILE / 4;
   const int tile = blockIdx.x, k = blockIdx.y, tid = threadIdx.x;
   int I, J;
-  if constexpr (TILE == 256)
+  if constexpr (CROSS) {
+    I = tile / a.nbt;
+    J = tile % a.nbt;
+  } else if constexpr (TILE == 256) {
     decode_offdiag_first(tile, a.nbt, I, J);
-  else
+  } else {
     decode_upper(tile, a.nbt, I, J);
+  }
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-  if (I == J && wm > wn) return;  // quarter below the diagonal: not computed
+  if (!CROSS && I == J && wm > wn) return;  // quarter below the diagonal: not computed
   const int i = k / (4 * WB), j = (k / 4) % WB, r4 = k % 4;
   int first, count;
   tile_slots(a, tile, first, count);
@@ -296,15 +338,15 @@ __global__ __launch_bounds__(256) void k_syrk_reduce(SyrkArgs a) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int gr = gr0 + e;
-    h[e] = (gr < n && gc < n && gr <= gc) ? a.H[(int64_t)gr * n + gc] : 0.f;
+    h[e] = (gr < n && gc < n && (CROSS || gr <= gc)) ? a.H[(int64_t)gr * n + gc] : 0.f;
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int gr = gr0 + e;
     v[e] = h[e] + 2.0f * sum[e];
-    if (gr < n && gc < n && gr <= gc) a.H[(int64_t)gr * n + gc] = v[e];
+    if (gr < n && gc < n && (CROSS || gr <= gc)) a.H[(int64_t)gr * n + gc] = v[e];
   }
-  if (gc < n) {
+  if (!CROSS && gc < n) {
     float* m = a.H + (int64_t)gc * n + gr0;
     if (a.h_vec && gr0 + 3 < gc && gr0 + 3 < n) {
       *reinterpret_cast<float4*>(m) = make_float4(v[0], v[1], v[2], v[3]);
@@ -481,7 +523,7 @@ __device__ __forceinline__ void mfma_frags(const StageFrags& f, f32x16 (&acc)[4]
 // barrier that retired its loads (reading a buffer straight after that
 // barrier returned stale data on this hardware).  The buffers are distinct
 // LDS objects, so fragment reads never wait for loads into another buffer.
-template <bool FULL>
+template <bool FULL, bool CROSS>
 __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
   __shared__ __attribute__((aligned(16))) char B0[2 * STAGEB];
   __shared__ __attribute__((aligned(16))) char B1[2 * STAGEB];
@@ -490,11 +532,20 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
 
   const Item it = decode_item(a, blockIdx.x);
   int I, J;
-  if (a.S == 1)
-    decode_supertiles(blockIdx.x, a.nbt, a.T, I, J);
-  else
-    decode_offdiag_first(it.tile, a.nbt, I, J);
-  const bool diag = (I == J);
+  if constexpr (CROSS) {
+    if (a.S == 1) {
+      decode_square_supertiles(blockIdx.x, a.nbt, a.T, I, J);
+    } else {
+      I = it.tile / a.nbt;
+      J = it.tile % a.nbt;
+    }
+  } else {
+    if (a.S == 1)
+      decode_supertiles(blockIdx.x, a.nbt, a.T, I, J);
+    else
+      decode_offdiag_first(it.tile, a.nbt, I, J);
+  }
+  const bool diag = !CROSS && (I == J);
   const int t0 = it.t0, t1 = it.t1;
   const int nst = t1 > t0 ? (t1 - t0 + KB - 1) / KB : 0;
 
@@ -504,6 +555,7 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   const bool idle = diag && wm > wn;  // quarter strictly below the diagonal
   const uint16_t* X = static_cast<const uint16_t*>(a.X);
+  const uint16_t* X2 = static_cast<const uint16_t*>(a.X2);
   const int colA = I * TB, colB = J * TB;
   const bool fullA = a.h_vec_x && colA + TB <= a.n;
   const bool fullB = a.h_vec_x && colB + TB <= a.n;
@@ -524,7 +576,7 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
   }
   const int64_t stage_step = (int64_t)KB * a.ldx;
   DirectSrc dA = direct_src(a, X, colA, t0, wave, lane);
-  DirectSrc dB = direct_src(a, X, colB, t0, wave, lane);
+  DirectSrc dB = direct_src(a, X2, colB, t0, wave, lane);
 
   // stages are issued in order, so the direct sources simply advance
   auto issue = [&](int st, char* buf) {
@@ -543,7 +595,7 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
       if (full_t && fullB)
         stage_direct<false>(dB, buf + STAGEB, wave, stage_step);
       else
-        stage_guarded(a, X, colB, t, t1, buf + STAGEB);
+        stage_guarded(a, X2, colB, t, t1, buf + STAGEB);
     }
   };
   auto rd = [&](const char* buf, StageFrags& f) {
@@ -664,7 +716,7 @@ __global__ __launch_bounds__(256, 1) void k_syrk_bf16(SyrkArgs a) {
   if (a.S > 1)
     store_partial<TB, 4>(a, it.slot, acc);
   else if (!idle)
-    write_tile<TB, 4>(a, I, J, acc, lane, wm, wn);
+    write_tile<TB, 4, CROSS>(a, I, J, acc, lane, wm, wn);
 }
 
 // ------------------------------------------------------------------ fp32 path
@@ -700,19 +752,25 @@ __device__ __forceinline__ void store_f32(float (*Xs)[F32_PITCH], const float4 (
   }
 }
 
-template <bool VEC>
+template <bool VEC, bool CROSS>
 __global__ __launch_bounds__(256) void k_syrk_f32(SyrkArgs a) {
   __shared__ __attribute__((aligned(16))) float As[2][KT_F32][F32_PITCH];
   __shared__ __attribute__((aligned(16))) float Bs[2][KT_F32][F32_PITCH];
 
   const Item it = decode_item(a, blockIdx.x);
   int I, J;
-  decode_upper(it.tile, a.nbt, I, J);
-  const bool diag = (I == J);
+  if constexpr (CROSS) {
+    I = it.tile / a.nbt;
+    J = it.tile % a.nbt;
+  } else {
+    decode_upper(it.tile, a.nbt, I, J);
+  }
+  const bool diag = !CROSS && (I == J);
   const int t0 = it.t0, t1 = it.t1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const float* X = static_cast<const float*>(a.X);
+  const float* X2 = static_cast<const float*>(a.X2);
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -725,7 +783,7 @@ __global__ __launch_bounds__(256) void k_syrk_f32(SyrkArgs a) {
   if (t0 < t1) {
     float4 va[2], vb[2];
     load_f32<VEC>(a, X, I * TF, t0, t1, va);
-    if (!diag) load_f32<VEC>(a, X, J * TF, t0, t1, vb);
+    if (!diag) load_f32<VEC>(a, X2, J * TF, t0, t1, vb);
     store_f32(As[0], va);
     if (!diag) store_f32(Bs[0], vb);
     __syncthreads();
@@ -734,7 +792,7 @@ __global__ __launch_bounds__(256) void k_syrk_f32(SyrkArgs a) {
       const bool more = t + KT_F32 < t1;
       if (more) {
         load_f32<VEC>(a, X, I * TF, t + KT_F32, t1, va);
-        if (!diag) load_f32<VEC>(a, X, J * TF, t + KT_F32, t1, vb);
+        if (!diag) load_f32<VEC>(a, X2, J * TF, t + KT_F32, t1, vb);
       }
       float(*Bsrc)[F32_PITCH] = diag ? As[buf] : Bs[buf];
 #pragma unroll
@@ -761,7 +819,7 @@ __global__ __launch_bounds__(256) void k_syrk_f32(SyrkArgs a) {
   if (a.S > 1)
     store_partial<TF, 2>(a, it.slot, acc);
   else
-    write_tile<TF, 2>(a, I, J, acc, lane, wm, wn);
+    write_tile<TF, 2, CROSS>(a, I, J, acc, lane, wm, wn);
 }
 
 struct Plan {
@@ -783,11 +841,11 @@ int cu_count() {
 // tiles left over for a last partial round are cut into token pieces so that
 // they fill that round.  fp32 (small problems): enough items for the chip
 // with at least 512 tokens per split.
-Plan plan(int64_t n, int64_t tokens, gptq_dtype dt) {
+Plan plan(int64_t n, int64_t tokens, gptq_dtype dt, bool cross = false) {
   Plan p{};
   p.tile = dt == GPTQ_BF16 ? TB : TF;
   p.nbt = (int)((n + p.tile - 1) / p.tile);
-  p.T = p.nbt * (p.nbt + 1) / 2;
+  p.T = cross ? p.nbt * p.nbt : p.nbt * (p.nbt + 1) / 2;
   const int kt = dt == GPTQ_BF16 ? KB : KT_F32;
   int64_t s;
   if (dt == GPTQ_BF16) {
@@ -824,18 +882,22 @@ Plan plan(int64_t n, int64_t tokens, gptq_dtype dt) {
 
 }  // namespace
 
-size_t hessian_workspace(int64_t n, int64_t tokens, gptq_dtype dt) {
+namespace {
+
+size_t syrk_workspace(int64_t n, int64_t tokens, gptq_dtype dt, bool cross) {
   if (n <= 0 || tokens <= 0) return 0;
-  const Plan p = plan(n, tokens, dt);
+  const Plan p = plan(n, tokens, dt, cross);
   if (p.S == 1) return 0;
   return align_up((size_t)p.slots * p.tile * p.tile * sizeof(float), 256);
 }
 
-int hessian_launch(float* H, int64_t n, const void* X, gptq_dtype dt, int64_t tokens, int64_t ldx, void* ws,
-                   size_t ws_bytes, hipStream_t stream) {
-  const Plan p = plan(n, tokens, dt);
+template <bool CROSS>
+int syrk_launch(float* H, int64_t n, const void* X, const void* X2, gptq_dtype dt, int64_t tokens, int64_t ldx,
+                void* ws, size_t ws_bytes, hipStream_t stream) {
+  const Plan p = plan(n, tokens, dt, CROSS);
   SyrkArgs a{};
   a.X = X;
+  a.X2 = X2;
   a.H = H;
   a.ldx = ldx;
   a.n = (int)n;
@@ -849,26 +911,45 @@ int hessian_launch(float* H, int64_t n, const void* X, gptq_dtype dt, int64_t to
   a.tpp = p.tpp;
   a.h_vec = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(H) & 15) == 0);
   if (p.S > 1) {
-    if (ws_bytes < hessian_workspace(n, tokens, dt) || ws == nullptr) return GPTQ_EWORKSPACE;
+    if (ws_bytes < syrk_workspace(n, tokens, dt, CROSS) || ws == nullptr) return GPTQ_EWORKSPACE;
     a.part = static_cast<float*>(ws);
   }
-  const dim3 grid((unsigned)((p.full + (p.T - p.full) * p.P) * p.S));
+  const int64_t items = ((int64_t)p.full + (int64_t)(p.T - p.full) * p.P) * p.S;
+  if (items > INT32_MAX) return GPTQ_EUNSUPPORTED;
+  const dim3 grid((unsigned)items);
+  const auto aligned16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
   if (dt == GPTQ_BF16) {
-    a.h_vec_x = (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+    a.h_vec_x = (ldx % 8 == 0) && aligned16(X) && aligned16(X2);
     if (a.h_vec_x && n % TB == 0 && tokens % KB == 0)
-      hipLaunchKernelGGL(k_syrk_bf16<true>, grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_syrk_bf16<true, CROSS>), grid, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL(k_syrk_bf16<false>, grid, dim3(256), 0, stream, a);
-    if (p.S > 1) hipLaunchKernelGGL((k_syrk_reduce<TB, 4>), dim3(p.T, 64), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_syrk_bf16<false, CROSS>), grid, dim3(256), 0, stream, a);
+    if (p.S > 1) hipLaunchKernelGGL((k_syrk_reduce<TB, 4, CROSS>), dim3(p.T, 64), dim3(256), 0, stream, a);
   } else {
-    const bool vec = (ldx % 4 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+    const bool vec = (ldx % 4 == 0) && aligned16(X) && aligned16(X2);
     if (vec)
-      hipLaunchKernelGGL(k_syrk_f32<true>, grid, dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_syrk_f32<true, CROSS>), grid, dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL(k_syrk_f32<false>, grid, dim3(256), 0, stream, a);
-    if (p.S > 1) hipLaunchKernelGGL((k_syrk_reduce<TF, 2>), dim3(p.T, 16), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_syrk_f32<false, CROSS>), grid, dim3(256), 0, stream, a);
+    if (p.S > 1) hipLaunchKernelGGL((k_syrk_reduce<TF, 2, CROSS>), dim3(p.T, 16), dim3(256), 0, stream, a);
   }
   return hipGetLastError() == hipSuccess ? GPTQ_OK : GPTQ_EHIP;
+}
+
+}  // namespace
+
+size_t hessian_workspace(int64_t n, int64_t tokens, gptq_dtype dt) { return syrk_workspace(n, tokens, dt, false); }
+
+int hessian_launch(float* H, int64_t n, const void* X, gptq_dtype dt, int64_t tokens, int64_t ldx, void* ws,
+                   size_t ws_bytes, hipStream_t stream) {
+  return syrk_launch<false>(H, n, X, X, dt, tokens, ldx, ws, ws_bytes, stream);
+}
+
+size_t cross_workspace(int64_t n, int64_t tokens, gptq_dtype dt) { return syrk_workspace(n, tokens, dt, true); }
+
+int cross_launch(float* C, int64_t n, const void* X, const void* Xq, gptq_dtype dt, int64_t tokens, int64_t ldx,
+                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  return syrk_launch<true>(C, n, X, Xq, dt, tokens, ldx, ws, ws_bytes, stream);
 }
 
 }  // namespace gptq

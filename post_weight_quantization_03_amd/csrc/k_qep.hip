@@ -7,17 +7,13 @@
 //   C = 2 X^T X^ (cross term), H^ = 2 X^T X^ (the GPTQ Hessian of X^),
 //   H_d = H^ + lambda I with GPTQ's damping and dead-column rule.
 //
-// The cross term is one plain GEMM over the tokens: bf16 (or fp32) inputs,
-// fp32 accumulation, through hipBLASLt.  The correction factors H^ in place
-// with the quantizer's own factor (H_d^-1 = U^T U, H then holds U exactly as
-// the quantizer leaves it, so the layer is quantized next with the factor
-// reused), and applies H_d^-1 as two triangular products with the library's
-// fp32 MFMA GEMM: W' = W + alpha ((W G) U^T) U (the U^T product skips the
-// zero half of its K range).
-#include <hipblaslt/hipblaslt.h>
-
-#include <mutex>
-
+// The cross term is the Hessian's SYRK kernel in its cross mode (every tile
+// of the square grid, the B operand from X^; k_hessian.hip).  The correction
+// factors H^ in place with the quantizer's own factor (H_d^-1 = U^T U, H then
+// holds U exactly as the quantizer leaves it, so the layer is quantized next
+// with the factor reused), and applies H_d^-1 as two triangular products with
+// the library's fp32 MFMA GEMM: W' = W + alpha ((W G) U^T) U (the U^T product
+// skips the zero half of its K range).
 #include "common.h"
 
 namespace gptq {
@@ -48,71 +44,7 @@ unsigned blocks_for(int64_t count) {
   return (unsigned)(b < 8192 ? (b > 0 ? b : 1) : 8192);
 }
 
-// One hipBLASLt handle per device, created on the device's first cross-term call.
-hipblasLtHandle_t lt_handle(int dev) {
-  static std::mutex mu;
-  static hipblasLtHandle_t handles[64] = {};
-  std::lock_guard<std::mutex> lock(mu);
-  if (dev < 0 || dev >= 64) return nullptr;
-  if (!handles[dev] && hipblasLtCreate(&handles[dev]) != HIPBLAS_STATUS_SUCCESS) handles[dev] = nullptr;
-  return handles[dev];
-}
-
 }  // namespace
-
-size_t cross_workspace(int64_t n) {
-  (void)n;
-  return (size_t)64 << 20;
-}
-
-// C[i][j] += 2 sum_t X[t][i] Xq[t][j] for row-major X, Xq [tokens, ldx] and C [n, n].
-// Column-major view: C^T (n x n) += 2 Xq^T (n x tokens) (X^T)^T.
-int cross_launch(float* C, int64_t n, const void* X, const void* Xq, bool bf16, int64_t tokens, int64_t ldx,
-                 void* ws, size_t ws_bytes, hipStream_t stream) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return GPTQ_EHIP;
-  hipblasLtHandle_t h = lt_handle(dev);
-  if (!h) return GPTQ_EHIP;
-  const hipDataType in_t = bf16 ? HIP_R_16BF : HIP_R_32F;
-  hipblasLtMatmulDesc_t desc = nullptr;
-  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
-  hipblasLtMatmulPreference_t pref = nullptr;
-  int status = GPTQ_EHIP;
-  do {
-    if (hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS) break;
-    const hipblasOperation_t opa = HIPBLAS_OP_N, opb = HIPBLAS_OP_T;
-    if (hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opa, sizeof(opa)) != HIPBLAS_STATUS_SUCCESS)
-      break;
-    if (hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opb, sizeof(opb)) != HIPBLAS_STATUS_SUCCESS)
-      break;
-    if (hipblasLtMatrixLayoutCreate(&la, in_t, (uint64_t)n, (uint64_t)tokens, ldx) != HIPBLAS_STATUS_SUCCESS) break;
-    if (hipblasLtMatrixLayoutCreate(&lb, in_t, (uint64_t)n, (uint64_t)tokens, ldx) != HIPBLAS_STATUS_SUCCESS) break;
-    if (hipblasLtMatrixLayoutCreate(&lc, HIP_R_32F, (uint64_t)n, (uint64_t)n, n) != HIPBLAS_STATUS_SUCCESS) break;
-    if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) break;
-    const uint64_t wmax = ws_bytes;
-    if (hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wmax,
-                                              sizeof(wmax)) != HIPBLAS_STATUS_SUCCESS)
-      break;
-    hipblasLtMatmulHeuristicResult_t res[4];
-    int nres = 0;
-    if (hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, lc, lc, pref, 4, res, &nres) != HIPBLAS_STATUS_SUCCESS ||
-        nres == 0) {
-      status = GPTQ_EUNSUPPORTED;
-      break;
-    }
-    const float alpha = 2.0f, beta = 1.0f;
-    if (hipblasLtMatmul(h, desc, &alpha, Xq, la, X, lb, &beta, C, lc, C, lc, &res[0].algo, ws, ws_bytes, stream) !=
-        HIPBLAS_STATUS_SUCCESS)
-      break;
-    status = GPTQ_OK;
-  } while (false);
-  if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-  if (lc) hipblasLtMatrixLayoutDestroy(lc);
-  if (lb) hipblasLtMatrixLayoutDestroy(lb);
-  if (la) hipblasLtMatrixLayoutDestroy(la);
-  if (desc) hipblasLtMatmulDescDestroy(desc);
-  return status;
-}
 
 // W_out = W + alpha ((W G) U^T) U, G = C - H (C is overwritten by G), H factored
 // in place (U in the upper triangle, dead flags below) with the scratch in f.

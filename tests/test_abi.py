@@ -170,12 +170,17 @@ def test_hadamard_argument_errors():
 def test_qep_argument_errors():
     L = g.lib()
     F = g.GPTQ_F32
-    ws = L.gptq_cross_workspace_bytes(256)
+    T = 100000
+    ws = L.gptq_cross_workspace_bytes(256, T, F)
     assert ws > 0
-    assert L.gptq_accumulate_cross(FAKE, 256, FAKE, FAKE, 7, 10, 256, FAKE, ws, None) == g.GPTQ_EINVAL   # dtype
-    assert L.gptq_accumulate_cross(FAKE, 256, FAKE, FAKE, F, 10, 128, FAKE, ws, None) == g.GPTQ_EINVAL   # ldx < n
-    assert L.gptq_accumulate_cross(FAKE, 256, FAKE, None, F, 10, 256, FAKE, ws, None) == g.GPTQ_EINVAL
-    assert L.gptq_accumulate_cross(FAKE, 256, FAKE, FAKE, F, 10, 256, FAKE, 16, None) == g.GPTQ_EWORKSPACE
+    assert L.gptq_cross_workspace_bytes(256, 10, F) == 0                   # too few tokens to split
+    assert L.gptq_cross_workspace_bytes(256, T, 7) == 0                    # bad dtype
+    # split partials over the whole square grid: at least the Hessian's upper-tile count
+    assert ws >= g.gptq_hessian_workspace_bytes(256, T, F)
+    assert L.gptq_accumulate_cross(FAKE, 256, FAKE, FAKE, 7, T, 256, FAKE, ws, None) == g.GPTQ_EINVAL    # dtype
+    assert L.gptq_accumulate_cross(FAKE, 256, FAKE, FAKE, F, T, 128, FAKE, ws, None) == g.GPTQ_EINVAL    # ldx < n
+    assert L.gptq_accumulate_cross(FAKE, 256, FAKE, None, F, T, 256, FAKE, ws, None) == g.GPTQ_EINVAL
+    assert L.gptq_accumulate_cross(FAKE, 256, FAKE, FAKE, F, T, 256, FAKE, ws - 1, None) == g.GPTQ_EWORKSPACE
     assert L.gptq_accumulate_cross(FAKE, 256, FAKE, FAKE, F, 0, 256, None, 0, None) == g.GPTQ_OK         # no tokens
     need = L.gptq_qep_workspace_bytes(64, 256)
     assert need >= 2 * 64 * 256 * 4 + 256 * 256 * 4

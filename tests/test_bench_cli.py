@@ -48,3 +48,21 @@ def test_traffic_figure_only_for_the_measured_workload():
     t = bench.SYRK_TRAFFIC
     assert bench.syrk_traffic("mlp_7b", t["tokens"]) is None
     assert bench.syrk_traffic(t["workload"], t["tokens"] // 2) is None
+
+
+def test_cpu_baseline_reports_host_and_stages():
+    """The oracle leg on the small 256x256 workload, in full: every stage timed on its own, the host's
+    cores, CPU model and BLAS recorded."""
+    import argparse
+
+    from post_weight_quantization_03_amd import synth
+    wl = synth.workload("linear256")
+    lin, acts = wl.linears[0], wl.hessians["x"]
+    args = argparse.Namespace(cpu_full=True, cpu_tokens=16384, cpu_rows=512)
+    r = bench.cpu_baseline(lin.weight(), acts, 256, 256, acts.tokens, 4, args, x_bf16=False, w_bf16=False)
+    assert r["kind"] == "oracle" and r["measured_in_full"] and r["value"] > 0
+    assert set(r["stage_seconds"]) == {"hessian", "factor", "quantize_loop"}
+    assert all(v > 0 for v in r["stage_seconds"].values())
+    assert r["seconds_full_layer"] == pytest.approx(sum(r["stage_seconds"].values()))
+    h = r["host"]
+    assert h["cpu_count"] == os.cpu_count() and h["cpu_model"] and r["cores"] >= 1

@@ -66,15 +66,34 @@ def _rel(a, b):
     return np.linalg.norm(a - b) / np.linalg.norm(b)
 
 
-@pytest.mark.parametrize("n,tokens,bf16,chunks", [(256, 1000, True, 1), (300, 777, False, 2), (1024, 4096, True, 3)])
+@pytest.mark.parametrize("n,tokens,bf16,chunks", [
+    (256, 1000, True, 1), (300, 777, False, 2), (1024, 4096, True, 3),
+    (300, 1000, True, 1),      # ragged width and tokens: guarded loads
+    (512, 16384, True, 1),     # token split with every tile cut into pieces
+    (2048, 8192, True, 1),     # token split, whole tiles
+    (2300, 5000, False, 1),    # fp32, ragged, several splits
+    (7168, 2048, True, 1),     # one token split, square supertile order with a partial edge
+    (7000, 1500, True, 1),     # the same, ragged width and tokens
+])
 def test_cross_parity(n, tokens, bf16, chunks):
-    say(f"cross term n={n} tokens={tokens} bf16={bf16} chunks={chunks}")
+    """C = 2 X^T Xq against the fp64 product, every entry; a second run is bit-identical."""
+    g = _lib()
+    say(f"cross term n={n} tokens={tokens} bf16={bf16} chunks={chunks} "
+        f"(workspace {g.gptq_cross_workspace_bytes(n, tokens, g.GPTQ_BF16 if bf16 else g.GPTQ_F32) >> 20} MiB)")
     X, Xq, X64, Xq64 = _inputs(n, tokens, bf16)
     _, C = _gpu_hc(X, Xq, n, bf16, chunks)
+    Cg = C.cpu().numpy()
+    del C
     ref = cross_ref([(X64, Xq64)], n)
-    rel = _rel(C.cpu().numpy().astype(np.float64), ref)
-    say(f"   rel Frobenius {rel:.3e}")
+    rel = _rel(Cg.astype(np.float64), ref)
+    # entry-wise against the Cauchy-Schwarz scale of each entry
+    scale = 2.0 * np.sqrt(np.outer(np.einsum("ti,ti->i", X64, X64), np.einsum("ti,ti->i", Xq64, Xq64)))
+    ent = np.max(np.abs(Cg - ref) / scale)
+    say(f"   rel Frobenius {rel:.3e}, max |dC| / scale {ent:.3e}")
     assert rel <= 1e-4
+    assert ent <= 1e-4
+    _, C2 = _gpu_hc(X, Xq, n, bf16, chunks)
+    assert np.array_equal(C2.cpu().numpy(), Cg)
 
 
 def test_cross_q_proj_full_width_sampled():
