@@ -215,7 +215,29 @@ def gemv_measure(g, torch, packed, scales, zeros, rows, cols, bits, groupsize, d
             "us_per_launch": us, "algorithmic_bytes": alg_bytes, "achieved_GBs": gbs, "peak_GBs": PEAK_HBM_GBS,
             "frac": gbs / PEAK_HBM_GBS, "weight_copies": copies,
             "batch8": {"kernel": "k_dequant_gemm", "us_per_launch": us_b, "algorithmic_bytes": bytes_b,
-                       "achieved_GBs": bytes_b / (us_b * 1e-6) / 1e9, "us_per_vector": us_b / B}}
+                       "achieved_GBs": bytes_b / (us_b * 1e-6) / 1e9,
+                       "frac": bytes_b / (us_b * 1e-6) / 1e9 / PEAK_HBM_GBS, "us_per_vector": us_b / B}}
+
+
+def gemv_shapes_measure(g, torch, dev, bits=4, groupsize=128):
+    """The dequantizing GEMV and the batch-8 GEMM on the other layer shapes of the workloads
+    (Llama-2-7B gate/up 11008x4096 and down 4096x11008, Qwen3-32B down 5120x25600), 4-bit g128,
+    over seeded random packed codes, scales in [0.005, 0.02] and zero points (the kernels' work
+    does not depend on the values), timed as gemv_measure times the step's own layer."""
+    out = {}
+    gen = torch.Generator(dev).manual_seed(5)
+    for rows, cols in ((11008, 4096), (4096, 11008), (5120, 25600)):
+        G = -(-cols // groupsize)
+        packed = torch.randint(-2 ** 31, 2 ** 31 - 1, (rows, cols * bits // 32), dtype=torch.int32, device=dev,
+                               generator=gen)
+        scales = 0.005 + 0.015 * torch.rand((rows, G), device=dev, generator=gen)
+        zeros = torch.randint(0, 2 ** bits, (rows, G), dtype=torch.uint8, device=dev, generator=gen)
+        r = gemv_measure(g, torch, packed, scales, zeros, rows, cols, bits, groupsize, dev)
+        out[f"{rows}x{cols}"] = {k: r[k] for k in ("us_per_launch", "algorithmic_bytes", "achieved_GBs", "frac",
+                                                   "weight_copies", "batch8")}
+        del packed, scales, zeros, r
+        torch.cuda.empty_cache()
+    return out
 
 
 def hadamard_measure(g, torch, Wd, n, dev, copies=6, rounds=3):
@@ -609,6 +631,7 @@ def main():
             "qep_correction": lambda: qep_measure(g, torch, st["Xd"], st["Wd"], cols, dev),
             "dequant_gemv": lambda: gemv_measure(g, torch, st["packed"], st["scales"], st["zeros"], rows, cols,
                                                  bits, wl.groupsize, dev),
+            "dequant_gemv_shapes": lambda: gemv_shapes_measure(g, torch, dev),
         }
         for name, fn in extras.items():
             try:

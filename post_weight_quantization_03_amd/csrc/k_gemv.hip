@@ -15,6 +15,8 @@
 // fp32 in a fixed order, so results are reproducible.  A small-batch variant
 // (k_dequant_gemm, below) converts each run's codes to floats once and applies
 // them to up to 8 vectors staged together.
+#include <type_traits>
+
 #include "common.h"
 
 namespace gptq {
@@ -154,14 +156,25 @@ __device__ __forceinline__ void run_codes(const uint32_t (&w)[BITS], float (&q)[
 
 // x goes through LDS in chunks of XCH runs, each run's 32 values in a row of XP
 // floats: the padding puts the rows of eight consecutive runs on different
-// banks, so the lanes' 16-byte reads of their runs do not collide.
+// banks, so the lanes' 16-byte reads of their runs do not collide.  Two chunk
+// buffers alternate: the next chunk's x is loaded into registers before the
+// lane's weight prefetches are issued and written to the other buffer after
+// the current chunk is applied.  Loads retire in issue order, so waiting for x
+// never waits for the weights queued after it, and the barrier between chunks
+// waits only for LDS: the weight loads of the next two runs stay in flight
+// across it.
 constexpr int XCH = 128;
 constexpr int XP = 36;
+
+// Barrier for LDS traffic only: this wave's LDS operations are done, then every
+// wave of the workgroup meets.  (__syncthreads also waits for every outstanding
+// global load, which would drain the weight prefetches at each chunk.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Template: NW waves per workgroup, R rows per wave, S waves share a row group
 // (column slices).  gr = runs per group (any value above the last run when the
 // row is one group).
-template <int BITS, int R, int S, int NW, typename XT>
+template <int BITS, int R, int S, int NW, bool WHOLE, typename XT>
 __global__ __launch_bounds__(64 * NW) void k_dequant_gemv(const uint32_t* __restrict__ packed,
                                                       const float* __restrict__ scales,
                                                       const uint8_t* __restrict__ zeros, int64_t rows, int64_t cols,
@@ -169,8 +182,10 @@ __global__ __launch_bounds__(64 * NW) void k_dequant_gemv(const uint32_t* __rest
                                                       float* __restrict__ y) {
   constexpr int RG = NW / S;             // row groups per workgroup
   constexpr int IT = XCH / (64 * S);     // runs per lane per chunk
+  constexpr int XV = XCH * 32 / (256 * NW);  // 4-float x vectors per thread and chunk
   static_assert(IT >= 1 && IT * 64 * S == XCH, "chunk must be whole lane sweeps");
-  __shared__ __align__(16) float xs[XCH * XP];
+  __shared__ __align__(16) float xs[2][XCH * XP];
+  __shared__ float sxs[2][XCH];  // sum of each run's 32 x values
   __shared__ float part[RG][R][S];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rg = wave / S, cs = wave % S;
@@ -193,7 +208,23 @@ __global__ __launch_bounds__(64 * NW) void k_dequant_gemv(const uint32_t* __rest
     uint32_t w[R][BITS];
     float s[R], z[R];
   };
+  // WHOLE (cols % 32 == 0): every run is whole, and a lane past the last run
+  // reloads the last one (ignored), so the loads carry no branch and the
+  // compiler's waits count them exactly.
   auto fetch = [&](int64_t k, Ops& o) {
+    if constexpr (WHOLE) {
+      const int64_t kc = k < nrun ? k : nrun - 1;
+#pragma unroll
+      for (int q = 0; q < R; ++q) load_run<BITS>(prow[q] + BITS * kc, o.w[q]);
+      const uint32_t gk = (uint32_t)kc / gr;
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        o.s[q] = srow[q][gk];
+        o.z[q] = (float)zrow[q][gk];
+      }
+      return;
+    }
+    if (k >= nrun) return;
     if (k < nfull) {
 #pragma unroll
       for (int q = 0; q < R; ++q) load_run<BITS>(prow[q] + BITS * k, o.w[q]);
@@ -212,47 +243,81 @@ __global__ __launch_bounds__(64 * NW) void k_dequant_gemv(const uint32_t* __rest
       o.z[q] = (float)zrow[q][gk];
     }
   };
-  float yacc[R] = {};
-  Ops cur;
-  {
-    const int64_t k = (int64_t)cs * 64 + lane;
-    if (k < nrun) fetch(k, cur);
-  }
-  for (int64_t c0 = 0; c0 < nrun; c0 += XCH) {
-    __syncthreads();  // the previous chunk's reads of xs are done
+  // raw x vectors (bf16 stays packed until stored, so nothing waits for its load before then)
+  using XR = typename std::conditional<std::is_same<XT, float>::value, f32x4, u16x4>::type;
+  XR xr[XV];
+  auto load_x = [&](int64_t c0) {
 #pragma unroll
-    for (int j = 0; j < XCH * 32 / (256 * NW); ++j) {
+    for (int j = 0; j < XV; ++j) {
       const int e = 4 * (threadIdx.x + 64 * NW * j);  // float index within the chunk
       const int64_t col = 32 * c0 + e;
-      // cols is a multiple of 4 (cols b is whole words), so a vector is all in or all out
-      const f32x4 v = col < cols ? load_x4(x + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      *reinterpret_cast<float4*>(xs + (e >> 5) * XP + (e & 31)) = make_float4(v.x, v.y, v.z, v.w);
+      // cols is a multiple of 4 (cols b is whole words), so a vector is all in or all
+      // out; one past the end reloads the last vector (no branch) and is zeroed when
+      // stored, not here, so that nothing waits for the load before then
+      xr[j] = *reinterpret_cast<const XR*>(x + (col < cols ? col : cols - 4));
     }
-    __syncthreads();
+  };
+  // a run's 8 vectors lie in 8 consecutive threads of one wave, whose butterfly gives
+  // every one of them the same sum
+  auto store_x = [&](float* buf, float* sbuf, int64_t c0) {
+#pragma unroll
+    for (int j = 0; j < XV; ++j) {
+      const int e = 4 * (threadIdx.x + 64 * NW * j);
+      const bool in = 32 * c0 + e < cols;
+      f32x4 v;
+      if constexpr (std::is_same<XT, float>::value)
+        v = xr[j];
+      else
+        v = f32x4{__uint_as_float((uint32_t)xr[j].x << 16), __uint_as_float((uint32_t)xr[j].y << 16),
+                  __uint_as_float((uint32_t)xr[j].z << 16), __uint_as_float((uint32_t)xr[j].w << 16)};
+      if (!in) v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      *reinterpret_cast<float4*>(buf + (e >> 5) * XP + (e & 31)) = make_float4(v.x, v.y, v.z, v.w);
+      float t = (v.x + v.y) + (v.z + v.w);
+      t += __shfl_xor(t, 1, 64);
+      t += __shfl_xor(t, 2, 64);
+      t += __shfl_xor(t, 4, 64);
+      if ((threadIdx.x & 7) == 0) sbuf[e >> 5] = t;
+    }
+  };
+  float yacc[R] = {};
+  const int64_t step = 64 * S;  // the lane's next run
+  const int64_t k0 = (int64_t)cs * 64 + lane;
+  load_x(0);
+  Ops cur, nx1;
+  fetch(k0, cur);
+  fetch(k0 + step, nx1);
+  store_x(xs[0], sxs[0], 0);
+  lds_barrier();
+  int buf = 0;
+  for (int64_t c0 = 0; c0 < nrun; c0 += XCH) {
+    const bool more = c0 + XCH < nrun;
+    if (more) load_x(c0 + XCH);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int kk = cs * 64 + lane + it * 64 * S;
       const int64_t k = c0 + kk;
-      // the lane's next run (in this chunk or the first of the next) is in flight
-      // while this one is applied
-      Ops nxt;
-      if (k + 64 * S < nrun) fetch(k + 64 * S, nxt);
+      // two runs of the lane ahead are in flight while this one is applied
+      Ops nx2;
+      fetch(k + 2 * step, nx2);
       if (k < nrun) {
         float xv[32];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float4 v = *reinterpret_cast<const float4*>(xs + kk * XP + 4 * i);
+          const float4 v = *reinterpret_cast<const float4*>(xs[buf] + kk * XP + 4 * i);
           xv[4 * i] = v.x; xv[4 * i + 1] = v.y; xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
         }
-        float sx = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) sx += xv[i];
+        const float sx = sxs[buf][kk];
 #pragma unroll
         for (int q = 0; q < R; ++q)
           yacc[q] = fmaf(cur.s[q], fmaf(run_dot<BITS>(cur.w[q], xv), unit, -cur.z[q] * sx), yacc[q]);
       }
-      cur = nxt;
+      cur = nx1;
+      nx1 = nx2;
     }
+    // the other buffer was last read in the previous chunk, before the last barrier
+    if (more) store_x(xs[buf ^ 1], sxs[buf ^ 1], c0 + XCH);
+    lds_barrier();
+    buf ^= 1;
   }
 #pragma unroll
   for (int q = 0; q < R; ++q) {
@@ -290,8 +355,12 @@ hipError_t launch(const uint32_t* packed, const float* scales, const uint8_t* ze
                   int64_t G, uint32_t gr, const XT* x, float* y, hipStream_t stream) {
   constexpr int64_t rows_per_wg = (NW / S) * R;
   const unsigned grid = (unsigned)((rows + rows_per_wg - 1) / rows_per_wg);
-  hipLaunchKernelGGL((k_dequant_gemv<BITS, R, S, NW, XT>), dim3(grid), dim3(64 * NW), 0, stream, packed, scales,
-                     zeros, rows, cols, G, gr, x, y);
+  if (cols % 32 == 0 && cols >= 32)
+    hipLaunchKernelGGL((k_dequant_gemv<BITS, R, S, NW, true, XT>), dim3(grid), dim3(64 * NW), 0, stream, packed,
+                       scales, zeros, rows, cols, G, gr, x, y);
+  else
+    hipLaunchKernelGGL((k_dequant_gemv<BITS, R, S, NW, false, XT>), dim3(grid), dim3(64 * NW), 0, stream, packed,
+                       scales, zeros, rows, cols, G, gr, x, y);
   return hipGetLastError();
 }
 
@@ -312,14 +381,16 @@ hipError_t launch_bits(const uint32_t* packed, const float* scales, const uint8_
 constexpr int BCH = 64;
 constexpr int GEMM_NW = 8;  // waves per workgroup (one staging of x serves 16 rows)
 
-template <int BITS, int T, int NW, typename XT>
+template <int BITS, int T, int NW, bool WHOLE, typename XT>
 __global__ __launch_bounds__(64 * NW) void k_dequant_gemm(const uint32_t* __restrict__ packed,
                                                       const float* __restrict__ scales,
                                                       const uint8_t* __restrict__ zeros, int64_t rows, int64_t cols,
                                                       int64_t G, uint32_t gr, const XT* __restrict__ X, int64_t ldx,
                                                       float* __restrict__ Y, int64_t ldy) {
   constexpr int R = 2;
+  static_assert(BCH * 32 == 256 * NW, "one 4-float x vector per thread and activation vector");
   __shared__ __align__(16) float xs[T][BCH * XP];
+  __shared__ float sxs[T][BCH];  // sum of each run's 32 x values
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t r0 = ((int64_t)blockIdx.x * NW + wave) * R;
   const int64_t wpr = cols * BITS / 32;
@@ -335,42 +406,90 @@ __global__ __launch_bounds__(64 * NW) void k_dequant_gemm(const uint32_t* __rest
     srow[q] = scales + r * G;
     zrow[q] = zeros + r * G;
   }
-  float yacc[T][R] = {};
-  for (int64_t c0 = 0; c0 < nrun; c0 += BCH) {
-    __syncthreads();  // the previous chunk's reads of xs are done
+  struct Ops {
+    uint32_t w[R][BITS];
+    float s[R], z[R];
+  };
+  // as in k_dequant_gemv: WHOLE runs load without a branch (a lane past the last
+  // run reloads it, ignored)
+  auto fetch = [&](int64_t k, Ops& o) {
+    if constexpr (WHOLE) {
+      const int64_t kc = k < nrun ? k : nrun - 1;
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-      for (int j = 0; j < (BCH * 32 + 256 * NW - 1) / (256 * NW); ++j) {
-        const int e = 4 * (threadIdx.x + 64 * NW * j);
-        if (e >= BCH * 32) break;
-        const int64_t col = 32 * c0 + e;
-        // cols is a multiple of 4 (cols b is whole words), so a vector is all in or all out
-        const f32x4 v = col < cols ? load_x4(X + t * ldx + col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        *reinterpret_cast<float4*>(&xs[t][(e >> 5) * XP + (e & 31)]) = make_float4(v.x, v.y, v.z, v.w);
-      }
-    __syncthreads();
-    const int64_t k = c0 + lane;
-    if (k < nrun) {
-      uint32_t w[R][BITS];
-      if (k < nfull) {
-#pragma unroll
-        for (int q = 0; q < R; ++q) load_run<BITS>(prow[q] + BITS * k, w[q]);
-      } else {
-        const int nw = (int)(cols - 32 * k) * BITS / 32;  // the partial last run's whole words
-#pragma unroll
-        for (int q = 0; q < R; ++q)
-#pragma unroll
-          for (int j = 0; j < BITS; ++j) w[q][j] = j < nw ? prow[q][BITS * k + j] : 0u;
-      }
-      const uint32_t gk = (uint32_t)k / gr;
-      float sv[R], zv[R], qv[R][32];
+      for (int q = 0; q < R; ++q) load_run<BITS>(prow[q] + BITS * kc, o.w[q]);
+      const uint32_t gk = (uint32_t)kc / gr;
 #pragma unroll
       for (int q = 0; q < R; ++q) {
-        sv[q] = srow[q][gk];
-        zv[q] = (float)zrow[q][gk];
-        run_codes<BITS>(w[q], qv[q]);
+        o.s[q] = srow[q][gk];
+        o.z[q] = (float)zrow[q][gk];
       }
+      return;
+    }
+    if (k >= nrun) return;
+    if (k < nfull) {
+#pragma unroll
+      for (int q = 0; q < R; ++q) load_run<BITS>(prow[q] + BITS * k, o.w[q]);
+    } else {
+      const int nw = (int)(cols - 32 * k) * BITS / 32;  // the partial last run's whole words
+#pragma unroll
+      for (int q = 0; q < R; ++q)
+#pragma unroll
+        for (int j = 0; j < BITS; ++j) o.w[q][j] = j < nw ? prow[q][BITS * k + j] : 0u;
+    }
+    const uint32_t gk = (uint32_t)k / gr;
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      o.s[q] = srow[q][gk];
+      o.z[q] = (float)zrow[q][gk];
+    }
+  };
+  // The next chunk's x is loaded into registers before the next run's weights
+  // are queued, and written to LDS after this chunk is applied, between two
+  // LDS-only barriers, so the weight loads stay in flight across them.
+  using XR = typename std::conditional<std::is_same<XT, float>::value, f32x4, u16x4>::type;
+  XR xr[T];
+  const int e = 4 * threadIdx.x;  // this thread's float index within a chunk
+  auto load_x = [&](int64_t c0) {
+    const int64_t col = 32 * c0 + e;
+    const int64_t cc = col < cols ? col : cols - 4;  // cols >= 4 (a multiple of 4)
+#pragma unroll
+    for (int t = 0; t < T; ++t) xr[t] = *reinterpret_cast<const XR*>(X + t * ldx + cc);
+  };
+  auto store_x = [&](int64_t c0) {
+    const bool in = 32 * c0 + e < cols;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      f32x4 v;
+      if constexpr (std::is_same<XT, float>::value)
+        v = xr[t];
+      else
+        v = f32x4{__uint_as_float((uint32_t)xr[t].x << 16), __uint_as_float((uint32_t)xr[t].y << 16),
+                  __uint_as_float((uint32_t)xr[t].z << 16), __uint_as_float((uint32_t)xr[t].w << 16)};
+      if (!in) v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      *reinterpret_cast<float4*>(&xs[t][(e >> 5) * XP + (e & 31)]) = make_float4(v.x, v.y, v.z, v.w);
+      float sm = (v.x + v.y) + (v.z + v.w);
+      sm += __shfl_xor(sm, 1, 64);
+      sm += __shfl_xor(sm, 2, 64);
+      sm += __shfl_xor(sm, 4, 64);
+      if ((threadIdx.x & 7) == 0) sxs[t][e >> 5] = sm;
+    }
+  };
+  float yacc[T][R] = {};
+  Ops cur;
+  load_x(0);
+  fetch(lane, cur);
+  store_x(0);
+  lds_barrier();
+  for (int64_t c0 = 0; c0 < nrun; c0 += BCH) {
+    const bool more = c0 + BCH < nrun;
+    if (more) load_x(c0 + BCH);
+    Ops nxt;
+    fetch(c0 + BCH + lane, nxt);
+    const int64_t k = c0 + lane;
+    if (k < nrun) {
+      float qv[R][32];
+#pragma unroll
+      for (int q = 0; q < R; ++q) run_codes<BITS>(cur.w[q], qv[q]);
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         float xv[32];
@@ -379,18 +498,22 @@ __global__ __launch_bounds__(64 * NW) void k_dequant_gemm(const uint32_t* __rest
           const float4 v = *reinterpret_cast<const float4*>(&xs[t][lane * XP + 4 * i]);
           xv[4 * i] = v.x; xv[4 * i + 1] = v.y; xv[4 * i + 2] = v.z; xv[4 * i + 3] = v.w;
         }
-        float sx = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) sx += xv[i];
+        const float sx = sxs[t][lane];
 #pragma unroll
         for (int q = 0; q < R; ++q) {
           float dot = 0.0f;
 #pragma unroll
           for (int i = 0; i < 32; ++i) dot = fmaf(qv[q][i], xv[i], dot);
-          yacc[t][q] = fmaf(sv[q], fmaf(dot, unit, -zv[q] * sx), yacc[t][q]);
+          yacc[t][q] = fmaf(cur.s[q], fmaf(dot, unit, -cur.z[q] * sx), yacc[t][q]);
         }
       }
     }
+    if (more) {
+      lds_barrier();  // every wave is done with this chunk's x
+      store_x(c0 + BCH);
+      lds_barrier();
+    }
+    cur = nxt;
   }
 #pragma unroll
   for (int t = 0; t < T; ++t)
@@ -408,8 +531,12 @@ hipError_t launch_gemm(const uint32_t* packed, const float* scales, const uint8_
                        int64_t G, uint32_t gr, const XT* X, int64_t ldx, float* Y, int64_t ldy, hipStream_t stream) {
   constexpr int NW = GEMM_NW;
   const unsigned grid = (unsigned)((rows + 2 * NW - 1) / (2 * NW));
-  hipLaunchKernelGGL((k_dequant_gemm<BITS, T, NW, XT>), dim3(grid), dim3(64 * NW), 0, stream, packed, scales, zeros,
-                     rows, cols, G, gr, X, ldx, Y, ldy);
+  if (cols % 32 == 0 && cols >= 32)
+    hipLaunchKernelGGL((k_dequant_gemm<BITS, T, NW, true, XT>), dim3(grid), dim3(64 * NW), 0, stream, packed, scales,
+                       zeros, rows, cols, G, gr, X, ldx, Y, ldy);
+  else
+    hipLaunchKernelGGL((k_dequant_gemm<BITS, T, NW, false, XT>), dim3(grid), dim3(64 * NW), 0, stream, packed, scales,
+                       zeros, rows, cols, G, gr, X, ldx, Y, ldy);
   return hipGetLastError();
 }
 
@@ -434,7 +561,9 @@ template <typename XT>
 hipError_t dequant_gemv_x(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
                           int64_t cols, int32_t bits, int32_t groupsize, const XT* x, float* y, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  // cols == 0 still launches: no runs, every y is written as 0
+  // no columns: every y is 0, written by a fill kernel (the product kernel's
+  // branch-free loads assume at least one whole run)
+  if (cols <= 0) return fill_i32(reinterpret_cast<int*>(y), rows, 0, stream);
   const int64_t nrun = (cols + 31) / 32;
   const int64_t G = groupsize == -1 ? 1 : (cols + groupsize - 1) / groupsize;
   const uint32_t gr = groupsize == -1 ? (uint32_t)(nrun > 0 ? nrun : 1) : (uint32_t)(groupsize / 32);
@@ -459,6 +588,14 @@ template <typename XT>
 hipError_t dequant_gemm_x(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
                           int64_t cols, int32_t bits, int32_t groupsize, const XT* X, int64_t ldx, int64_t batch,
                           float* Y, int64_t ldy, hipStream_t stream) {
+  if (cols <= 0) {
+    // no columns: every output is 0 (the product kernels' loads assume a column)
+    for (int64_t t = 0; t < batch; ++t) {
+      const hipError_t e = fill_i32(reinterpret_cast<int*>(Y + t * ldy), rows, 0, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   const int64_t nrun = (cols + 31) / 32;
   const int64_t G = groupsize == -1 ? 1 : (cols + groupsize - 1) / groupsize;
   const uint32_t gr = groupsize == -1 ? (uint32_t)(nrun > 0 ? nrun : 1) : (uint32_t)(groupsize / 32);

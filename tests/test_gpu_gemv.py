@@ -235,3 +235,21 @@ def test_dequant_gemm_batch_of_one_is_the_gemv():
     y = _gpu(packed, scales, zeros, 4, 128, X[0], 64)
     assert np.array_equal(Yg[0], y)
 
+
+
+def test_dequant_gemm_empty_columns():
+    """A batch over a layer with no columns writes zeros into every output row (row stride 9 for 7
+    rows) and leaves the padding between output rows alone."""
+    import ctypes
+    say("dequant_gemm with no columns, batch 5")
+    g = _lib()
+    torch, dev = torch_dev()
+    Y = torch.full((5, 9), float("nan"), dtype=torch.float32, device=dev)
+    buf = torch.zeros(64, dtype=torch.int32, device=dev)  # stands for the empty inputs
+    p = ctypes.c_void_p(buf.data_ptr())
+    st = g.lib().gptq_dequant_gemm(p, p, p, 7, 0, 4, -1, p, g.GPTQ_F32, 0, 5, ctypes.c_void_p(Y.data_ptr()), 9,
+                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.all(Y[:, :7] == 0)
+    assert torch.all(torch.isnan(Y[:, 7:]))
