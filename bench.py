@@ -36,9 +36,9 @@ PEAK_HBM_GBS = 8000.0
 # rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by the reading of a plain 1 GiB copy;
 # the summary with the commands is profiles/hbm_counters_q_proj_4096x4096_262144tok.md.  Valid
 # only for the kernel source they were taken on: a different k_hessian.hip reports null.
-SYRK_TRAFFIC = {"k_hessian_sha256": "ad5690e19bdd38695b7538e2e12ec82c1fec6b918d275b72c06b7738a3ebed1c",
+SYRK_TRAFFIC = {"k_hessian_sha256": "7c4239606312840df1d660666ecd92f0a6e0c879e66322fd123812bcab15937b",
                 "workload": "q_proj_4096", "tokens": 262144,
-                "fetch_bytes": 9210818884.9, "write_bytes": 492769221.3}
+                "fetch_bytes": 9208407915.7, "write_bytes": 492683057.3}
 
 
 def syrk_traffic(workload, tokens):
@@ -591,7 +591,7 @@ def time_layer(args, g, torch, wl, lin, acts, bits, dev, workload_name, descript
                      "achieved": hess_tflops,
                      "peak": hess_peak, "unit": "TFLOP/s", "frac": hess_tflops / hess_peak,
                      "traffic": syrk_traffic(workload_name, tokens),
-                     "algorithmic_bytes": alg["x_bytes"] + 4.0 * cols * cols},
+                     "algorithmic_bytes": alg["x_bytes"] + 8.0 * cols * cols},  # X read, H read and written
         "input_generation_s": gen_s,
     }
     state = {"W_bits": W_bits, "Xd": Xd, "Wd": Wd, "packed": packed, "scales": scales, "zeros": zeros,
