@@ -47,6 +47,7 @@ struct GemmF32 {
   int tri;
   int klo_n;
   int khi_m;
+  int kfl_lo, kfl_hi;  // tile rows m0 in [kfl_lo, kfl_hi) start their K range at m0 - kfl_lo
   int batch;
   int order;  // set by gemm_f32: 1 = tiles by ascending column, 2 = by descending row (longest K first)
 };

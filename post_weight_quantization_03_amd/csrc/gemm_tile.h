@@ -341,6 +341,10 @@ __device__ __forceinline__ void gemm_tile(const GemmF32& g, int tm, int tn, int 
   int kbeg = 0, kend = g.K;
   if (g.klo_n) kbeg = n0 < g.K ? n0 : g.K;
   if (g.khi_m) kend = (m0 + TM) < g.K ? (m0 + TM) : g.K;
+  if (m0 >= g.kfl_lo && m0 < g.kfl_hi) {
+    const int f = m0 - g.kfl_lo;
+    kbeg = f > kbeg ? (f < kend ? f : kend) : kbeg;
+  }
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;

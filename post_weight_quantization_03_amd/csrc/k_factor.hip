@@ -23,6 +23,16 @@
 //     block and hands L^T to the solves in a buffer of its own).  The
 //     inverse's work thus fills the CUs that the Cholesky's late, narrow
 //     steps leave idle, and nothing of it is left after the loop.
+//     On large steps the GEMM is lazy in two levels: block column k+1 (the
+//     next to be solved) takes every panel at once, the columns past it only
+//     every FACTOR_LAZY panels, with K = 128 FACTOR_LAZY, so the trailing
+//     matrix is read and written once per FACTOR_LAZY panels instead of once
+//     per panel.
+//     A row of a pending panel's own block is an inverse row only for the
+//     panels from its own block on (before it, its entries right of the
+//     diagonal were above the trailing matrix's lower triangle, which the
+//     Cholesky update leaves alone), so such rows start their K range at
+//     their own block (GemmF32::kfl_lo / kfl_hi).
 //  4. k_write_factor   U[i][j] = Y[n-1-j][n-1-i] for i <= j into H (Y = L^-T,
 //     A's upper triangle), plus the dead flags in H's strictly lower triangle.
 #include <utility>
@@ -33,6 +43,12 @@ namespace gptq {
 namespace {
 
 constexpr int NB = 128;
+constexpr int64_t FACTOR_LAZY = 2;  // panels per update of the columns past the next block
+// Deferral pays only on steps whose GEMM is large: more tiles than four rounds
+// of the chip's 256 CUs.  On smaller steps the doubled K of the update that
+// follows costs more than the saved pass over the trailing matrix (measured at
+// n = 4096, where every step is below this).
+constexpr int64_t FACTOR_LAZY_TILES = 4 * 256;
 
 __global__ __launch_bounds__(1024) void k_damp_stats(const float* H, int64_t n, float damp, uint8_t* dead,
                                                      float* lam) {
@@ -308,14 +324,24 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 // More than half of the CU's LDS per workgroup: one workgroup per CU, so the
 // diagonal factor never shares its CU with a tile (sharing one made the factor
 // up to 1.9x slower; the tiles lose less than that gains).
-__global__ __launch_bounds__(256) void k_factor_step(GemmF32 g, int ntri, int rrows, int nt, const float* A,
-                                                     int64_t n, int64_t k0n, float* Lt, int* status) {
+__global__ __launch_bounds__(256) void k_factor_step(GemmF32 g, int ntri, int rrows, int nt, int near_only,
+                                                     const float* A, int64_t n, int64_t k0n, float* Lt,
+                                                     int* status) {
   __shared__ __attribute__((aligned(16))) char lds[cmax(96 * 1024, cmax(POTRF_LDS, gemm_tile_lds<128>()))];
   if (blockIdx.x == 0) {
     potrf_diag(A, n, k0n, Lt, status, lds);
     return;
   }
   const int u = (int)blockIdx.x - 1;
+  if (near_only) {
+    // tile column 0 only (block column k+1): the lower tiles below its
+    // diagonal block, then the rectangle above
+    if (u < nt - 1)
+      gemm_tile<128, false, true>(g, rrows + u + 1, 0, 0, lds);
+    else
+      gemm_tile<128, false, true>(g, u - (nt - 1), 0, 0, lds);
+    return;
+  }
   if (u < ntri - 1) {
     const int t = u + 1;
     int r = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
@@ -337,6 +363,7 @@ __global__ __launch_bounds__(256) void k_factor_step(GemmF32 g, int ntri, int rr
 // of each row, all in flight at once with the workgroup's elements of D.  The
 // quarters are summed through LDS in a fixed order.  On the factor's critical
 // path, so it is built for latency.
+template <int PASSES>
 __global__ __launch_bounds__(256) void k_diag_update(float* A, int64_t n, int64_t k0, int64_t c1, int kb1) {
   __shared__ float part[4][32 * 32];
   const int t = blockIdx.x;
@@ -347,22 +374,27 @@ __global__ __launch_bounds__(256) void k_diag_update(float* A, int64_t n, int64_
   const int ra = 32 * ti + j, rb = 32 * tj + j;
   const int kq = 32 * w + 16 * h;
   const bool vec = (n & 3) == 0 && (k0 & 3) == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
-  float a[16], b[16];
-  if (vec) {
+  // pass p covers k0 + 128 p .. k0 + 128 p + 127 (PASSES pending panels)
+  float a[PASSES][16], b[PASSES][16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 va = ra < kb1 ? *reinterpret_cast<const float4*>(A + (c1 + ra) * n + k0 + kq + 4 * q)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 vb = rb < kb1 ? *reinterpret_cast<const float4*>(A + (c1 + rb) * n + k0 + kq + 4 * q)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-      a[4 * q + 0] = va.x; a[4 * q + 1] = va.y; a[4 * q + 2] = va.z; a[4 * q + 3] = va.w;
-      b[4 * q + 0] = vb.x; b[4 * q + 1] = vb.y; b[4 * q + 2] = vb.z; b[4 * q + 3] = vb.w;
-    }
-  } else {
+  for (int p = 0; p < PASSES; ++p) {
+    const int64_t kp = k0 + 128 * p + kq;
+    if (vec) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      a[e] = ra < kb1 ? A[(c1 + ra) * n + k0 + kq + e] : 0.0f;
-      b[e] = rb < kb1 ? A[(c1 + rb) * n + k0 + kq + e] : 0.0f;
+      for (int q = 0; q < 4; ++q) {
+        const float4 va = ra < kb1 ? *reinterpret_cast<const float4*>(A + (c1 + ra) * n + kp + 4 * q)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 vb = rb < kb1 ? *reinterpret_cast<const float4*>(A + (c1 + rb) * n + kp + 4 * q)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        a[p][4 * q + 0] = va.x; a[p][4 * q + 1] = va.y; a[p][4 * q + 2] = va.z; a[p][4 * q + 3] = va.w;
+        b[p][4 * q + 0] = vb.x; b[p][4 * q + 1] = vb.y; b[p][4 * q + 2] = vb.z; b[p][4 * q + 3] = vb.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        a[p][e] = ra < kb1 ? A[(c1 + ra) * n + kp + e] : 0.0f;
+        b[p][e] = rb < kb1 ? A[(c1 + rb) * n + kp + e] : 0.0f;
+      }
     }
   }
   // this thread's four elements of D, read now so that their latency hides too
@@ -377,10 +409,12 @@ __global__ __launch_bounds__(256) void k_diag_update(float* A, int64_t n, int64_
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 16; e += 2) {
-    acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e + 1], b[e + 1], acc1, 0, 0, 0);
-  }
+  for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[p][e], b[p][e], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[p][e + 1], b[p][e + 1], acc1, 0, 0, 0);
+    }
 #pragma unroll
   for (int r = 0; r < 16; ++r) part[w][acc_row(r, lane) * 32 + j] = acc0[r] + acc1[r];
   __syncthreads();
@@ -444,6 +478,30 @@ __global__ __launch_bounds__(256) void k_trsm_block(float* A, const float* Ltk, 
   __shared__ __attribute__((aligned(16))) float Lt[NB][NB];
   __shared__ float rL[NB];
   const int tid = threadIdx.x;
+  TrsmLane L;
+  const int lane = tid & 63;
+  L.t = lane & 15;
+  const int64_t grow = (int64_t)blockIdx.x * 16 + (tid >> 6) * 4 + (lane >> 4);
+  const bool ok = grow < n;
+  const bool ident = grow >= k0 && grow < k0 + kb;
+  const int rr = (int)(grow - k0);
+  const bool vec = kb == NB && (n & 3) == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
+  // the row's right-hand side first, so that its load is in flight with L^T's
+  if (ok && !ident && vec) {
+    const float4 b0 = *reinterpret_cast<const float4*>(A + grow * n + k0 + 8 * L.t);
+    const float4 b1 = *reinterpret_cast<const float4*>(A + grow * n + k0 + 8 * L.t + 4);
+    L.b[0] = b0.x; L.b[1] = b0.y; L.b[2] = b0.z; L.b[3] = b0.w;
+    L.b[4] = b1.x; L.b[5] = b1.y; L.b[6] = b1.z; L.b[7] = b1.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = 8 * L.t + i;
+      if (ident)
+        L.b[i] = c == rr ? 1.0f : 0.0f;
+      else
+        L.b[i] = (ok && c < kb) ? A[grow * n + k0 + c] : 0.0f;
+    }
+  }
   // Lt[j][m] = L[m][j] for m > j, else 0 (the buffer holds zeros below its diagonal)
   {
     constexpr int PER = NB * NB / 4 / 256;
@@ -467,29 +525,6 @@ __global__ __launch_bounds__(256) void k_trsm_block(float* A, const float* Ltk, 
   if (tid < NB) rL[tid] = tid < kb ? 1.0f / Ltk[tid * (NB + 1)] : 0.0f;
   __syncthreads();
 
-  TrsmLane L;
-  const int lane = tid & 63;
-  L.t = lane & 15;
-  const int64_t grow = (int64_t)blockIdx.x * 16 + (tid >> 6) * 4 + (lane >> 4);
-  const bool ok = grow < n;
-  const bool ident = grow >= k0 && grow < k0 + kb;
-  const int rr = (int)(grow - k0);
-  const bool vec = kb == NB && (n & 3) == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
-  if (ok && !ident && vec) {
-    const float4 b0 = *reinterpret_cast<const float4*>(A + grow * n + k0 + 8 * L.t);
-    const float4 b1 = *reinterpret_cast<const float4*>(A + grow * n + k0 + 8 * L.t + 4);
-    L.b[0] = b0.x; L.b[1] = b0.y; L.b[2] = b0.z; L.b[3] = b0.w;
-    L.b[4] = b1.x; L.b[5] = b1.y; L.b[6] = b1.z; L.b[7] = b1.w;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = 8 * L.t + i;
-      if (ident)
-        L.b[i] = c == rr ? 1.0f : 0.0f;
-      else
-        L.b[i] = (ok && c < kb) ? A[grow * n + k0 + c] : 0.0f;
-    }
-  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) L.ru[i] = rL[8 * L.t + i];
   L.un[0] = *reinterpret_cast<const float4*>(&Lt[0][8 * L.t]);
@@ -599,6 +634,7 @@ hipError_t factor_run(float* H, int64_t n, float damp, const FactorWs& ws, hipSt
                      ws.status);
   FCHECK(hipGetLastError());
   const unsigned grows = (unsigned)((n + 15) / 16);
+  int64_t kp = 0;  // first column of the panels whose update of the columns past the next block is pending
   for (int64_t k = 0; k < nk; ++k) {
     const int64_t k0 = k * NB;
     const int64_t kb = (n - k0) < NB ? (n - k0) : NB;
@@ -608,34 +644,46 @@ hipError_t factor_run(float* H, int64_t n, float damp, const FactorWs& ws, hipSt
                        k0, (int)kb);
     FCHECK(hipGetLastError());
     if (rest <= 0) break;
-    // A[r][j] -= A[r][k0:c1] L[j][k0:c1]^T for every row r and the columns j >= c1
+    const int kb1 = (int)(rest < NB ? rest : NB);
+    // the pending panels kp .. c1 reach block column k+1 now, the columns past
+    // it once FACTOR_LAZY panels are pending (or none are past it)
+    const int64_t kn = c1 - kp;
+    const int64_t nt = (rest + 127) / 128, ntri = nt * (nt + 1) / 2, rrows = c1 / 128;
+    const bool flush = kn >= FACTOR_LAZY * NB || rest <= kb1 || rrows * nt + ntri - 1 <= FACTOR_LAZY_TILES;
+    // A[r][j] -= A[r][kp:c1] L[j][kp:c1]^T for every row r and the columns j >= c1
     GemmF32 t{};
-    t.A = ws.A + k0;
+    t.A = ws.A + kp;
     t.lda = n;
-    t.B = ws.A + c1 * n + k0;
+    t.B = ws.A + c1 * n + kp;
     t.ldb = n;
-    t.b_kmajor = 0;  // B(k, j) = L[c1 + j][k0 + k]
+    t.b_kmajor = 0;  // B(k, j) = L[c1 + j][kp + k]
     t.C = ws.A + c1;
     t.ldc = n;
     t.M = (int)n;
     t.N = (int)rest;
-    t.K = (int)kb;
+    t.K = (int)kn;
+    t.kfl_lo = (int)kp;  // rows of a pending panel's block: only the panels from their own block on
+    t.kfl_hi = (int)c1;
     t.alpha = -1.0f;
     t.beta = 1;
     t.batch = 1;
     {
-      // look-ahead: the diagonal block of block k+1 alone
-      const int kb1 = (int)(rest < NB ? rest : NB), t32 = (kb1 + 31) / 32;
-      hipLaunchKernelGGL(k_diag_update, dim3((unsigned)(t32 * (t32 + 1) / 2)), dim3(256), 0, stream, ws.A, n, k0, c1,
-                         kb1);
+      // look-ahead: the diagonal block of block k+1 alone, every pending panel
+      const int t32 = (kb1 + 31) / 32;
+      if (kn > NB)
+        hipLaunchKernelGGL(k_diag_update<2>, dim3((unsigned)(t32 * (t32 + 1) / 2)), dim3(256), 0, stream, ws.A, n, kp,
+                           c1, kb1);
+      else
+        hipLaunchKernelGGL(k_diag_update<1>, dim3((unsigned)(t32 * (t32 + 1) / 2)), dim3(256), 0, stream, ws.A, n, kp,
+                           c1, kb1);
       FCHECK(hipGetLastError());
     }
     // the rest beside block k+1's factor
-    const int64_t nt = (rest + 127) / 128, ntri = nt * (nt + 1) / 2, rrows = c1 / 128;
-    hipLaunchKernelGGL(k_factor_step, dim3((unsigned)(1 + rrows * nt + ntri - 1)), dim3(256), 0, stream, t,
-                       (int)ntri, (int)rrows, (int)nt, (const float*)ws.A, n, c1, ws.Lt + (k + 1) * NB * NB,
-                       ws.status);
+    const int64_t tiles = flush ? rrows * nt + ntri - 1 : rrows + nt - 1;
+    hipLaunchKernelGGL(k_factor_step, dim3((unsigned)(1 + tiles)), dim3(256), 0, stream, t, (int)ntri, (int)rrows,
+                       (int)nt, flush ? 0 : 1, (const float*)ws.A, n, c1, ws.Lt + (k + 1) * NB * NB, ws.status);
     FCHECK(hipGetLastError());
+    if (flush) kp = c1;
   }
   {
     const unsigned nt = (unsigned)((n + 63) / 64);

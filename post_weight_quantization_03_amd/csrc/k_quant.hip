@@ -148,12 +148,31 @@ __device__ __forceinline__ float row_bcast(float v) {
   return __builtin_amdgcn_update_dpp(0.0f, v, 0x150 + O, 0xf, 0xf, false);
 }
 
+// The value of lane i ^ m for m = 1, 2 (DPP quad permutations), and of a
+// lane in the other half of its group of 8 or 16 for m = 4, 8 (half-row and
+// row mirrors).  Used after the steps for the smaller m, when every lane of a
+// group of m lanes holds the same value, the mirror's partner holds what lane
+// i ^ m holds, so these reductions equal the xor butterfly bit for bit.
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  constexpr int CTRL = M == 1 ? 0xB1 : M == 2 ? 0x4E : M == 4 ? 0x141 : 0x140;
+  return __builtin_amdgcn_update_dpp(0.0f, v, CTRL, 0xf, 0xf, false);
+}
+
 template <int WIDTH>
 __device__ __forceinline__ void reduce_minmax(float& mn, float& mx) {
-#pragma unroll
-  for (int m = 1; m < WIDTH; m <<= 1) {
-    mn = fminf(mn, __shfl_xor(mn, m, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+  static_assert(WIDTH == 4 || WIDTH == 8 || WIDTH == 16, "lane groups of 4, 8 or 16");
+  mn = fminf(mn, lane_xor<1>(mn));
+  mx = fmaxf(mx, lane_xor<1>(mx));
+  mn = fminf(mn, lane_xor<2>(mn));
+  mx = fmaxf(mx, lane_xor<2>(mx));
+  if constexpr (WIDTH >= 8) {
+    mn = fminf(mn, lane_xor<4>(mn));
+    mx = fmaxf(mx, lane_xor<4>(mx));
+  }
+  if constexpr (WIDTH >= 16) {
+    mn = fminf(mn, lane_xor<8>(mn));
+    mx = fmaxf(mx, lane_xor<8>(mx));
   }
 }
 
@@ -335,6 +354,8 @@ __device__ __forceinline__ void quant_block_wg(const BlockArgs& a, int64_t wg, c
       uv[i] = *reinterpret_cast<const float4*>(a.U + (c0 + j) * cols + c0 + k);
     }
   }
+  // U_jj for 1/U_jj, with the other loads
+  const float udiag = tid < a.bw ? a.U[(c0 + tid) * cols + c0 + tid] : 1.0f;
   f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   if (a.Eprev) {
 #pragma unroll
@@ -361,7 +382,7 @@ __device__ __forceinline__ void quant_block_wg(const BlockArgs& a, int64_t wg, c
       Us[j][k] = v;
     }
   }
-  if (tid < B) rUd[tid] = tid < a.bw ? 1.0f / a.U[(c0 + tid) * cols + c0 + tid] : 0.0f;
+  if (tid < B) rUd[tid] = tid < a.bw ? 1.0f / udiag : 0.0f;
   if (a.Eprev) {
     // tile h holds D[4g + r][i16] for columns 32 wv + 16 h + i16
 #pragma unroll
@@ -441,8 +462,10 @@ __device__ __forceinline__ void quant_block_wg(const BlockArgs& a, int64_t wg, c
     ls += 0.5f * e[i] * e[i];
   }
   // loss over the row's 16 lanes
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) ls += __shfl_xor(ls, m, 64);
+  ls += lane_xor<1>(ls);
+  ls += lane_xor<2>(ls);
+  ls += lane_xor<4>(ls);
+  ls += lane_xor<8>(ls);
   if (!row_ok) return;
   if (L.t == 0) a.row_loss[row] = (c0 == 0 ? 0.0f : a.row_loss[row]) + ls;
   const bool full = (8 * L.t + 8 <= a.bw);

@@ -100,6 +100,14 @@ def _check(rows, cols, bits, groupsize, seed, x_bf16=False):
     (8193, 36, 8, -1),     # many rows, partial run
     (8192, 4128, 2, 64),   # many rows, 129 runs: a second x chunk
     (40, 4160, 4, 128),    # 130 runs: a second x chunk with few rows
+    (5, 2056, 4, -1),      # 65 runs, the last partial (64 runs + 8 codes)
+    (3, 2052, 8, -1),      # 8 bits, partial last run of 4 codes
+    (1, 2048, 2, -1),      # one row, exactly 64 runs
+    (4100, 2048, 3, 32),
+    (600, 25600, 4, 128),  # the 5120x25600 layer's width: 7 x chunks, the last partial
+    (300, 32768, 4, 128),  # 1024 runs: 8 whole x chunks
+    (2, 32800, 4, 128),    # 1025 runs: a chunk of one run at the end
+    (65600, 2048, 8, -1),  # many rows, 8 bits
 ])
 def test_dequant_gemv_parity(rows, cols, bits, groupsize):
     say(f"dequant_gemv rows={rows} cols={cols} bits={bits} groupsize={groupsize}")
@@ -108,6 +116,7 @@ def test_dequant_gemv_parity(rows, cols, bits, groupsize):
 
 @pytest.mark.parametrize("rows,cols,bits,groupsize", [
     (37, 4096, 4, 128), (8200, 512, 4, 128), (5, 1000, 4, -1), (9, 2080, 3, 32), (11, 1024, 2, 64), (6, 36, 8, -1),
+    (37, 25600, 4, 128), (5, 2056, 4, -1), (3, 2052, 8, -1),
 ])
 def test_dequant_gemv_bf16_activations(rows, cols, bits, groupsize):
     say(f"dequant_gemv bf16 x rows={rows} cols={cols} bits={bits} groupsize={groupsize}")

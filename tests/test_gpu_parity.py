@@ -186,7 +186,10 @@ def test_quantize_linear256():
     (33, 256, 8, -1), (48, 320, 3, 64), (40, 256, 4, 32), (5, 130, 4, 128),
     # several 128-blocks past a group of 8 (the trailing update's second level and
     # the factor's folded inverse over many steps), ragged tails
-    (8, 1040, 2, 128), (24, 1300, 4, 128), (16, 2176, 4, 128)])
+    (8, 1040, 2, 128), (24, 1300, 4, 128), (16, 2176, 4, 128),
+    # more loop workgroups (16 rows each) than the chip holds at once (512), the
+    # last ragged, in every group mode
+    (8200, 384, 4, 128), (8200, 300, 3, 32), (8195, 272, 2, 64), (8210, 260, 4, -1)])
 def test_quantize_ragged_and_groups(rows, cols, bits, g):
     _lib_loaded()
     say(f"quantize rows={rows} cols={cols} bits={bits} g={g}")
@@ -274,6 +277,31 @@ def test_factor_matches_oracle():
     rel = np.linalg.norm(out["U"] - U) / np.linalg.norm(U)
     say(f"   U rel Frobenius {rel:.3e}")
     assert rel <= 1e-4
+
+
+@pytest.mark.parametrize("n", [6144, 6000])
+def test_factor_matches_oracle_deferred_steps(n):
+    """Widths whose first factor steps are large enough for the deferred
+    (two-level) update of the columns past the next block, and whose later
+    steps are not: U against the fp64 factor of the same damped H."""
+    _lib_loaded()
+    import torch
+    from oracle import damp_ref, factor_ref_large
+    say(f"factor U vs oracle, n={n} (deferred trailing updates on the early steps)")
+    a = synth.Activations(seed=n, tensor=synth.T_X, n=n, tokens=8192, dist=synth.STUDENT_T4,
+                          outliers=max(1, n // 100), outlier_factor=20.0, bf16=True)
+    X = torch.from_numpy(synth.bf16_to_f32(a.full())).double()
+    H32 = (2.0 * (X.T @ X)).float().numpy()
+    del X
+    W = synth.rows(n, synth.T_W, synth.NORMAL, 0.02, n, 0, 8, bf16=True)
+    out = gpu_quantize(W, H32, 4, 128, w_bf16=True)
+    Hd, _, _, _ = damp_ref(H32.astype(np.float64), synth.bf16_to_f32(W).astype(np.float64), 0.01)
+    U = factor_ref_large(Hd)
+    rel = np.linalg.norm(out["U"] - U) / np.linalg.norm(U)
+    rows = np.linalg.norm(out["U"] - U, axis=1) / np.linalg.norm(U, axis=1)
+    say(f"   U rel Frobenius {rel:.3e}, worst row {rows.max():.3e}")
+    assert rel <= 1e-4
+    assert rows.max() <= 1e-3
 
 
 # --------------------------------------------------------------------------- pack
