@@ -72,6 +72,9 @@ def parse():
                     help="time the oracle over the whole layer (every token, every row) instead of a sample")
     ap.add_argument("--no-second", action="store_true",
                     help="skip the metric's second shape (11008x4096, 4-bit g128) on the default workload")
+    ap.add_argument("--trace", action="store_true",
+                    help="instead of the bench line: one pass of the layer on libgptq_trace.so, printing the "
+                         "phase timestamps of the column loop and the factor's chain (medians, us)")
     return ap.parse_args()
 
 
@@ -599,6 +602,88 @@ def time_layer(args, g, torch, wl, lin, acts, bits, dev, workload_name, descript
     return rec, state
 
 
+TRACE_REC = 32  # words per trace record (gptq_trace_set in include/gptq.h)
+TRACE_LOOP, TRACE_POTRF, TRACE_TRSM, TRACE_DIAG, TRACE_TILE = 1, 2, 3, 4, 5
+
+
+def trace_summary(words, count):
+    """Decodes the trace buffer (uint64 words as gptq_trace_set lays them out) into phase medians
+    in microseconds (the stamps are a 100 MHz clock).  Host logic only."""
+    words = np.asarray(words, dtype=np.int64)
+    n = min(int(count), int(words[0]))
+    rec = words[TRACE_REC:TRACE_REC * (n + 1)].reshape(n, TRACE_REC)
+    kind, tag, cnt, st = rec[:, 0], rec[:, 2], rec[:, 3], rec[:, 4:].astype(np.float64) / 100.0
+    med = lambda v: float(np.median(v)) if len(v) else None  # noqa: E731
+    out = {"records": int(count), "kept": n}
+    lp = st[(kind == TRACE_LOOP) & (cnt >= 7) & (tag >= 1)]
+    names = ("operands_and_near_update", "stores_to_lds", "barrier", "update_applied_and_group_range",
+             "steps_128", "outputs")
+    out["loop_workgroup_us"] = {nm: med(lp[:, i + 1] - lp[:, i]) for i, nm in enumerate(names)}
+    out["loop_workgroup_us"]["total"] = med(lp[:, 6] - lp[:, 0])
+    po = st[(kind == TRACE_POTRF) & (cnt >= 18)]
+    ptag = tag[(kind == TRACE_POTRF) & (cnt >= 18)]
+    if len(po):
+        panels = sum(po[:, 2 + 2 * p] - (po[:, 1] if p == 0 else po[:, 1 + 2 * p]) for p in range(8))
+        updates = sum(po[:, 3 + 2 * p] - po[:, 2 + 2 * p] for p in range(7))
+        late = ptag >= 10
+        out["diagonal_factor_us"] = {"load": med(po[:, 1] - po[:, 0]), "panels": med(panels),
+                                     "updates": med(updates), "write": med(po[:, 17] - po[:, 16]),
+                                     "total": med(po[:, 17] - po[:, 0]),
+                                     "total_late_steps": med((po[:, 17] - po[:, 0])[late])}
+    tr = kind == TRACE_TRSM
+    if tr.any():
+        out["block_solve_workgroup_us"] = {"fill_and_rows": med(st[tr, 1] - st[tr, 0]),
+                                           "steps_128": med(st[tr, 2] - st[tr, 1])}
+    # the chain, step by step: diagonal factor k -> solve k -> update of block k+1 -> factor k+1
+    spans = {}
+    for kd in (TRACE_POTRF, TRACE_TRSM, TRACE_DIAG, TRACE_TILE):
+        sel = kind == kd
+        last = np.where(cnt[sel] > 0, st[sel, np.maximum(cnt[sel] - 1, 0)], 0.0)
+        for t, a, b in zip(tag[sel], st[sel, 0], last):
+            lo, hi = spans.get((kd, int(t)), (np.inf, -np.inf))
+            spans[(kd, int(t))] = (min(lo, a), max(hi, b))
+    gaps, solve, diag, tiles = [], [], [], []
+    for k in sorted(t for (kd, t) in spans if kd == TRACE_POTRF):
+        if (TRACE_TRSM, k) not in spans or (TRACE_DIAG, k + 1) not in spans or (TRACE_POTRF, k + 1) not in spans:
+            continue
+        p0, p1 = spans[(TRACE_POTRF, k)]
+        s0, s1 = spans[(TRACE_TRSM, k)]
+        d0, d1 = spans[(TRACE_DIAG, k + 1)]
+        n0 = spans[(TRACE_POTRF, k + 1)][0]
+        gaps.append((s0 - p1) + (d0 - s1) + (n0 - d1))
+        solve.append(s1 - s0)
+        diag.append(d1 - d0)
+        if (TRACE_TILE, k + 1) in spans:
+            tiles.append(spans[(TRACE_TILE, k + 1)][1] - spans[(TRACE_TILE, k + 1)][0])
+    out["chain_step_us"] = {"solve_span": med(solve), "diagonal_update_span": med(diag),
+                            "gaps_between_launches": med(gaps), "step_tiles_span": med(tiles), "steps": len(gaps)}
+    return out
+
+
+def trace_layer(args, g, torch, wl, lin, acts, bits, dev):
+    """One pass of the layer (Hessian, factor, quantize) on the trace build, after one untimed pass."""
+    Xd = host_tensor(torch, acts.full(), acts.bf16).to(dev)
+    Wd = host_tensor(torch, lin.weight(), lin.bf16).to(dev)
+    params = g.Params(bits=bits, groupsize=wl.groupsize, blocksize=wl.blocksize, damp=wl.damp)
+    H = torch.zeros((lin.cols, lin.cols), dtype=torch.float32, device=dev)
+    g.gptq_accumulate_hessian(H, Xd)
+    g.quantize(Wd, H, params)
+    cap = 1 << 18
+    buf = torch.zeros(TRACE_REC * (cap + 1), dtype=torch.int64, device=dev)
+    buf[0] = cap
+    torch.cuda.synchronize()
+    g.gptq_trace_set(buf)
+    H.zero_()
+    g.gptq_accumulate_hessian(H, Xd)
+    g.quantize(Wd, H, params)
+    torch.cuda.synchronize()
+    g.gptq_trace_set(None)
+    words = buf.cpu().numpy()
+    out = trace_summary(words, int(words[1]))
+    out["config"] = {"workload": wl.description, "layer": lin.name, "rows": lin.rows, "cols": lin.cols, "bits": bits}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -614,6 +699,12 @@ def main():
 
     wl = synth.workload(args.workload, tokens=args.tokens)
     dev = torch.device("cuda:0")
+    if args.trace:
+        g.LIB_PATH = os.path.join(os.path.dirname(g.__file__), "libgptq_trace.so")
+        lin = wl.linears[args.layer]
+        print(json.dumps({"trace": trace_layer(args, g, torch, wl, lin, wl.hessians[lin.hessian], lin.bits, dev)}),
+              flush=True)
+        return
     if args.whole:
         print(json.dumps(whole_workload(args, g, torch, wl, dev)), flush=True)
         return

@@ -286,6 +286,24 @@ const char* gptq_status_string(int status);
 /* Library version, major * 10000 + minor * 100 + patch. */
 int gptq_version(void);
 
+/* ---------------------------------------------------------------------------
+ * Phase timestamps, a measurement aid (not an operation of the method).  The
+ * library built with the GPTQ_TRACE option (libgptq_trace.so) records, for
+ * each workgroup of the column loop and of the factor's chain (diagonal-block
+ * factor, block-column solve, diagonal-block update, step tiles), the 100 MHz
+ * s_memrealtime clock at its phase boundaries into buf, a device buffer of
+ * uint64 words:
+ *   buf[0] = capacity in records (set by the caller), buf[1] = records
+ *   appended (set to 0 by the caller; the kernels add to it atomically),
+ *   record i at buf[32 * (i + 1)]: kind (1 loop, 2 diagonal factor, 3 solve,
+ *   4 diagonal update, 5 step tile), workgroup index, tag (the 128-column
+ *   block), stamp count, then the stamps.
+ * Records past the capacity are dropped (buf[1] still counts them).  buf ==
+ * NULL stops recording.  The pointer is per device (the current one) and
+ * process-wide, so concurrent calls append to the same buffer.  The library
+ * built without the option returns GPTQ_EUNSUPPORTED and records nothing. */
+int gptq_trace_set(void* buf);
+
 #ifdef __cplusplus
 }
 #endif

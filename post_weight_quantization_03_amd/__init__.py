@@ -97,6 +97,8 @@ def lib():
     L.gptq_status_string.restype = ctypes.c_char_p
     L.gptq_version.argtypes = []
     L.gptq_version.restype = ctypes.c_int
+    L.gptq_trace_set.argtypes = [vp]
+    L.gptq_trace_set.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -153,6 +155,15 @@ def gptq_status_string(status: int) -> str:
 
 def gptq_version() -> int:
     return int(lib().gptq_version())
+
+
+def gptq_trace_set(buf) -> None:
+    """Points the trace build's phase timestamps at buf (an int64 device tensor laid out as
+    gptq_trace_set in gptq.h describes), or stops them (None).  Raises GptqError with
+    GPTQ_EUNSUPPORTED on the library built without tracing."""
+    st = lib().gptq_trace_set(None if buf is None else _ptr(buf))
+    if st:
+        raise GptqError(st, "gptq_trace_set")
 
 
 def gptq_hessian_workspace_bytes(n: int, tokens: int, x_dtype: int) -> int:

@@ -1,7 +1,9 @@
 """Builds the native libraries in-tree.
 
-libgptq.so  -- the HIP kernels and the C ABI (hipcc, gfx950)
-libsynth.so -- the seeded input generator (gcc, OpenMP)
+libgptq.so       -- the HIP kernels and the C ABI (hipcc, gfx950)
+libgptq_trace.so -- the same, built with GPTQ_TRACE: phase timestamps of the column
+                    loop and the factor's chain (gptq_trace_set; bench.py --trace)
+libsynth.so      -- the seeded input generator (gcc, OpenMP)
 """
 
 from __future__ import annotations
@@ -29,14 +31,14 @@ def _run(cmd):
     return out
 
 
-def build_gptq() -> str:
+def build_gptq(trace: bool = False) -> str:
     """Compiles each kernel file to an object (in parallel), then links the shared library."""
     from concurrent.futures import ThreadPoolExecutor
 
     srcs = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
-    obj_dir = os.path.join(ROOT, "_build", "gptq")
+    obj_dir = os.path.join(ROOT, "_build", "gptq_trace" if trace else "gptq")
     os.makedirs(obj_dir, exist_ok=True)
-    cflags = [f for f in HIP_FLAGS if f != "-shared"]
+    cflags = [f for f in HIP_FLAGS if f != "-shared"] + (["-DGPTQ_TRACE"] if trace else [])
 
     def compile_one(src):
         obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
@@ -46,7 +48,7 @@ def build_gptq() -> str:
     jobs = max(1, min(len(srcs), os.cpu_count() or 1, 16))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(compile_one, srcs))
-    out = os.path.join(PKG, "libgptq.so")
+    out = os.path.join(PKG, "libgptq_trace.so" if trace else "libgptq.so")
     tmp = out + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", *objs, "-o", tmp])
     os.replace(tmp, out)
@@ -63,7 +65,7 @@ def build_synth() -> str:
 
 
 def build_all():
-    return [build_synth(), build_gptq()]
+    return [build_synth(), build_gptq(), build_gptq(trace=True)]
 
 
 if __name__ == "__main__":

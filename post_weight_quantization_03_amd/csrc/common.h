@@ -26,6 +26,50 @@ __device__ __forceinline__ void raise_status(int* st, int code) { atomicMax(st, 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---------------------------------------------------------------------------
+// Phase timestamps, a build option (libgptq_trace.so, built with -DGPTQ_TRACE).
+// The column loop's workgroups and the factor chain's kernels read the 100 MHz
+// s_memrealtime clock at their phase boundaries and thread 0 of each workgroup
+// appends one record to a device buffer set by gptq_trace_set:
+//   buf[0] = capacity in records, buf[1] = records appended (atomic),
+//   record i at buf[32 (i + 1)]: kind, workgroup, tag, stamp count, stamps.
+// Device variables are per kernel file (no relocatable device code), so each
+// instrumented file holds its own buffer pointer and setter.  Without the
+// option the macros are empty and nothing of this is compiled.
+enum TraceKind { TR_LOOP = 1, TR_POTRF = 2, TR_TRSM = 3, TR_DIAG = 4, TR_TILE = 5 };
+constexpr int TRACE_REC = 32;           // words per record
+constexpr int TRACE_STAMPS = TRACE_REC - 4;
+#ifdef GPTQ_TRACE
+namespace {
+__device__ unsigned long long* trace_buf;
+__device__ __forceinline__ void trace_write(int kind, int64_t tag, const unsigned long long* t, int n) {
+  unsigned long long* b = trace_buf;
+  if (b == nullptr || threadIdx.x != 0) return;
+  const unsigned long long i = atomicAdd(b + 1, 1ull);
+  if (i >= b[0]) return;
+  unsigned long long* r = b + TRACE_REC * (i + 1);
+  r[0] = (unsigned long long)kind;
+  r[1] = blockIdx.x;
+  r[2] = (unsigned long long)tag;
+  r[3] = (unsigned long long)n;
+  for (int j = 0; j < n && j < TRACE_STAMPS; ++j) r[4 + j] = t[j];
+}
+}  // namespace
+#define GPTQ_TRACE_DECL unsigned long long trace_t_[TRACE_STAMPS]; int trace_n_ = 0
+#define GPTQ_TRACE_STAMP() (trace_t_[trace_n_++] = __builtin_amdgcn_s_memrealtime())
+#define GPTQ_TRACE_WRITE(kind, tag) trace_write(kind, tag, trace_t_, trace_n_)
+#define GPTQ_TRACE_ONLY(...) __VA_ARGS__
+#define GPTQ_TRACE_SETTER(name) \
+  hipError_t name(unsigned long long* p) { return hipMemcpyToSymbol(HIP_SYMBOL(trace_buf), &p, sizeof(p)); }
+#else
+#define GPTQ_TRACE_ONLY(...)
+#define GPTQ_TRACE_DECL
+#define GPTQ_TRACE_STAMP()
+#define GPTQ_TRACE_WRITE(kind, tag)
+#endif
+hipError_t trace_set_factor(unsigned long long* p);  // trace build only
+hipError_t trace_set_quant(unsigned long long* p);
+
+// ---------------------------------------------------------------------------
 // fp32 MFMA GEMM:  C(m, n) = alpha * sum_k A(m, k) B(k, n) + (beta ? C(m, n) : 0)
 //   A(m, k) = A[m * lda + k]
 //   B(k, n) = B[k * ldb + n]        (b_kmajor)   or   B[n * ldb + k]   (!b_kmajor)

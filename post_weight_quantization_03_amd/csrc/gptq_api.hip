@@ -78,6 +78,17 @@ const char* gptq_status_string(int status) {
 
 int gptq_version(void) { return VERSION; }
 
+int gptq_trace_set(void* buf) {
+#ifdef GPTQ_TRACE
+  auto* p = static_cast<unsigned long long*>(buf);
+  if (gptq::trace_set_factor(p) != hipSuccess || gptq::trace_set_quant(p) != hipSuccess) return GPTQ_EHIP;
+  return GPTQ_OK;
+#else
+  (void)buf;
+  return GPTQ_EUNSUPPORTED;
+#endif
+}
+
 size_t gptq_hessian_workspace_bytes(int64_t n, int64_t tokens, gptq_dtype x_dtype) {
   if (n <= 0 || tokens <= 0 || n > MAX_DIM || tokens > MAX_DIM) return 0;
   return hessian_workspace(n, tokens, x_dtype);

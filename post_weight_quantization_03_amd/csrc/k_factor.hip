@@ -232,13 +232,15 @@ __device__ __forceinline__ void potrf_update(float (*As)[LP], int wave, int lane
 }
 
 template <int P>
-__device__ __forceinline__ void potrf_step(float (*As)[LP], int wave, int lane) {
+__device__ __forceinline__ void potrf_step(float (*As)[LP], int wave, int lane, unsigned long long* tr) {
   potrf_panel<P>(As, wave, lane);
   __syncthreads();
+  GPTQ_TRACE_ONLY(tr[2 + 2 * P] = __builtin_amdgcn_s_memrealtime();)  // panel P
   if constexpr (P + 1 < NB / PB) {
     potrf_update<P>(As, wave, lane);
     __syncthreads();
-    potrf_step<P + 1>(As, wave, lane);
+    GPTQ_TRACE_ONLY(tr[3 + 2 * P] = __builtin_amdgcn_s_memrealtime();)  // its update
+    potrf_step<P + 1>(As, wave, lane, tr);
   }
 }
 
@@ -251,6 +253,9 @@ __device__ __forceinline__ bool block_vec(const float* A, int64_t n, int kb) {
 constexpr int POTRF_LDS = NB * LP * 4;
 
 __device__ __forceinline__ void potrf_diag(const float* A, int64_t n, int64_t k0, float* Lt, int* status, char* lds) {
+  // stamps: start, loaded, then panel / update pairs, written
+  unsigned long long tr[2 + 2 * (NB / PB) - 1 + 1];
+  GPTQ_TRACE_ONLY(tr[0] = __builtin_amdgcn_s_memrealtime();)
   float(*As)[LP] = reinterpret_cast<float(*)[LP]>(lds);
   const int kb = (int)((n - k0) < NB ? (n - k0) : NB);
   const int tid = threadIdx.x;
@@ -280,8 +285,9 @@ __device__ __forceinline__ void potrf_diag(const float* A, int64_t n, int64_t k0
     }
   }
   __syncthreads();
+  GPTQ_TRACE_ONLY(tr[1] = __builtin_amdgcn_s_memrealtime();)
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  potrf_step<0>(As, wave, lane);
+  potrf_step<0>(As, wave, lane, tr);
   if (tid < kb) {
     const float d = As[tid][tid];
     if (!(d > 0.0f && d < INFINITY)) raise_status(status, GPTQ_ENOTPD);
@@ -297,6 +303,8 @@ __device__ __forceinline__ void potrf_diag(const float* A, int64_t n, int64_t k0
     v.w = q + 3 >= r ? As[r][q + 3] : 0.0f;
     *reinterpret_cast<float4*>(Lt + r * NB + q) = v;
   }
+  GPTQ_TRACE_ONLY(tr[2 * (NB / PB) + 1] = __builtin_amdgcn_s_memrealtime();
+                  trace_write(TR_POTRF, k0 / NB, tr, 2 * (NB / PB) + 2);)
 }
 
 __global__ __launch_bounds__(256) void k_potrf_diag(const float* A, int64_t n, int64_t k0, float* Lt, int* status) {
@@ -332,6 +340,8 @@ __global__ __launch_bounds__(256) void k_factor_step(GemmF32 g, int ntri, int rr
     potrf_diag(A, n, k0n, Lt, status, lds);
     return;
   }
+  GPTQ_TRACE_DECL;
+  GPTQ_TRACE_STAMP();
   const int u = (int)blockIdx.x - 1;
   if (near_only) {
     // tile column 0 only (block column k+1): the lower tiles below its
@@ -340,6 +350,8 @@ __global__ __launch_bounds__(256) void k_factor_step(GemmF32 g, int ntri, int rr
       gemm_tile<128, false, true>(g, rrows + u + 1, 0, 0, lds);
     else
       gemm_tile<128, false, true>(g, u - (nt - 1), 0, 0, lds);
+    GPTQ_TRACE_STAMP();
+    GPTQ_TRACE_WRITE(TR_TILE, k0n / NB);
     return;
   }
   if (u < ntri - 1) {
@@ -352,6 +364,8 @@ __global__ __launch_bounds__(256) void k_factor_step(GemmF32 g, int ntri, int rr
     const int v = u - (ntri - 1);
     gemm_tile<128, false, true>(g, v / nt, v % nt, 0, lds);
   }
+  GPTQ_TRACE_STAMP();
+  GPTQ_TRACE_WRITE(TR_TILE, k0n / NB);
 }
 
 // Look-ahead update of block k+1's diagonal block, D -= P P^T, with P =
@@ -366,6 +380,8 @@ __global__ __launch_bounds__(256) void k_factor_step(GemmF32 g, int ntri, int rr
 template <int PASSES>
 __global__ __launch_bounds__(256) void k_diag_update(float* A, int64_t n, int64_t k0, int64_t c1, int kb1) {
   __shared__ float part[4][32 * 32];
+  GPTQ_TRACE_DECL;
+  GPTQ_TRACE_STAMP();
   const int t = blockIdx.x;
   int ti = 0;
   while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
@@ -424,6 +440,8 @@ __global__ __launch_bounds__(256) void k_diag_update(float* A, int64_t n, int64_
     const float sum = ((part[0][e] + part[1][e]) + part[2][e]) + part[3][e];
     if (gi < kb1 && gj < kb1) A[(c1 + gi) * n + c1 + gj] = dv[q] - sum;
   }
+  GPTQ_TRACE_STAMP();
+  GPTQ_TRACE_WRITE(TR_DIAG, c1 / NB);
 }
 
 // ------------------------------------------------------------------ triangular solves
@@ -474,14 +492,23 @@ __device__ __forceinline__ void trsm_steps(TrsmLane& L, const float (*Lt)[NB], s
   (trsm_step<Js>(L, Lt), ...);
 }
 
-__global__ __launch_bounds__(256) void k_trsm_block(float* A, const float* Ltk, int64_t n, int64_t k0, int kb) {
+// 16 rows a workgroup (4 waves): one wave a SIMD keeps each row's 128-step
+// chain at full issue rate (32-row workgroups, two waves a SIMD, measured
+// slower per launch at n = 4096 and 11008).
+constexpr int TRSM_THREADS = 256;
+constexpr int TRSM_ROWS = TRSM_THREADS / 16;
+
+__global__ __launch_bounds__(TRSM_THREADS) void k_trsm_block(float* A, const float* Ltk, int64_t n, int64_t k0,
+                                                             int kb) {
   __shared__ __attribute__((aligned(16))) float Lt[NB][NB];
   __shared__ float rL[NB];
+  GPTQ_TRACE_DECL;
+  GPTQ_TRACE_STAMP();  // start
   const int tid = threadIdx.x;
   TrsmLane L;
   const int lane = tid & 63;
   L.t = lane & 15;
-  const int64_t grow = (int64_t)blockIdx.x * 16 + (tid >> 6) * 4 + (lane >> 4);
+  const int64_t grow = (int64_t)blockIdx.x * TRSM_ROWS + (tid >> 6) * 4 + (lane >> 4);
   const bool ok = grow < n;
   const bool ident = grow >= k0 && grow < k0 + kb;
   const int rr = (int)(grow - k0);
@@ -504,16 +531,16 @@ __global__ __launch_bounds__(256) void k_trsm_block(float* A, const float* Ltk, 
   }
   // Lt[j][m] = L[m][j] for m > j, else 0 (the buffer holds zeros below its diagonal)
   {
-    constexpr int PER = NB * NB / 4 / 256;
+    constexpr int PER = NB * NB / 4 / TRSM_THREADS;
     float4 v[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int idx = tid + 256 * i, j = idx >> 5, m = 4 * (idx & 31);
+      const int idx = tid + TRSM_THREADS * i, j = idx >> 5, m = 4 * (idx & 31);
       v[i] = *reinterpret_cast<const float4*>(Ltk + j * NB + m);
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int idx = tid + 256 * i, j = idx >> 5, m = 4 * (idx & 31);
+      const int idx = tid + TRSM_THREADS * i, j = idx >> 5, m = 4 * (idx & 31);
       float4 w = v[i];
       w.x = m + 0 > j ? w.x : 0.0f;
       w.y = m + 1 > j ? w.y : 0.0f;
@@ -524,12 +551,15 @@ __global__ __launch_bounds__(256) void k_trsm_block(float* A, const float* Ltk, 
   }
   if (tid < NB) rL[tid] = tid < kb ? 1.0f / Ltk[tid * (NB + 1)] : 0.0f;
   __syncthreads();
+  GPTQ_TRACE_STAMP();  // rows loaded, L^T in LDS
 
 #pragma unroll
   for (int i = 0; i < 8; ++i) L.ru[i] = rL[8 * L.t + i];
   L.un[0] = *reinterpret_cast<const float4*>(&Lt[0][8 * L.t]);
   L.un[1] = *reinterpret_cast<const float4*>(&Lt[0][8 * L.t + 4]);
   trsm_steps(L, Lt, std::make_integer_sequence<int, NB>{});
+  GPTQ_TRACE_STAMP();  // 128 steps
+  GPTQ_TRACE_WRITE(TR_TRSM, k0 / NB);
   if (!ok) return;
   float y[8];
 #pragma unroll
@@ -589,6 +619,10 @@ __global__ void k_copy_status(const int* src, int32_t* dst) {
 
 }  // namespace
 
+#ifdef GPTQ_TRACE
+GPTQ_TRACE_SETTER(trace_set_factor)
+#endif
+
 size_t factor_scratch_floats(int64_t n) { return (size_t)((n + NB - 1) / NB) * NB * NB; }
 
 hipError_t fill_i32(int* p, int64_t n, int v, hipStream_t stream) {
@@ -633,15 +667,15 @@ hipError_t factor_run(float* H, int64_t n, float damp, const FactorWs& ws, hipSt
   hipLaunchKernelGGL(k_potrf_diag, dim3(1), dim3(256), 0, stream, (const float*)ws.A, n, (int64_t)0, ws.Lt,
                      ws.status);
   FCHECK(hipGetLastError());
-  const unsigned grows = (unsigned)((n + 15) / 16);
+  const unsigned grows = (unsigned)((n + TRSM_ROWS - 1) / TRSM_ROWS);
   int64_t kp = 0;  // first column of the panels whose update of the columns past the next block is pending
   for (int64_t k = 0; k < nk; ++k) {
     const int64_t k0 = k * NB;
     const int64_t kb = (n - k0) < NB ? (n - k0) : NB;
     const int64_t c1 = k0 + kb, rest = n - c1;
     // block column k: the panel below, the inverse above, L_kk^-T on its rows
-    hipLaunchKernelGGL(k_trsm_block, dim3(grows), dim3(256), 0, stream, ws.A, (const float*)(ws.Lt + k * NB * NB), n,
-                       k0, (int)kb);
+    hipLaunchKernelGGL(k_trsm_block, dim3(grows), dim3(TRSM_THREADS), 0, stream, ws.A,
+                       (const float*)(ws.Lt + k * NB * NB), n, k0, (int)kb);
     FCHECK(hipGetLastError());
     if (rest <= 0) break;
     const int kb1 = (int)(rest < NB ? rest : NB);

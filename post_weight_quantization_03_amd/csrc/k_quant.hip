@@ -295,6 +295,8 @@ constexpr int QUANT_LDS = B * B * 4 + B * 4 + 16 * B * 4;
 // under it.
 template <int MODE>
 __device__ __forceinline__ void quant_block_wg(const BlockArgs& a, int64_t wg, char* lds) {
+  GPTQ_TRACE_DECL;
+  GPTQ_TRACE_STAMP();  // start
   float(*Us)[B] = reinterpret_cast<float(*)[B]>(lds);
   float* rUd = reinterpret_cast<float*>(lds + B * B * 4);
   float(*Es)[B] = reinterpret_cast<float(*)[B]>(lds + B * B * 4 + B * 4);
@@ -363,6 +365,7 @@ __device__ __forceinline__ void quant_block_wg(const BlockArgs& a, int64_t wg, c
 #pragma unroll
       for (int h = 0; h < 2; ++h) acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[kk], ub[h][kk], acc[h], 0, 0, 0);
   }
+  GPTQ_TRACE_STAMP();  // operands loaded, near update issued
   if (vec) {
 #pragma unroll
     for (int i = 0; i < B * B / 4 / 256; ++i) {
@@ -390,7 +393,9 @@ __device__ __forceinline__ void quant_block_wg(const BlockArgs& a, int64_t wg, c
 #pragma unroll
       for (int r = 0; r < 4; ++r) Es[4 * g + r][32 * wv + 16 * h + i16] = acc[h][r];
   }
+  GPTQ_TRACE_STAMP();  // U block and update stored
   __syncthreads();
+  GPTQ_TRACE_STAMP();  // barrier
   if (a.Eprev) {
     const int rl = (tid >> 6) * 4 + (lane >> 4);
     const float4 d0 = *reinterpret_cast<const float4*>(&Es[rl][t8]);
@@ -448,7 +453,9 @@ __device__ __forceinline__ void quant_block_wg(const BlockArgs& a, int64_t wg, c
     }
   }
 
+  GPTQ_TRACE_STAMP();  // update applied, group range taken
   run_steps<MODE>(L, a, Us, row, row_ok, std::make_integer_sequence<int, B>{});
+  GPTQ_TRACE_STAMP();  // 128 steps
 
   // every column's decision again, from its value at decision time (the step's
   // operations exactly); e and the loss vanish past the block's width
@@ -489,6 +496,8 @@ __device__ __forceinline__ void quant_block_wg(const BlockArgs& a, int64_t wg, c
   float* ep = a.E + row * a.ldE + 8 * L.t;
   *reinterpret_cast<float4*>(ep) = make_float4(e[0], e[1], e[2], e[3]);
   *reinterpret_cast<float4*>(ep + 4) = make_float4(e[4], e[5], e[6], e[7]);
+  GPTQ_TRACE_STAMP();  // outputs written
+  GPTQ_TRACE_WRITE(TR_LOOP, a.c0 / B);
 }
 
 // One launch per 128-column block b: the column loop of block b (workgroups
@@ -535,6 +544,10 @@ hipError_t launch_block(const BlockArgs& a, FarJobs far, int64_t nq, hipStream_t
 }
 
 }  // namespace
+
+#ifdef GPTQ_TRACE
+GPTQ_TRACE_SETTER(trace_set_quant)
+#endif
 
 size_t quant_split_bytes(int64_t cols, int64_t groupsize) {
   const bool overlap = groupsize <= B || groupsize >= cols;

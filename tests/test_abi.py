@@ -27,9 +27,20 @@ def test_every_declared_symbol_is_exported():
                           "gptq_quantize_workspace_bytes", "gptq_quantize_layer", "gptq_pack",
                           "gptq_dequant_gemv", "gptq_dequant_gemm", "gptq_hadamard_rows", "gptq_hadamard_hessian",
                           "gptq_cross_workspace_bytes", "gptq_accumulate_cross", "gptq_qep_workspace_bytes",
-                          "gptq_qep_correct", "gptq_status_string", "gptq_version"}
+                          "gptq_qep_correct", "gptq_status_string", "gptq_version", "gptq_trace_set"}
     for n in names:
         assert hasattr(lib, n), n
+    # the trace build exports the same symbols
+    trace = ctypes.CDLL(os.path.join(os.path.dirname(g.LIB_PATH), "libgptq_trace.so"))
+    for n in names:
+        assert hasattr(trace, n), n
+
+
+def test_trace_entry_is_refused_by_the_plain_build():
+    """The library built without GPTQ_TRACE records nothing and says so (no device call)."""
+    assert g.lib().gptq_trace_set(None) == g.GPTQ_EUNSUPPORTED
+    with pytest.raises(g.GptqError):
+        g.gptq_trace_set(None)
 
 
 def test_version_and_status_strings():

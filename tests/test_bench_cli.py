@@ -66,3 +66,47 @@ def test_cpu_baseline_reports_host_and_stages():
     assert r["seconds_full_layer"] == pytest.approx(sum(r["stage_seconds"].values()))
     h = r["host"]
     assert h["cpu_count"] == os.cpu_count() and h["cpu_model"] and r["cores"] >= 1
+
+
+def test_trace_decoding_on_a_synthetic_buffer():
+    """bench.trace_summary on records laid out as gptq_trace_set describes, with known phases."""
+    import numpy as np
+    R = bench.TRACE_REC
+    recs = []
+
+    def add(kind, wg, tag, stamps):
+        r = np.zeros(R, dtype=np.int64)
+        r[:4] = (kind, wg, tag, len(stamps))
+        r[4:4 + len(stamps)] = stamps
+        recs.append(r)
+
+    # two loop workgroups of block 1: phases of 5, 1, 0.1, 0.5, 7, 1.5 us (stamps in 10 ns ticks)
+    for wg in range(2):
+        base = 1000 * wg
+        add(bench.TRACE_LOOP, wg, 1, np.cumsum([base, 500, 100, 10, 50, 700, 150]))
+    # diagonal factors of blocks 0 and 1: load 2 us, panels 1.5 us, updates 0.5 us, write 1 us
+    for k in range(2):
+        st = [100000 * k, 100000 * k + 200]
+        for p in range(8):
+            st.append(st[-1] + 150)
+            if p < 7:
+                st.append(st[-1] + 50)
+        st.append(st[-1] + 100)
+        add(bench.TRACE_POTRF, 0, k, st)
+    p0_end = 200 + 8 * 150 + 7 * 50 + 100  # end of the diagonal factor of block 0
+    # solve of block 0: 2 us after the factor, spanning 6 us; update of block 1: 3 us later, 2 us long
+    add(bench.TRACE_TRSM, 0, 0, [p0_end + 200, p0_end + 300, p0_end + 800])
+    add(bench.TRACE_DIAG, 0, 1, [p0_end + 1100, p0_end + 1300])
+    words = np.zeros(R * (len(recs) + 1), dtype=np.int64)
+    words[0] = 100
+    words[R:] = np.concatenate(recs)
+    out = bench.trace_summary(words, len(recs))
+    lw = out["loop_workgroup_us"]
+    assert lw["operands_and_near_update"] == 5.0 and lw["steps_128"] == 7.0 and abs(lw["total"] - 15.1) < 1e-9
+    df = out["diagonal_factor_us"]
+    assert df["load"] == 2.0 and df["panels"] == 12.0 and df["updates"] == 3.5 and df["write"] == 1.0
+    assert out["block_solve_workgroup_us"] == {"fill_and_rows": 1.0, "steps_128": 5.0}
+    ch = out["chain_step_us"]
+    assert ch["steps"] == 1 and ch["solve_span"] == 6.0 and ch["diagonal_update_span"] == 2.0
+    # gaps: factor end -> solve 2 us, solve end -> update 3 us, update end -> next factor
+    assert abs(ch["gaps_between_launches"] - (2.0 + 3.0 + (100000 - (p0_end + 1300)) / 100.0)) < 1e-9
