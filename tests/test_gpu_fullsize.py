@@ -6,7 +6,8 @@ outputs it can compute one by one:
   Hessian   every calibration token of the workload goes through the GPU in one
             call; the oracle recomputes H[i, j] = 2 sum_t X[t, i] X[t, j] in float64
             for a sample of columns (both ends of the range, tile edges, random
-            ones) and every pair among them.
+            ones) and every pair among them; for q_proj (4096 columns, all
+            262144 tokens) it recomputes every entry.
   Quantize  the GPU quantizes the full layer and the oracle runs the GPTQ loop
             for every row against its own fp64 factor; the replay protocol
             compares codes, scales and zeros, and the relative layer output
@@ -44,6 +45,39 @@ def _sample_cols(n, k, seed):
     edges = [0, 1, 127, 128, 255, 256, n // 2, n - 257, n - 256, n - 2, n - 1]
     extra = rng.choice(n, size=k, replace=False)
     return np.unique(np.clip(np.concatenate([edges, extra]), 0, n - 1))
+
+
+def test_hessian_full_size_whole_matrix_q_proj():
+    """The q_proj Hessian (4096 columns, all 262144 tokens, the bench's call) against the oracle's
+    fp64 H over every entry: the whole-matrix gate of the small cases at the full size."""
+    import torch
+
+    import post_weight_quantization_03_amd as g
+    from oracle import hessian_ref
+    acts = synth.workload("q_proj_4096").hessians["x"]
+    n, N = acts.n, acts.tokens
+    say(f"-- q_proj_4096/x: n={n} tokens={N}, every entry")
+    X = acts.full()
+    Xd = bf16_dev(X)
+    H = torch.zeros((n, n), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(max(g.gptq_hessian_workspace_bytes(n, N, g.GPTQ_BF16), 1), dtype=torch.uint8,
+                     device="cuda:0")
+    g.gptq_accumulate_hessian(H, Xd, workspace=ws)
+    torch.cuda.synchronize()
+    del Xd, ws
+    Hg = H.cpu().numpy().astype(np.float64)
+    del H
+    t0 = time.perf_counter()
+    Hr = hessian_ref((synth.bf16_to_f32(X[t:t + 16384]) for t in range(0, N, 16384)), n)
+    say(f"   oracle H took {time.perf_counter() - t0:.1f}s")
+    del X
+    d = np.sqrt(np.outer(np.diag(Hr), np.diag(Hr)))
+    rel_entry = np.abs(Hg - Hr) / d
+    rel_fro = np.linalg.norm(Hg - Hr) / np.linalg.norm(Hr)
+    say(f"   max |dH|/sqrt(Hii Hjj) {rel_entry.max():.3e}, Frobenius {rel_fro:.3e}")
+    assert rel_fro <= H_RTOL
+    assert rel_entry.max() <= H_RTOL
+    np.testing.assert_array_equal(Hg, Hg.T)
 
 
 @pytest.mark.parametrize("wl,key", [("q_proj_4096", "x"), ("mlp_7b", "x"), ("mlp_7b", "mid"),
