@@ -198,9 +198,12 @@ def gemv_measure(g, torch, packed, scales, zeros, rows, cols, bits, groupsize, d
     Xb = torch.randn(B, cols, dtype=torch.float32, device=dev, generator=torch.Generator(dev).manual_seed(2))
     Yb = torch.empty(B, rows, dtype=torch.float32, device=dev)
     fb = g.lib().gptq_dequant_gemm
+    wsb = g.gptq_dequant_gemm_workspace_bytes(rows, cols, bits, groupsize, B)
+    wsp = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
     bcalls = [(ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(s_.data_ptr()), ctypes.c_void_p(z.data_ptr()), rows,
                cols, bits, groupsize, ctypes.c_void_p(Xb.data_ptr()), g.GPTQ_F32, cols, B,
-               ctypes.c_void_p(Yb.data_ptr()), rows, stream) for p, s_, z in bufs]
+               ctypes.c_void_p(Yb.data_ptr()), rows, ctypes.c_void_p(wsp.data_ptr()), wsb, stream)
+              for p, s_, z in bufs]
     for a in bcalls:
         if fb(*a):
             raise RuntimeError("gptq_dequant_gemm failed")
@@ -217,7 +220,9 @@ def gemv_measure(g, torch, packed, scales, zeros, rows, cols, bits, groupsize, d
     return {"kernel": "k_dequant_gemv", "shape": [rows, cols], "bits": bits, "groupsize": groupsize,
             "us_per_launch": us, "algorithmic_bytes": alg_bytes, "achieved_GBs": gbs, "peak_GBs": PEAK_HBM_GBS,
             "frac": gbs / PEAK_HBM_GBS, "weight_copies": copies,
-            "batch8": {"kernel": "k_dequant_gemm", "us_per_launch": us_b, "algorithmic_bytes": bytes_b,
+            "batch8": {"kernel": ("k_dequant_mma" + (" + k_mma_reduce" if wsb else "")
+                                  if groupsize == -1 or groupsize % 128 == 0 else "k_dequant_gemm"),
+                       "us_per_launch": us_b, "algorithmic_bytes": bytes_b,
                        "achieved_GBs": bytes_b / (us_b * 1e-6) / 1e9,
                        "frac": bytes_b / (us_b * 1e-6) / 1e9 / PEAK_HBM_GBS, "us_per_vector": us_b / B}}
 

@@ -197,15 +197,29 @@ int gptq_dequant_gemv(const uint32_t* packed, const float* scales, const uint8_t
                       int64_t cols, int32_t bits, int32_t groupsize, const void* x, gptq_dtype x_dtype, float* y,
                       gptq_stream_t stream);
 
-/* The same product for a small batch: Y[t, :] = W^ X[t, :] for t < batch, with
+/* The same product for a batch: Y[t, :] = W^ X[t, :] for t < batch, with
  * X [batch, cols] (row stride ldx >= cols, bf16 or fp32; for bf16 ldx even)
- * and Y [batch, rows] fp32 (row stride ldy >= rows).  The codes are read once
- * per group of up to 8 vectors.  Accumulation as in gptq_dequant_gemv; a batch
- * of one gives exactly gptq_dequant_gemv's result.  batch == 0 or rows == 0:
- * no work.  Y must not alias the inputs. */
+ * and Y [batch, rows] fp32 (row stride ldy >= rows).  X finite.
+ *   - batch of one: exactly gptq_dequant_gemv's result.
+ *   - batch >= 2 with groupsize -1 or a multiple of 128: the matrix-core path.
+ *     The codes are read once per group of up to 16 vectors and converted
+ *     exactly to bf16; a bf16 x is exact in bf16 and an fp32 x is split
+ *     exactly into three bf16 parts, so the products are exact and only the
+ *     fp32 accumulation rounds (inside the matrix core, then per 128-column
+ *     chunk, slice and part, in a fixed order).  Column slices go to the
+ *     workspace as partial sums, which a second kernel adds in slice order.
+ *   - other batches: VALU kernels, groups of up to 8 vectors, accumulation as
+ *     in gptq_dequant_gemv; no workspace.
+ * Results are bit-reproducible run to run.  workspace: at least
+ * gptq_dequant_gemm_workspace_bytes(rows, cols, bits, groupsize, batch) bytes,
+ * 4-byte aligned (NULL when that is 0; GPTQ_EWORKSPACE when short).  batch == 0
+ * or rows == 0: no work.  Y must not alias the inputs or the workspace. */
+size_t gptq_dequant_gemm_workspace_bytes(int64_t rows, int64_t cols, int32_t bits, int32_t groupsize,
+                                        int64_t batch);
 int gptq_dequant_gemm(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
                       int64_t cols, int32_t bits, int32_t groupsize, const void* X, gptq_dtype x_dtype, int64_t ldx,
-                      int64_t batch, float* Y, int64_t ldy, gptq_stream_t stream);
+                      int64_t batch, float* Y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                      gptq_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Fixed randomised Hadamard rotation, the untrained form of the rotation
@@ -289,14 +303,16 @@ int gptq_version(void);
 /* ---------------------------------------------------------------------------
  * Phase timestamps, a measurement aid (not an operation of the method).  The
  * library built with the GPTQ_TRACE option (libgptq_trace.so) records, for
- * each workgroup of the column loop and of the factor's chain (diagonal-block
- * factor, block-column solve, diagonal-block update, step tiles), the 100 MHz
+ * each workgroup of the column loop, of the factor's chain (diagonal-block
+ * factor, block-column solve, diagonal-block update, step tiles) and of the
+ * matrix-core batch product, the 100 MHz
  * s_memrealtime clock at its phase boundaries into buf, a device buffer of
  * uint64 words:
  *   buf[0] = capacity in records (set by the caller), buf[1] = records
  *   appended (set to 0 by the caller; the kernels add to it atomically),
  *   record i at buf[32 * (i + 1)]: kind (1 loop, 2 diagonal factor, 3 solve,
- *   4 diagonal update, 5 step tile), workgroup index, tag (the 128-column
+ *   4 diagonal update, 5 step tile, 6 batch product), workgroup index (for
+ *   6 the column slice), tag (the 128-column block; for 6 the 128-row
  *   block), stamp count, then the stamps.
  * Records past the capacity are dropped (buf[1] still counts them).  buf ==
  * NULL stops recording.  The pointer is per device (the current one) and

@@ -78,7 +78,10 @@ def lib():
     L.gptq_pack.restype = ctypes.c_int
     L.gptq_dequant_gemv.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, vp, vp]
     L.gptq_dequant_gemv.restype = ctypes.c_int
-    L.gptq_dequant_gemm.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, i64, i64, vp, i64, vp]
+    L.gptq_dequant_gemm_workspace_bytes.argtypes = [i64, i64, i32, i32, i64]
+    L.gptq_dequant_gemm_workspace_bytes.restype = ctypes.c_size_t
+    L.gptq_dequant_gemm.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, i64, i64, vp, i64, vp,
+                                    ctypes.c_size_t, vp]
     L.gptq_dequant_gemm.restype = ctypes.c_int
     L.gptq_hadamard_rows.argtypes = [vp, ctypes.c_int, i64, vp, i64, i64, i64, vp, i32, vp]
     L.gptq_hadamard_rows.restype = ctypes.c_int
@@ -262,8 +265,14 @@ def gptq_dequant_gemv(packed, scales, zeros, bits: int, groupsize: int, x, y, st
     return y
 
 
-def gptq_dequant_gemm(packed, scales, zeros, bits: int, groupsize: int, X, Y, stream=None):
-    """Y [batch, rows] fp32 = (W^ X^T)^T for X [batch, cols] bf16 or fp32 (unit column stride)."""
+def gptq_dequant_gemm_workspace_bytes(rows: int, cols: int, bits: int, groupsize: int, batch: int) -> int:
+    return int(lib().gptq_dequant_gemm_workspace_bytes(rows, cols, bits, groupsize, batch))
+
+
+def gptq_dequant_gemm(packed, scales, zeros, bits: int, groupsize: int, X, Y, workspace=None, stream=None):
+    """Y [batch, rows] fp32 = (W^ X^T)^T for X [batch, cols] bf16 or fp32 (unit column stride).
+    workspace: a device tensor of at least gptq_dequant_gemm_workspace_bytes bytes; allocated here
+    (through torch) when None."""
     _check_dev(packed, scales, zeros, Y)
     torch = _torch()
     rows = packed.shape[0]
@@ -275,9 +284,13 @@ def gptq_dequant_gemm(packed, scales, zeros, bits: int, groupsize: int, X, Y, st
             or packed.element_size() != 4 or scales.shape != zeros.shape or scales.shape[0] != rows):
         raise ValueError("shape or dtype mismatch")
     ldx = X.stride(0) if batch > 1 else cols
+    need = gptq_dequant_gemm_workspace_bytes(rows, cols, bits, groupsize, batch)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Y.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().gptq_dequant_gemm(_ptr(packed), _ptr(scales), _ptr(zeros), rows, cols, bits, groupsize, _ptr(X),
                                  _dtype_code(X), ldx, batch, _ptr(Y), Y.stride(0) if batch > 1 else rows,
-                                 _stream(stream))
+                                 None if workspace is None else _ptr(workspace), wsz, _stream(stream))
     if st:
         raise GptqError(st, "gptq_dequant_gemm")
     return Y

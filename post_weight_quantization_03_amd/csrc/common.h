@@ -27,7 +27,8 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ---------------------------------------------------------------------------
 // Phase timestamps, a build option (libgptq_trace.so, built with -DGPTQ_TRACE).
-// The column loop's workgroups and the factor chain's kernels read the 100 MHz
+// The column loop's workgroups, the factor chain's kernels and the batch
+// product's workgroups read the 100 MHz
 // s_memrealtime clock at their phase boundaries and thread 0 of each workgroup
 // appends one record to a device buffer set by gptq_trace_set:
 //   buf[0] = capacity in records, buf[1] = records appended (atomic),
@@ -35,7 +36,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Device variables are per kernel file (no relocatable device code), so each
 // instrumented file holds its own buffer pointer and setter.  Without the
 // option the macros are empty and nothing of this is compiled.
-enum TraceKind { TR_LOOP = 1, TR_POTRF = 2, TR_TRSM = 3, TR_DIAG = 4, TR_TILE = 5 };
+enum TraceKind { TR_LOOP = 1, TR_POTRF = 2, TR_TRSM = 3, TR_DIAG = 4, TR_TILE = 5, TR_MMA = 6 };
 constexpr int TRACE_REC = 32;           // words per record
 constexpr int TRACE_STAMPS = TRACE_REC - 4;
 #ifdef GPTQ_TRACE
@@ -68,6 +69,7 @@ __device__ __forceinline__ void trace_write(int kind, int64_t tag, const unsigne
 #endif
 hipError_t trace_set_factor(unsigned long long* p);  // trace build only
 hipError_t trace_set_quant(unsigned long long* p);
+hipError_t trace_set_mma(unsigned long long* p);
 
 // ---------------------------------------------------------------------------
 // fp32 MFMA GEMM:  C(m, n) = alpha * sum_k A(m, k) B(k, n) + (beta ? C(m, n) : 0)
@@ -165,6 +167,13 @@ hipError_t dequant_gemv(const uint32_t* packed, const float* scales, const uint8
 hipError_t dequant_gemm(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
                         int64_t cols, int32_t bits, int32_t groupsize, const void* X, bool x_bf16, int64_t ldx,
                         int64_t batch, float* Y, int64_t ldy, hipStream_t stream);
+// The batch product on the matrix cores (k_dequant_mma.hip): batches of two or
+// more, groups a multiple of 128 columns or the whole row.
+bool dequant_mma_supported(int64_t cols, int32_t groupsize, int64_t batch);
+size_t dequant_mma_workspace(int64_t rows, int64_t cols, int64_t batch);
+hipError_t dequant_mma(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
+                       int64_t cols, int32_t bits, int32_t groupsize, const void* X, bool x_bf16, int64_t ldx,
+                       int64_t batch, float* Y, int64_t ldy, void* workspace, hipStream_t stream);
 
 // Fixed randomised Hadamard rotation (k_hadamard.hip).
 int64_t hadamard_chunks(int64_t n);

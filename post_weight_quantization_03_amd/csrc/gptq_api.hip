@@ -81,7 +81,9 @@ int gptq_version(void) { return VERSION; }
 int gptq_trace_set(void* buf) {
 #ifdef GPTQ_TRACE
   auto* p = static_cast<unsigned long long*>(buf);
-  if (gptq::trace_set_factor(p) != hipSuccess || gptq::trace_set_quant(p) != hipSuccess) return GPTQ_EHIP;
+  if (gptq::trace_set_factor(p) != hipSuccess || gptq::trace_set_quant(p) != hipSuccess ||
+      gptq::trace_set_mma(p) != hipSuccess)
+    return GPTQ_EHIP;
   return GPTQ_OK;
 #else
   (void)buf;
@@ -275,9 +277,17 @@ int gptq_dequant_gemv(const uint32_t* packed, const float* scales, const uint8_t
              : GPTQ_EHIP;
 }
 
+size_t gptq_dequant_gemm_workspace_bytes(int64_t rows, int64_t cols, int32_t bits, int32_t groupsize,
+                                        int64_t batch) {
+  if (rows <= 0 || cols <= 0 || batch <= 0 || rows > MAX_DIM || cols > MAX_DIM || batch > MAX_DIM) return 0;
+  if (!dequant_gemv_supported(cols, bits, groupsize) || !dequant_mma_supported(cols, groupsize, batch)) return 0;
+  return dequant_mma_workspace(rows, cols, batch);
+}
+
 int gptq_dequant_gemm(const uint32_t* packed, const float* scales, const uint8_t* zeros, int64_t rows,
                       int64_t cols, int32_t bits, int32_t groupsize, const void* X, gptq_dtype x_dtype, int64_t ldx,
-                      int64_t batch, float* Y, int64_t ldy, gptq_stream_t stream) {
+                      int64_t batch, float* Y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                      gptq_stream_t stream) {
   if (rows < 0 || cols < 0 || batch < 0 || rows > MAX_DIM || cols > MAX_DIM || batch > MAX_DIM) return GPTQ_EINVAL;
   if (!(bits == 2 || bits == 3 || bits == 4 || bits == 8)) return GPTQ_EINVAL;
   if (groupsize == 0 || groupsize < -1) return GPTQ_EINVAL;
@@ -290,6 +300,15 @@ int gptq_dequant_gemm(const uint32_t* packed, const float* scales, const uint8_t
   auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) != 0; };
   if (misaligned(packed) || misaligned(scales) || misaligned(X) || misaligned(Y)) return GPTQ_EINVAL;
   if (x_dtype == GPTQ_BF16 && (ldx & 1)) return GPTQ_EINVAL;  // every row of X dword aligned
+  if (cols > 0 && dequant_mma_supported(cols, groupsize, batch)) {
+    const size_t need = dequant_mma_workspace(rows, cols, batch);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return GPTQ_EWORKSPACE;
+    if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 3)) return GPTQ_EINVAL;
+    return dequant_mma(packed, scales, zeros, rows, cols, bits, groupsize, X, x_dtype == GPTQ_BF16, ldx, batch, Y,
+                       ldy, workspace, (hipStream_t)stream) == hipSuccess
+               ? GPTQ_OK
+               : GPTQ_EHIP;
+  }
   return dequant_gemm(packed, scales, zeros, rows, cols, bits, groupsize, X, x_dtype == GPTQ_BF16, ldx, batch, Y,
                       ldy, (hipStream_t)stream) == hipSuccess
              ? GPTQ_OK

@@ -25,7 +25,8 @@ def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert set(names) == {"gptq_hessian_workspace_bytes", "gptq_accumulate_hessian", "gptq_accumulate_hessian_static",
                           "gptq_quantize_workspace_bytes", "gptq_quantize_layer", "gptq_pack",
-                          "gptq_dequant_gemv", "gptq_dequant_gemm", "gptq_hadamard_rows", "gptq_hadamard_hessian",
+                          "gptq_dequant_gemv", "gptq_dequant_gemm_workspace_bytes", "gptq_dequant_gemm",
+                          "gptq_hadamard_rows", "gptq_hadamard_hessian",
                           "gptq_cross_workspace_bytes", "gptq_accumulate_cross", "gptq_qep_workspace_bytes",
                           "gptq_qep_correct", "gptq_status_string", "gptq_version", "gptq_trace_set"}
     for n in names:
@@ -152,13 +153,30 @@ def test_dequant_gemv_argument_errors():
 def test_dequant_gemm_argument_errors():
     L = g.lib()
     q = L.gptq_dequant_gemm
-    assert q(FAKE, FAKE, FAKE, 8, 256, 4, 128, FAKE, 1, 128, 4, FAKE, 8, None) == g.GPTQ_EINVAL      # ldx < cols
-    assert q(FAKE, FAKE, FAKE, 8, 256, 4, 128, FAKE, 1, 256, 4, FAKE, 4, None) == g.GPTQ_EINVAL      # ldy < rows
-    assert q(FAKE, FAKE, FAKE, 8, 256, 4, 128, FAKE, 0, 257, 4, FAKE, 8, None) == g.GPTQ_EINVAL      # odd bf16 ldx
-    assert q(FAKE, FAKE, FAKE, 8, 256, 5, 128, FAKE, 1, 256, 4, FAKE, 8, None) == g.GPTQ_EINVAL      # bits
-    assert q(FAKE, FAKE, FAKE, 8, 256, 4, 48, FAKE, 1, 256, 4, FAKE, 8, None) == g.GPTQ_EUNSUPPORTED # group
-    assert q(FAKE, FAKE, FAKE, 8, 256, 4, 128, FAKE, 1, 256, -1, FAKE, 8, None) == g.GPTQ_EINVAL     # batch
-    assert q(None, None, None, 8, 256, 4, 128, None, 1, 256, 0, None, 8, None) == g.GPTQ_OK         # no vectors
+    assert q(FAKE, FAKE, FAKE, 8, 256, 4, 128, FAKE, 1, 128, 4, FAKE, 8, None, 0, None) == g.GPTQ_EINVAL   # ldx < cols
+    assert q(FAKE, FAKE, FAKE, 8, 256, 4, 128, FAKE, 1, 256, 4, FAKE, 4, None, 0, None) == g.GPTQ_EINVAL   # ldy < rows
+    assert q(FAKE, FAKE, FAKE, 8, 256, 4, 128, FAKE, 0, 257, 4, FAKE, 8, None, 0, None) == g.GPTQ_EINVAL   # odd bf16 ldx
+    assert q(FAKE, FAKE, FAKE, 8, 256, 5, 128, FAKE, 1, 256, 4, FAKE, 8, None, 0, None) == g.GPTQ_EINVAL   # bits
+    assert q(FAKE, FAKE, FAKE, 8, 256, 4, 48, FAKE, 1, 256, 4, FAKE, 8, None, 0, None) == g.GPTQ_EUNSUPPORTED
+    assert q(FAKE, FAKE, FAKE, 8, 256, 4, 128, FAKE, 1, 256, -1, FAKE, 8, None, 0, None) == g.GPTQ_EINVAL  # batch
+    assert q(None, None, None, 8, 256, 4, 128, None, 1, 256, 0, None, 8, None, 0, None) == g.GPTQ_OK      # no vectors
+    # the matrix-core path splits the columns of a wide layer over workgroups: a short
+    # workspace is refused before any launch
+    need = L.gptq_dequant_gemm_workspace_bytes(64, 8192, 4, 128, 8)
+    assert need >= 2 * 8 * 64 * 4 and need % 256 == 0
+    assert q(FAKE, FAKE, FAKE, 64, 8192, 4, 128, FAKE, 1, 8192, 8, FAKE, 64, FAKE, need - 1, None) == \
+        g.GPTQ_EWORKSPACE
+    assert q(FAKE, FAKE, FAKE, 64, 8192, 4, 128, FAKE, 1, 8192, 8, FAKE, 64, None, need, None) == g.GPTQ_EWORKSPACE
+    assert q(FAKE, FAKE, FAKE, 64, 8192, 4, 128, FAKE, 1, 8192, 8, FAKE, 64, ctypes.c_void_p(0x1002), need,
+             None) == g.GPTQ_EINVAL                                                                # misaligned
+    # no workspace where the path is not taken: one vector, groups of 64, or one slice
+    assert L.gptq_dequant_gemm_workspace_bytes(64, 8192, 4, 128, 1) == 0
+    assert L.gptq_dequant_gemm_workspace_bytes(64, 8192, 4, 64, 8) == 0
+    assert L.gptq_dequant_gemm_workspace_bytes(64, 256, 4, 128, 8) == 0
+    assert L.gptq_dequant_gemm_workspace_bytes(64, 8192, 4, -1, 8) == need
+    # up to 16 vectors share a launch: the workspace stops growing there
+    assert L.gptq_dequant_gemm_workspace_bytes(64, 8192, 4, 128, 40) == L.gptq_dequant_gemm_workspace_bytes(
+        64, 8192, 4, 128, 16)
 
 
 def test_hadamard_argument_errors():

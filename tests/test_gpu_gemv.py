@@ -194,6 +194,29 @@ def test_dequant_gemv_q_proj_full_size():
     _check(4096, 4096, 4, 128, seed=11)
 
 
+def _mma_path(groupsize, batch):
+    """Batches of two or more over groups of a multiple of 128 columns (or whole rows) take the
+    matrix-core kernel."""
+    return batch >= 2 and (groupsize == -1 or groupsize % 128 == 0)
+
+
+def _mma_depth(cols, batch, x_bf16):
+    """fp32 roundings a term of y passes through on the matrix-core path, with every addition
+    inside the matrix core taken as an fp32 round-to-nearest step in any order (products of a
+    code and a bf16 part of x are exact): per 128-column chunk a chain of 4 MFMA steps of 32
+    products each on each operand plane, the sum of the NM planes (1 for bf16 x or at most 5
+    fp32 vectors a launch, 2 for up to 8, 3 for up to 16), the zero-point fma and the scale
+    fma, the chunks of one slice, up to two more parts of the same vector, and the slices
+    (together at most 2 nch + 1, nch the chunk count).  The zero-point term passes 7 roundings
+    in its chunk sum instead of the chain."""
+    nm = 1
+    for b0 in range(0, batch, 16):
+        t = min(16, batch - b0)
+        nm = max(nm, 1 if (x_bf16 or t <= 5) else (2 if t <= 8 else 3))
+    nch = -(-cols // 128)
+    return 32 * 4 + (nm - 1) + 2 + (2 * nch + 1) + 2
+
+
 def _check_batch(rows, cols, bits, groupsize, batch, seed, x_bf16=False):
     g = _lib()
     torch, dev = torch_dev()
@@ -214,8 +237,13 @@ def _check_batch(rows, cols, bits, groupsize, batch, seed, x_bf16=False):
     gi = np.arange(cols) // gsz
     mag = scales.astype(np.float64)[:, gi] * (codes.astype(np.float64) + zeros.astype(np.float64)[:, gi])
     runs = -(-cols // 32)
-    D = 32 + 3 + -(-runs // 64) + 6 + 1
-    bound = D * U32 * (np.abs(X.astype(np.float64)) @ mag.T)
+    if _mma_path(groupsize, batch):
+        D = _mma_depth(cols, batch, x_bf16)
+        gain = 1.01  # the bf16 parts of an fp32 x add up to at most (1 + 2^-8) |x| in magnitude
+    else:
+        D = 32 + 3 + -(-runs // 64) + 6 + 1
+        gain = 1.0
+    bound = gain * D * U32 * (np.abs(X.astype(np.float64)) @ mag.T)
     err = np.abs(Yg.astype(np.float64) - Y0)
     say(f"   max err/bound {np.max(err / bound):.3f}")
     assert np.all(err <= bound)
@@ -232,10 +260,30 @@ def _check_batch(rows, cols, bits, groupsize, batch, seed, x_bf16=False):
     (4096, 4096, 4, 128, 8, False),   # the q_proj shape at a batch of eight
     (300, 1024, 4, 128, 16, True),    # two groups of eight, bf16
     (64, 2048, 2, 64, 200, True),     # 25 groups of eight
+    # matrix-core path: code widths, groups, ragged rows and chunks, slices, A-row layouts
+    (600, 25600, 4, 128, 8, False),   # the 5120x25600 layer's width: many column slices, 5 row blocks
+    (130, 4160, 8, 256, 7, False),    # 8 bits, groups of 256, 33 chunks (a half stage at the end)
+    (70, 2080, 3, 128, 9, False),     # 3 bits, nine fp32 vectors (three planes), a one-run last chunk
+    (45, 1008, 2, -1, 4, True),       # 2 bits, partial last run, bf16
+    (17, 36, 8, -1, 3, False),        # one chunk, one partial run, three fp32 vectors in one plane
+    (1000, 8192, 4, -1, 17, False),   # 16 + 1 vectors: the second launch has one
+    (256, 4096, 2, 128, 2, True),     # two bf16 vectors
+    (200, 3072, 4, 384, 5, False),    # groups of three chunks, five fp32 vectors (15 A rows)
 ])
 def test_dequant_gemm_parity(rows, cols, bits, groupsize, batch, x_bf16):
     say(f"dequant_gemm rows={rows} cols={cols} bits={bits} groupsize={groupsize} batch={batch} bf16={x_bf16}")
     _check_batch(rows, cols, bits, groupsize, batch, seed=rows + cols + batch, x_bf16=x_bf16)
+
+
+def test_dequant_gemm_mma_reproducible():
+    say("dequant_gemm matrix-core repeat rows=300 cols=8192 bits=4 groupsize=128 batch=8")
+    g = _lib()
+    torch, dev = torch_dev()
+    packed, scales, zeros, X, Yg = _check_batch(300, 8192, 4, 128, 8, seed=21)
+    Y2 = torch.full((8, 300), float("nan"), dtype=torch.float32, device=dev)
+    g.gptq_dequant_gemm(to_dev(packed.view(np.int32)), to_dev(scales), to_dev(zeros), 4, 128, to_dev(X), Y2)
+    torch.cuda.synchronize()
+    assert np.array_equal(Yg, Y2.cpu().numpy())
 
 
 def test_dequant_gemm_batch_of_one_is_the_gemv():
@@ -257,7 +305,7 @@ def test_dequant_gemm_empty_columns():
     buf = torch.zeros(64, dtype=torch.int32, device=dev)  # stands for the empty inputs
     p = ctypes.c_void_p(buf.data_ptr())
     st = g.lib().gptq_dequant_gemm(p, p, p, 7, 0, 4, -1, p, g.GPTQ_F32, 0, 5, ctypes.c_void_p(Y.data_ptr()), 9,
-                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                                   None, 0, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     torch.cuda.synchronize()
     assert st == 0
     assert torch.all(Y[:, :7] == 0)
