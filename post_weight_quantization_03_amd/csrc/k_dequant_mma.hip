@@ -394,20 +394,22 @@ __global__ __launch_bounds__(64 * MM_NW) void k_dequant_mma(
   GPTQ_TRACE_WRITE(TR_MMA, item);
 }
 
-// Y[t, r] = sum over slices s (in order) of P[s][t][r]; the loads of sixteen
-// slices are queued before they are added.
+// Y[t, r] = sum over slices s (in order) of P[s][t][r]; the loads of up to 64
+// slices are queued before they are added (one memory round trip a call for
+// every slice count the plans make).
+template <int NS>
 __global__ void k_mma_reduce(const float* __restrict__ P, int64_t nslices, int64_t T, int64_t rows,
                              float* __restrict__ Y, int64_t ldy) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= T * rows) return;
   const int64_t t = i / rows, r = i % rows, n = T * rows;
   float v = 0.0f;
-  for (int64_t s0 = 0; s0 < nslices; s0 += 16) {
-    float p[16];
+  for (int64_t s0 = 0; s0 < nslices; s0 += NS) {
+    float p[NS];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) p[k] = P[(s0 + k < nslices ? s0 + k : nslices - 1) * n + i];
+    for (int k = 0; k < NS; ++k) p[k] = P[(s0 + k < nslices ? s0 + k : nslices - 1) * n + i];
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
+    for (int k = 0; k < NS; ++k)
       if (s0 + k < nslices) v = (s0 + k == 0) ? p[k] : v + p[k];
   }
   Y[t * ldy + r] = v;
@@ -524,8 +526,14 @@ hipError_t dequant_mma_x(const uint32_t* packed, const float* scales, const uint
     if (e != hipSuccess) return e;
     if (pl.ks > 1) {
       const int64_t n = (int64_t)T * rows;
-      hipLaunchKernelGGL(k_mma_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                         static_cast<const float*>(workspace), pl.ks, (int64_t)T, rows, yb, ldy);
+      const dim3 rg((unsigned)((n + 255) / 256));
+      const float* P = static_cast<const float*>(workspace);
+      if (pl.ks <= 16)
+        hipLaunchKernelGGL(k_mma_reduce<16>, rg, dim3(256), 0, stream, P, pl.ks, (int64_t)T, rows, yb, ldy);
+      else if (pl.ks <= 32)
+        hipLaunchKernelGGL(k_mma_reduce<32>, rg, dim3(256), 0, stream, P, pl.ks, (int64_t)T, rows, yb, ldy);
+      else
+        hipLaunchKernelGGL(k_mma_reduce<64>, rg, dim3(256), 0, stream, P, pl.ks, (int64_t)T, rows, yb, ldy);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
