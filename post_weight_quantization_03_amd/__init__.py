@@ -272,7 +272,7 @@ def gptq_dequant_gemm_workspace_bytes(rows: int, cols: int, bits: int, groupsize
 def gptq_dequant_gemm(packed, scales, zeros, bits: int, groupsize: int, X, Y, workspace=None, stream=None):
     """Y [batch, rows] fp32 = (W^ X^T)^T for X [batch, cols] bf16 or fp32 (unit column stride).
     workspace: a device tensor of at least gptq_dequant_gemm_workspace_bytes bytes; allocated here
-    (through torch) when None."""
+    (through torch, tied to the stream the kernels run on) when None."""
     _check_dev(packed, scales, zeros, Y)
     torch = _torch()
     rows = packed.shape[0]
@@ -286,7 +286,7 @@ def gptq_dequant_gemm(packed, scales, zeros, bits: int, groupsize: int, X, Y, wo
     ldx = X.stride(0) if batch > 1 else cols
     need = gptq_dequant_gemm_workspace_bytes(rows, cols, bits, groupsize, batch)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=Y.device)
+        workspace = _workspace(need, Y, stream)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().gptq_dequant_gemm(_ptr(packed), _ptr(scales), _ptr(zeros), rows, cols, bits, groupsize, _ptr(X),
                                  _dtype_code(X), ldx, batch, _ptr(Y), Y.stride(0) if batch > 1 else rows,

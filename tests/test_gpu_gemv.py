@@ -17,7 +17,7 @@ import pytest
 
 from gpuhelp import bf16_dev, say, to_dev, torch_dev
 from post_weight_quantization_03_amd import synth
-from oracle import dequant_gemv_ref, pack_ref
+from oracle import dequant_gemv_ref, pack_ref, unpack_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -284,6 +284,67 @@ def test_dequant_gemm_mma_reproducible():
     g.gptq_dequant_gemm(to_dev(packed.view(np.int32)), to_dev(scales), to_dev(zeros), 4, 128, to_dev(X), Y2)
     torch.cuda.synchronize()
     assert np.array_equal(Yg, Y2.cpu().numpy())
+
+
+def test_dequant_gemm_full_size_5120x25600_sampled_rows():
+    """The Qwen3-32B down_proj shape (5120x25600, 4-bit g128) against a batch of 8 fp32 vectors, in
+    the launch configuration the benchmark times (every row computed; 25 column slices reduced in
+    order): 96 sampled rows (both ends, the 128-row block and 16-row tile edges, random) against the
+    oracle over all 25600 columns, under the matrix-core path's bound."""
+    g = _lib()
+    torch, dev = torch_dev()
+    rows, cols, bits, gs, batch = 5120, 25600, 4, 128, 8
+    say(f"dequant_gemm full size rows={rows} cols={cols} batch={batch}, sampled rows")
+    rng = np.random.default_rng(29)
+    G = cols // gs
+    packed = rng.integers(0, 2 ** 32, size=(rows, cols * bits // 32), dtype=np.uint64).astype(np.uint32)
+    scales = (rng.uniform(0.5, 2.0, size=(rows, G)) * 0.01).astype(np.float32)
+    zeros = rng.integers(0, 2 ** bits, size=(rows, G)).astype(np.uint8)
+    X = rng.standard_normal((batch, cols)).astype(np.float32)
+    X[:, rng.integers(0, cols, size=cols // 100)] *= 20.0
+    Y = torch.full((batch, rows), float("nan"), dtype=torch.float32, device=dev)
+    g.gptq_dequant_gemm(to_dev(packed.view(np.int32)), to_dev(scales), to_dev(zeros), bits, gs, to_dev(X), Y)
+    torch.cuda.synchronize()
+    Yg = Y.cpu().numpy()
+    assert np.all(np.isfinite(Yg))
+    sel = np.unique(np.concatenate([[0, 1, 15, 16, 127, 128, 129, 2559, 2560, rows - 129, rows - 128, rows - 17,
+                                     rows - 16, rows - 1], rng.choice(rows, 82, replace=False)]))
+    Y0 = dequant_gemv_ref(packed[sel], scales[sel], zeros[sel], bits, gs, X.T.astype(np.float64), cols).T
+    codes = unpack_ref(packed[sel], cols, bits)
+    gi = np.arange(cols) // gs
+    mag = scales[sel].astype(np.float64)[:, gi] * (codes.astype(np.float64) + zeros[sel].astype(np.float64)[:, gi])
+    bound = 1.01 * _mma_depth(cols, batch, False) * U32 * (np.abs(X.astype(np.float64)) @ mag.T)
+    err = np.abs(Yg[:, sel].astype(np.float64) - Y0)
+    say(f"   {len(sel)} rows, max err/bound {np.max(err / bound):.4f}")
+    assert np.all(err <= bound)
+
+
+def test_dequant_gemm_side_stream_workspace():
+    """The binding's temporary workspace, used on a stream that is not the current one, is not
+    handed to a new allocation while that stream's kernels still write it: allocating and filling
+    memory on the current stream right after the call leaves Y unchanged."""
+    g = _lib()
+    torch, dev = torch_dev()
+    rows, cols, bits, gs, batch = 1000, 16384, 4, 128, 8
+    say(f"dequant_gemm on a side stream rows={rows} cols={cols} batch={batch}")
+    need = g.gptq_dequant_gemm_workspace_bytes(rows, cols, bits, gs, batch)
+    assert need > 0
+    codes, scales, zeros, _ = _inputs(rows, cols, bits, gs, seed=17)
+    X = np.random.default_rng(18).standard_normal((batch, cols)).astype(np.float32)
+    pk, sd, zd, Xd = to_dev(pack_ref(codes, bits).view(np.int32)), to_dev(scales), to_dev(zeros), to_dev(X)
+    ref = torch.empty((batch, rows), dtype=torch.float32, device=dev)
+    g.gptq_dequant_gemm(pk, sd, zd, bits, gs, Xd, ref)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for _ in range(3):
+        Y = torch.full((batch, rows), float("nan"), dtype=torch.float32, device=dev)
+        side.wait_stream(torch.cuda.current_stream())
+        g.gptq_dequant_gemm(pk, sd, zd, bits, gs, Xd, Y, stream=side)
+        junk = torch.full((need // 4,), 7.0, device=dev)
+        side.synchronize()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, ref)
+        del junk
 
 
 def test_dequant_gemm_batch_of_one_is_the_gemv():
