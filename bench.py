@@ -74,7 +74,8 @@ def parse():
                     help="skip the metric's second shape (11008x4096, 4-bit g128) on the default workload")
     ap.add_argument("--trace", action="store_true",
                     help="instead of the bench line: one pass of the layer on libgptq_trace.so, printing the "
-                         "phase timestamps of the column loop and the factor's chain (medians, us)")
+                         "phase timestamps of the column loop and the factor's chain (medians, us), and one "
+                         "call of the batch product (5120x25600, 8 fp32 vectors) with its workgroups' phases")
     return ap.parse_args()
 
 
@@ -608,7 +609,7 @@ def time_layer(args, g, torch, wl, lin, acts, bits, dev, workload_name, descript
 
 
 TRACE_REC = 32  # words per trace record (gptq_trace_set in include/gptq.h)
-TRACE_LOOP, TRACE_POTRF, TRACE_TRSM, TRACE_DIAG, TRACE_TILE = 1, 2, 3, 4, 5
+TRACE_LOOP, TRACE_POTRF, TRACE_TRSM, TRACE_DIAG, TRACE_TILE, TRACE_MMA = 1, 2, 3, 4, 5, 6
 
 
 def trace_summary(words, count):
@@ -665,6 +666,59 @@ def trace_summary(words, count):
     return out
 
 
+def trace_batch_summary(words, count):
+    """Decodes the matrix-core batch product's records (kind 6: one a workgroup, stamps at its start,
+    after its x loads, after its scale and code loads, after the LDS zeroing, after staging, after the
+    chunks, at its end) into phase medians and percentiles in microseconds, the workgroups' start and
+    life times relative to the first start, and how many were alive at 12 points of the kernel's span.
+    Host logic only."""
+    words = np.asarray(words, dtype=np.int64)
+    n = min(int(count), int(words[0]))
+    rec = words[TRACE_REC:TRACE_REC * (n + 1)].reshape(n, TRACE_REC)
+    rec = rec[(rec[:, 0] == TRACE_MMA) & (rec[:, 3] >= 7)]
+    if not len(rec):
+        return {"workgroups": 0}
+    st = rec[:, 4:11].astype(np.float64) / 100.0
+    st -= st[:, 0].min()
+    ph = np.diff(st, axis=1)
+    names = ("x_loads_issued", "scale_and_code_loads_issued", "lds_zeroed", "staged", "chunks_applied",
+             "rows_combined_and_written")
+    span = float(st[:, 6].max())
+    pct = lambda v: [float(np.percentile(v, q)) for q in (0, 25, 50, 75, 100)]  # noqa: E731
+    return {"workgroups": int(len(rec)), "kernel_span_us": span,
+            "start_us_percentiles": pct(st[:, 0]), "lifetime_us_percentiles": pct(st[:, 6] - st[:, 0]),
+            "phase_median_us": {nm: float(np.median(ph[:, i])) for i, nm in enumerate(names)},
+            "phase_p90_us": {nm: float(np.percentile(ph[:, i], 90)) for i, nm in enumerate(names)},
+            "alive": [int(((st[:, 0] <= t) & (st[:, 6] > t)).sum()) for t in np.linspace(0.0, span, 12)]}
+
+
+def trace_batch(g, torch, dev, rows=5120, cols=25600, batch=8, bits=4, groupsize=128):
+    """One call of the batch product (5120x25600, 4-bit g128, 8 fp32 vectors, seeded random codes,
+    scales and zeros) on the trace build, after one untimed call."""
+    gen = torch.Generator(dev).manual_seed(5)
+    G = -(-cols // groupsize)
+    packed = torch.randint(-2 ** 31, 2 ** 31 - 1, (rows, cols * bits // 32), dtype=torch.int32, device=dev,
+                           generator=gen)
+    scales = 0.005 + 0.015 * torch.rand((rows, G), device=dev, generator=gen)
+    zeros = torch.randint(0, 2 ** bits, (rows, G), dtype=torch.uint8, device=dev, generator=gen)
+    X = torch.randn(batch, cols, device=dev, generator=gen)
+    Y = torch.empty(batch, rows, device=dev)
+    g.gptq_dequant_gemm(packed, scales, zeros, bits, groupsize, X, Y)
+    cap = 1 << 14
+    buf = torch.zeros(TRACE_REC * (cap + 1), dtype=torch.int64, device=dev)
+    buf[0] = cap
+    torch.cuda.synchronize()
+    g.gptq_trace_set(buf)
+    g.gptq_dequant_gemm(packed, scales, zeros, bits, groupsize, X, Y)
+    torch.cuda.synchronize()
+    g.gptq_trace_set(None)
+    words = buf.cpu().numpy()
+    out = trace_batch_summary(words, int(words[1]))
+    out["config"] = {"rows": rows, "cols": cols, "batch": batch, "bits": bits, "groupsize": groupsize,
+                     "x": "fp32"}
+    return out
+
+
 def trace_layer(args, g, torch, wl, lin, acts, bits, dev):
     """One pass of the layer (Hessian, factor, quantize) on the trace build, after one untimed pass."""
     Xd = host_tensor(torch, acts.full(), acts.bf16).to(dev)
@@ -707,8 +761,8 @@ def main():
     if args.trace:
         g.LIB_PATH = os.path.join(os.path.dirname(g.__file__), "libgptq_trace.so")
         lin = wl.linears[args.layer]
-        print(json.dumps({"trace": trace_layer(args, g, torch, wl, lin, wl.hessians[lin.hessian], lin.bits, dev)}),
-              flush=True)
+        print(json.dumps({"trace": trace_layer(args, g, torch, wl, lin, wl.hessians[lin.hessian], lin.bits, dev),
+                          "batch_product": trace_batch(g, torch, dev)}), flush=True)
         return
     if args.whole:
         print(json.dumps(whole_workload(args, g, torch, wl, dev)), flush=True)

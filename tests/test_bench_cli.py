@@ -110,3 +110,35 @@ def test_trace_decoding_on_a_synthetic_buffer():
     assert ch["steps"] == 1 and ch["solve_span"] == 6.0 and ch["diagonal_update_span"] == 2.0
     # gaps: factor end -> solve 2 us, solve end -> update 3 us, update end -> next factor
     assert abs(ch["gaps_between_launches"] - (2.0 + 3.0 + (100000 - (p0_end + 1300)) / 100.0)) < 1e-9
+
+
+def test_batch_trace_decoding_on_a_synthetic_buffer():
+    """bench.trace_batch_summary on batch-product records (kind 6) with known phases and start times;
+    records of other kinds and short records are ignored."""
+    import numpy as np
+    R = bench.TRACE_REC
+    recs = []
+
+    def add(kind, wg, tag, stamps):
+        r = np.zeros(R, dtype=np.int64)
+        r[:4] = (kind, wg, tag, len(stamps))
+        r[4:4 + len(stamps)] = stamps
+        recs.append(r)
+
+    # four workgroups: two start at 1 us (ticks of 10 ns), two at 21 us; phases 1, 3, 1, 2, 4, 1 us
+    for wg, t0 in enumerate((100, 100, 2100, 2100)):
+        add(bench.TRACE_MMA, wg, wg, np.cumsum([t0, 100, 300, 100, 200, 400, 100]))
+    add(bench.TRACE_LOOP, 0, 1, np.cumsum([0, 1, 2, 3, 4, 5, 6]))       # another kind
+    add(bench.TRACE_MMA, 9, 9, [5, 6, 7])                                # too few stamps
+    words = np.zeros(R * (len(recs) + 1), dtype=np.int64)
+    words[0] = 100
+    words[R:] = np.concatenate(recs)
+    out = bench.trace_batch_summary(words, len(recs))
+    assert out["workgroups"] == 4
+    assert out["kernel_span_us"] == 32.0                  # last end 21 + 12 us, from the first start at 1 us
+    assert out["phase_median_us"] == {"x_loads_issued": 1.0, "scale_and_code_loads_issued": 3.0, "lds_zeroed": 1.0,
+                                      "staged": 2.0, "chunks_applied": 4.0, "rows_combined_and_written": 1.0}
+    assert out["start_us_percentiles"][0] == 0.0 and out["start_us_percentiles"][-1] == 20.0
+    assert out["lifetime_us_percentiles"] == [12.0] * 5
+    assert out["alive"][0] == 2 and out["alive"][-1] == 0 and max(out["alive"]) == 2
+    assert bench.trace_batch_summary(words[:R], 0) == {"workgroups": 0}
