@@ -275,6 +275,29 @@ def test_dequant_gemm_parity(rows, cols, bits, groupsize, batch, x_bf16):
     _check_batch(rows, cols, bits, groupsize, batch, seed=rows + cols + batch, x_bf16=x_bf16)
 
 
+def _random_cases(n, seed):
+    """Seeded random batch cases over both paths: bits, groups (multiples of 32 and of 128, and
+    whole rows), ragged rows and columns (whole code words), batches 2..40, bf16 and fp32."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        bits = int(rng.choice([2, 3, 4, 8]))
+        step = {2: 16, 3: 32, 4: 8, 8: 4}[bits]            # cols * bits is whole words
+        cols = int(rng.integers(1, 3000 // step + 1)) * step
+        g = int(rng.choice([-1, 32, 64, 96, 128, 256, 384]))
+        rows = int(rng.integers(1, 700))
+        batch = int(rng.integers(2, 41))
+        out.append((rows, cols, bits, g, batch, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("rows,cols,bits,groupsize,batch,x_bf16", _random_cases(24, 2024))
+def test_dequant_gemm_random_shapes(rows, cols, bits, groupsize, batch, x_bf16):
+    say(f"dequant_gemm random rows={rows} cols={cols} bits={bits} groupsize={groupsize} batch={batch} "
+        f"bf16={x_bf16}")
+    _check_batch(rows, cols, bits, groupsize, batch, seed=rows * 7 + cols + batch, x_bf16=x_bf16)
+
+
 def test_dequant_gemm_mma_reproducible():
     say("dequant_gemm matrix-core repeat rows=300 cols=8192 bits=4 groupsize=128 batch=8")
     g = _lib()
