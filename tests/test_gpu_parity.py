@@ -198,6 +198,36 @@ def test_quantize_ragged_and_groups(rows, cols, bits, g):
     check_quantize(W64, H32, bits, g, out, blocked=False)
 
 
+def _random_layers(n, seed):
+    """Seeded random layers: 1 to 600 rows, 1 to 1600 columns, bits 2/3/4/8, every group mode the
+    quantizer takes (-1, 32, 64, 128, 256, 384), bf16 or fp32 weights, and now and then dead input
+    channels."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        out.append((int(rng.integers(1, 601)), int(rng.integers(1, 1601)), int(rng.choice([2, 3, 4, 8])),
+                    int(rng.choice([-1, 32, 64, 128, 256, 384])), bool(rng.integers(0, 2)),
+                    int(rng.integers(0, 4)) if rng.random() < 0.3 else 0))
+    return out
+
+
+@pytest.mark.parametrize("rows,cols,bits,g,wbf16,dead", _random_layers(16, 77))
+def test_quantize_random_shapes(rows, cols, bits, g, wbf16, dead):
+    _lib_loaded()
+    say(f"quantize random rows={rows} cols={cols} bits={bits} g={g} wbf16={wbf16} dead={dead}")
+    rng = np.random.default_rng(rows * 1009 + cols)
+    a = synth.Activations(seed=rows + cols, tensor=synth.T_X, n=cols, tokens=4 * cols + 64, dist=synth.STUDENT_T4,
+                          outliers=max(1, cols // 100), outlier_factor=20.0, bf16=True)
+    X = synth.bf16_to_f32(a.full())
+    if dead:
+        X[:, rng.choice(cols, size=min(dead, cols), replace=False)] = 0.0
+    H32 = hessian_ref([X], cols).astype(np.float32)
+    W = synth.rows(rows + 3, synth.T_W, synth.NORMAL, 0.02, cols, 0, rows, bf16=wbf16)
+    W64 = (synth.bf16_to_f32(W) if wbf16 else W).astype(np.float64)
+    out = gpu_quantize(W, H32, bits, g, w_bf16=wbf16)
+    check_quantize(W64, H32, bits, g, out, blocked=False)
+
+
 def test_quantize_dead_column():
     _lib_loaded()
     say("quantize with dead input channels")
