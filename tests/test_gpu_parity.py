@@ -56,6 +56,33 @@ def test_hessian_parity(n, tokens, bf16, chunks, pad):
     assert np.array_equal(Hg, Hg2), "Hessian not bit-reproducible"
 
 
+def _random_hessians(n_cases, seed):
+    """Seeded random Hessian calls: widths 1 to 1100 (four tiny ones first), 1 to 20000 tokens,
+    bf16 or fp32 X, split over 1 to 3 calls, row strides padded by 0 to 5 elements."""
+    rng = np.random.default_rng(seed)
+    out = [(1, 5, True, 1, 0), (2, 333, False, 2, 1), (3, 77, True, 1, 3), (7, 4097, True, 3, 0)]
+    for _ in range(n_cases - len(out)):
+        out.append((int(rng.integers(1, 1101)), int(rng.integers(1, 20001)), bool(rng.integers(0, 2)),
+                    int(rng.integers(1, 4)), int(rng.integers(0, 6))))
+    return out
+
+
+@pytest.mark.parametrize("n,tokens,bf16,chunks,pad", _random_hessians(12, 11))
+def test_hessian_random_shapes(n, tokens, bf16, chunks, pad):
+    _lib_loaded()
+    say(f"hessian random n={n} tokens={tokens} bf16={bf16} chunks={chunks} pad={pad}")
+    a = synth.Activations(seed=n * 31 + tokens, tensor=synth.T_X, n=n, tokens=tokens, dist=synth.STUDENT_T4,
+                          outliers=max(1, n // 100), outlier_factor=20.0, bf16=bf16)
+    X = a.full()
+    Xf = synth.bf16_to_f32(X) if bf16 else X
+    H0 = hessian_ref([Xf], n)
+    Hg = gpu_hessian(X, bf16, chunks=chunks, ldx_pad=pad)
+    rel = np.linalg.norm(Hg - H0) / np.linalg.norm(H0)
+    say(f"   rel Frobenius {rel:.3e}")
+    assert rel <= H_RTOL
+    assert np.array_equal(Hg, Hg.T)
+
+
 @pytest.mark.parametrize("n,tokens", [(512, 992), (512, 8192), (768, 4096)])
 def test_hessian_full_tiles_repeatable(n, tokens):
     """Full 256-wide tiles take the direct global-to-LDS pipeline; repeated runs must agree bit for bit
