@@ -377,6 +377,31 @@ def test_pack_parity(bits, rows, cols):
     np.testing.assert_array_equal(packed.cpu().numpy().view(np.uint32), pack_ref(codes, bits))
 
 
+def _random_packs(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        bits = int(rng.choice([2, 3, 4, 8]))
+        step = {2: 16, 3: 32, 4: 8, 8: 4}[bits]  # cols * bits is whole words
+        out.append((bits, int(rng.integers(1, 5001)), int(rng.integers(1, 400)) * step))
+    return out
+
+
+@pytest.mark.parametrize("bits,rows,cols", _random_packs(10, 5))
+def test_pack_random_shapes(bits, rows, cols):
+    """Seeded random shapes with full-byte codes: the library keeps each code's low bits (the
+    header's masking rule), bit for bit against the oracle's packing of the masked codes."""
+    g = _lib_loaded()
+    torch, dev = torch_dev()
+    say(f"pack random bits={bits} rows={rows} cols={cols}")
+    rng = np.random.default_rng(rows * 3 + cols)
+    codes = rng.integers(0, 256, size=(rows, cols)).astype(np.uint8)
+    packed = torch.full((rows, cols * bits // 32), -1, dtype=torch.int32, device=dev)
+    g.gptq_pack(to_dev(codes), bits, packed)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(packed.cpu().numpy().view(np.uint32), pack_ref(codes & ((1 << bits) - 1), bits))
+
+
 # --------------------------------------------------------------------------- end to end
 
 def test_end_to_end_linear256():
