@@ -291,6 +291,14 @@ def _random_cases(n, seed):
     return out
 
 
+@pytest.mark.parametrize("rows,cols,bits,groupsize,batch,x_bf16",
+                         [(r * 17 + 1, c, b, g, 1, x) for r, c, b, g, _, x in _random_cases(16, 99)])
+def test_dequant_gemv_random_shapes(rows, cols, bits, groupsize, batch, x_bf16):
+    """Seeded random single-vector shapes (rows up to about 12000, so both launch shapes)."""
+    say(f"dequant_gemv random rows={rows} cols={cols} bits={bits} groupsize={groupsize} bf16={x_bf16}")
+    _check(rows, cols, bits, groupsize, seed=rows + 3 * cols, x_bf16=x_bf16)
+
+
 @pytest.mark.parametrize("rows,cols,bits,groupsize,batch,x_bf16", _random_cases(24, 2024))
 def test_dequant_gemm_random_shapes(rows, cols, bits, groupsize, batch, x_bf16):
     say(f"dequant_gemm random rows={rows} cols={cols} bits={bits} groupsize={groupsize} batch={batch} "
