@@ -336,6 +336,33 @@ def test_factor_matches_oracle():
     assert rel <= 1e-4
 
 
+def _random_factors(n_cases, seed):
+    """Seeded random widths (a few tiny and block-edge ones first), tokens from a quarter of the
+    width (rank-deficient, damping-bound H) to four times it, and both factor routes."""
+    rng = np.random.default_rng(seed)
+    out = [(9, 40, False), (17, 6, True), (127, 500, False), (129, 100, True), (257, 1028, False)]
+    for _ in range(n_cases - len(out)):
+        n = int(rng.integers(3, 2601))
+        out.append((n, int(rng.integers(max(2, n // 4), 4 * n + 1)), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("n,tokens,f64", _random_factors(12, 21))
+def test_factor_random_shapes(n, tokens, f64):
+    """U from the device factor against the fp64 factor of the same damped H: relative Frobenius
+    error 1e-4 for the fp32 route, 2e-7 for the fp64 option."""
+    _lib_loaded()
+    from oracle import damp_ref, factor_ref
+    say(f"factor random n={n} tokens={tokens} f64={f64}")
+    W, W64, H32 = _layer(4, n, seed=n + tokens, tokens=tokens)
+    out = gpu_quantize(W, H32, 4, 128, w_bf16=True, flags=2 if f64 else 0)
+    Hd, _, _, _ = damp_ref(H32.astype(np.float64), W64, 0.01)
+    U = factor_ref(Hd)
+    rel = np.linalg.norm(out["U"] - U) / np.linalg.norm(U)
+    say(f"   U rel Frobenius {rel:.3e}")
+    assert rel <= (2e-7 if f64 else 1e-4)
+
+
 @pytest.mark.parametrize("n", [6144, 6000])
 def test_factor_matches_oracle_deferred_steps(n):
     """Widths whose first factor steps are large enough for the deferred
