@@ -95,8 +95,13 @@ def check_quantize(W64, H32, bits, groupsize, out, rows_sel=None, blocked=True, 
     if lerr:
         e_or = layer_error(ref["W_staged"], ref["what"], H64)
         e_gpu = layer_error(ref["W_staged"], out["w_hat"].astype(np.float64), H64)
-        say(f"   layer error gpu {e_gpu:.6e} oracle {e_or:.6e} ratio-1 {e_gpu / e_or - 1:.2e}")
-        assert abs(e_gpu / e_or - 1.0) <= LERR_RTOL
+        if e_or == 0.0:
+            # every group exact (a one-value group quantizes without error): so must the GPU's be
+            say(f"   layer error gpu {e_gpu:.6e} oracle 0")
+            assert e_gpu == 0.0
+        else:
+            say(f"   layer error gpu {e_gpu:.6e} oracle {e_or:.6e} ratio-1 {e_gpu / e_or - 1:.2e}")
+            assert abs(e_gpu / e_or - 1.0) <= LERR_RTOL
         st["lerr_gpu"], st["lerr_oracle"] = e_gpu, e_or
     # the w_hat output decodes the codes with the group grid, bit for bit
     g = W64.shape[1] if groupsize == -1 else groupsize

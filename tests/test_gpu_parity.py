@@ -255,6 +255,22 @@ def test_quantize_random_shapes(rows, cols, bits, g, wbf16, dead):
     check_quantize(W64, H32, bits, g, out, blocked=False)
 
 
+@pytest.mark.parametrize("rows,cols,bits,g", [(5, 1, 4, 128), (3, 2, 8, -1), (17, 3, 2, 32), (9, 5, 3, 64),
+                                             (4, 7, 4, -1), (33, 4, 4, 128)])
+def test_quantize_narrow_layers(rows, cols, bits, g):
+    """Layers narrower than one 8-column lane run: the factor's identity-padded 128-block, the
+    element-wise staging and the column loop's masked lanes, against the oracle."""
+    _lib_loaded()
+    from oracle import damp_ref, factor_ref
+    say(f"quantize narrow rows={rows} cols={cols} bits={bits} g={g}")
+    W, W64, H32 = _layer(rows, cols, seed=rows * 13 + cols, tokens=8 * cols + 16)
+    out = gpu_quantize(W, H32, bits, g, w_bf16=True)
+    check_quantize(W64, H32, bits, g, out, blocked=False)
+    Hd, _, _, _ = damp_ref(H32.astype(np.float64), W64, 0.01)
+    U = factor_ref(Hd)
+    assert np.linalg.norm(out["U"] - U) <= 1e-4 * np.linalg.norm(U)
+
+
 def test_quantize_dead_column():
     _lib_loaded()
     say("quantize with dead input channels")
