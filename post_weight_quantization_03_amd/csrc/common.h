@@ -146,7 +146,7 @@ struct QuantArgs {
   float* w_hat;
   float* row_loss;
   float* Wf;  // [rows, cols] working copy
-  float* E;   // [2][rows, 128] scaled errors of the current and the previous block
+  float* E;   // [rows, 128 ceil(cols / 128)] scaled errors of every block, kept for the layer
   uint16_t* Usplit;  // [3][cols, cols] bf16 planes of U for the split trailing GEMM, or null
   int64_t G;
 };
