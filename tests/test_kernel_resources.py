@@ -13,7 +13,9 @@ produces for gfx950 (host-only: hipcc cross-compiles without a GPU):
     instructions are the direct-to-LDS loads, and the loads issued between consecutive counted
     barriers number exactly the count of the later barrier;
   * other vector-memory operations in the prologue and tail loops (spill traffic) are counted:
-    they can only make a counted wait stricter.
+    they can only make a counted wait stricter;
+  * the pipelined kernels outside the Hessian (the fp32 GEMM tiles, the factor's step, the
+    quantize launch with its split tiles) use no scratch memory at all.
 """
 
 from __future__ import annotations
@@ -121,10 +123,45 @@ def check_file(lines):
     return checked, single, extra
 
 
-@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
-def test_counted_pipelines_hold_only_their_own_loads(tmp_path):
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    tmp = tmp_path_factory.mktemp("asm")
     with ThreadPoolExecutor(max_workers=len(FILES)) as ex:
-        asm = dict(zip(FILES, ex.map(lambda f: _asm(f, tmp_path), FILES)))
+        return dict(zip(FILES, ex.map(lambda f: _asm(f, tmp), FILES)))
+
+
+def scratch_sizes(lines):
+    """kernel symbol -> (private segment bytes per lane, whether it issues direct-to-LDS loads)."""
+    dma = {name: any(DMA.match(ln) for ln in body) for name, body in _kernels(lines).items()}
+    out, cur = {}, None
+    for ln in lines:
+        m = re.match(r"^\s*\.amdhsa_kernel (\S+)", ln)
+        if m:
+            cur = m.group(1)
+            continue
+        m = re.match(r"^\s*\.amdhsa_private_segment_fixed_size (\d+)", ln)
+        if m and cur is not None:
+            out[cur] = (int(m.group(1)), dma.get(cur, False))
+            cur = None
+    return out
+
+
+def test_pipelined_tiles_use_no_scratch(asm):
+    """A tile that keeps its operands' addresses in scratch memory (for instance a copy of its job
+    indexed at run time) issues scratch loads inside its pipeline; outside the Hessian's kernels,
+    whose epilogues spill, no pipelined kernel may use scratch at all."""
+    seen = 0
+    for f in ("k_gemm.hip", "k_factor.hip", "k_quant.hip"):
+        for name, (nbytes, dma) in scratch_sizes(asm[f]).items():
+            if dma:
+                seen += 1
+                assert nbytes == 0, f"{f}: {name} uses {nbytes} bytes of scratch per lane"
+    assert seen >= 6, seen  # four GEMM tiles, the factor step, the quantize launches
+
+
+def test_counted_pipelines_hold_only_their_own_loads(asm):
     totals = {f: check_file(lines) for f, lines in asm.items()}
     print(totals)
     # every file with such a pipeline has its steady-state loops checked
