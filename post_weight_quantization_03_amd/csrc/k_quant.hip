@@ -22,13 +22,13 @@
 #include <utility>
 
 #include "gemm_tile.h"
+#include "quant_schedule.h"
 #include "sgemm_tile.h"
 
 namespace gptq {
 namespace {
 
 constexpr int B = 128;
-constexpr int64_t LAZY = 8;  // blocks per group of the trailing update's second level
 
 enum GroupMode { GM_BIG = 0, GM_32 = 1, GM_64 = 2 };
 
@@ -616,15 +616,11 @@ hipError_t quant_run(const QuantArgs& q, hipStream_t stream) {
     a.bw = (int)((cols - c0) < B ? (cols - c0) : B);
     a.E = q.E + b * B;
     a.Eprev = (overlap && b > 0) ? q.E + (b - 1) * B : nullptr;
-    // The trailing update in two levels.  The errors of block e reach the
-    // column blocks of its own group of LAZY blocks (groups aligned at
-    // multiples of LAZY) beyond e + 1 right away, K = 128, in launch e + 1;
-    // block e + 1 itself is updated by the loop workgroups of that launch.
-    // Column blocks past the group receive the whole group at once, K =
-    // 128 LAZY, in the launch after the group's last block: W's far columns
-    // are read and written once per group instead of once per block.  Every
-    // pair (block e, column block j >= e + 2) is covered exactly once, before
-    // launch j, and no two jobs of one launch touch the same columns.
+    // The trailing update in two levels (quant_schedule.h): the errors of
+    // block e reach the column blocks of its own group beyond e + 1 in launch
+    // e + 1 (block e + 1 itself from the loop workgroups of that launch), and
+    // the column blocks past the group receive the whole group at once in the
+    // launch after the group's last block.
     FarJobs far{};
     if (overlap && b > 0) {
       auto job = [&](SplitGemm& g, int64_t e0, int64_t ne, int64_t j0, int64_t j1) {  // blocks [e0, e0+ne) -> [j0, j1]
@@ -638,10 +634,10 @@ hipError_t quant_run(const QuantArgs& q, hipStream_t stream) {
         g.N = (int)((j1 + 1) * B < cols ? (j1 + 1 - j0) * B : cols - j0 * B);
         g.K = (int)(ne * B);
       };
-      if (b % LAZY == 0 && b + 1 < nb) job(far.g[0], b - LAZY, LAZY, b + 1, nb - 1);
-      const int64_t e = b - 1, gend = (e / LAZY + 1) * LAZY;  // last column block of e's group
-      const int64_t j1 = gend < nb - 1 ? gend : nb - 1;
-      if (e + 2 <= j1) job(far.g[1], e, 1, e + 2, j1);
+      UpdateJob jobs[2];
+      update_jobs(b, nb, jobs);
+      for (int k = 0; k < 2; ++k)
+        if (jobs[k].ne > 0) job(far.g[k], jobs[k].e0, jobs[k].ne, jobs[k].j0, jobs[k].j1);
     }
     hipError_t e;
     if (mode == GM_32)
