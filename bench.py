@@ -35,17 +35,25 @@ PEAK_HBM_GBS = 8000.0
 # HBM bytes per Hessian accumulation call (k_syrk_bf16 and k_syrk_reduce together), from two
 # rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) scaled by the reading of a plain 1 GiB copy;
 # the summary with the commands is profiles/hbm_counters_q_proj_4096x4096_262144tok.md.  Valid
-# only for the kernel source they were taken on: a different k_hessian.hip reports null.
-SYRK_TRAFFIC = {"k_hessian_sha256": "7c4239606312840df1d660666ecd92f0a6e0c879e66322fd123812bcab15937b",
+# only for the kernel sources they were taken on (k_hessian.hip and the work decomposition it
+# includes, syrk_plan.h): different sources report null.
+SYRK_TRAFFIC = {"sources_sha256": "9daeb3705703cd2709aba5e44ec8439a48e329726251bfc3a4ed44f8da19812d",
                 "workload": "q_proj_4096", "tokens": 262144,
-                "fetch_bytes": 9208407915.7, "write_bytes": 492683057.3}
+                "fetch_bytes": 9207598266.6, "write_bytes": 492690001.3}
+SYRK_SOURCES = ("k_hessian.hip", "syrk_plan.h")
+
+
+def syrk_sources_sha256():
+    h = hashlib.sha256()
+    for name in SYRK_SOURCES:
+        with open(os.path.join(ROOT, "post_weight_quantization_03_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def syrk_traffic(workload, tokens):
-    path = os.path.join(ROOT, "post_weight_quantization_03_amd", "csrc", "k_hessian.hip")
-    sha = hashlib.sha256(open(path, "rb").read()).hexdigest()
     t = SYRK_TRAFFIC
-    if sha != t["k_hessian_sha256"] or workload != t["workload"] or tokens != t["tokens"]:
+    if syrk_sources_sha256() != t["sources_sha256"] or workload != t["workload"] or tokens != t["tokens"]:
         return None
     return t["fetch_bytes"] + t["write_bytes"]
 

@@ -50,6 +50,14 @@ def test_traffic_figure_only_for_the_measured_workload():
     assert bench.syrk_traffic(t["workload"], t["tokens"] // 2) is None
 
 
+def test_traffic_figure_belongs_to_the_committed_kernel_sources():
+    # the counters were taken on the Hessian sources as committed; a change to them must come
+    # with new counters (or the line reports no traffic figure)
+    t = bench.SYRK_TRAFFIC
+    assert bench.syrk_sources_sha256() == t["sources_sha256"]
+    assert bench.syrk_traffic(t["workload"], t["tokens"]) == t["fetch_bytes"] + t["write_bytes"]
+
+
 def test_cpu_baseline_reports_host_and_stages():
     """The oracle leg on the small 256x256 workload, in full: every stage timed on its own, the host's
     cores, CPU model and BLAS recorded."""
