@@ -89,7 +89,7 @@ def _spd(n, seed):
 @pytest.mark.parametrize("n,NB,lazy,tiles_limit", [
     (300, 32, 2, 0), (512, 64, 2, 0), (520, 64, 3, 0), (384, 128, 2, 0), (1000, 128, 2, 0),
     (700, 32, 2, 60),   # the size rule mixes deferred and immediate steps
-    (610, 32, 4, 0), (257, 32, 1, 0),
+    (610, 32, 4, 0), (900, 32, 8, 0), (257, 32, 1, 0),
 ])
 def test_blocked_factor_is_exact(n, NB, lazy, tiles_limit):
     H = _spd(n, n + NB)
